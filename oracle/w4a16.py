@@ -1,0 +1,111 @@
+"""W4A16 reference: per-group asymmetric uint4 weights, 16-bit activations
+(test infrastructure only).
+
+What the path computes ([QK] §9.5 "关键 Kernel: Dequant + GEMM"; [LQ] "W4A16：
+权重在寄存器里'现场解压'" (W4A16: weights decompressed in registers)):
+
+    Y[m, n] = sum_k X[m, k] * s[g(k), n] * (q[n, k] - z[g(k), n]),   g(k) = k // group
+
+The fused kernel must equal "dequantize W explicitly, then multiply"; this
+module is that plain definition: explicit dequant to fp64 (exact, since
+s * (q - z) with an fp16 s and |q - z| <= 15 has at most 15 significant bits)
+and an fp64 BLAS product.
+
+Shapes follow [LQ]'s notation paragraph: X is [T, K] (tokens x input
+channels), W is [N, K] (nn.Linear.weight), Y = X·Wᵀ is [T, N].
+"""
+
+import numpy as np
+
+from .numerics import rne, to_f16
+
+GROUP = 128
+
+
+def quantize_w4(W, group=GROUP):
+    """Per-group asymmetric round-to-nearest quantization to uint4.
+
+    For each output channel n and each run of ``group`` consecutive input
+    channels (one group g), in IEEE fp32 ([QK] §9.3 "量化方案的粒度" and [LQ]
+    "粒度" (granularity): per-group along K, g = 128; [LQ] "对称与非对称":
+    asymmetric uint4 codes 0..15; the range-to-(s, z) rule of [LQ]
+    "线性量化：一把刻度尺"; the degenerate-range clamp at 1e-5 of the
+    ``pseudo_quant`` routine in [LQ]'s AWQ section):
+
+        mn = min(min_k w, 0)        mx = max(max_k w, 0)
+        s16 = fp16(max(mx - mn, 1e-5) / 15)           (stored scale, RNE)
+        z = clamp(round(-mn / s16), 0, 15)            (stored zero point)
+        q = clamp(round(w / s16) + z, 0, 15)
+
+    Readings where the pages are silent: the range is widened to contain 0 so
+    that the integer z keeps real 0 on a tick ([LQ] linear-quantization
+    section says z is an integer for exactly that reason); the codes are
+    computed with the fp16-ROUNDED scale, so that the stored (s, z, q) are
+    self-consistent.
+
+    W: float array [N, K] (converted to fp32).  Returns
+    q uint8 [N, K], s16 float16 [K/group, N], z uint8 [K/group, N].
+    """
+    W = np.asarray(W, np.float32)
+    N, K = W.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    G = K // group
+    Wg = W.reshape(N, G, group)
+    mn = np.minimum(Wg.min(axis=2), np.float32(0))         # [N, G]
+    mx = np.maximum(Wg.max(axis=2), np.float32(0))
+    rng = np.maximum(mx - mn, np.float32(1e-5))
+    s16 = to_f16(rng / np.float32(15))                      # fp32 divide, then RNE to fp16
+    sf = s16.astype(np.float32)
+    z = np.clip(rne(-mn / sf), 0, 15).astype(np.float32)
+    q = np.clip(rne(Wg / sf[:, :, None]) + z[:, :, None], 0, 15)
+    return (q.reshape(N, K).astype(np.uint8),
+            np.ascontiguousarray(s16.T),
+            np.ascontiguousarray(z.T.astype(np.uint8)))
+
+
+def pack_canonical(q):
+    """Canonical int32 packing: 8 codes along K per 32-bit word, code i of a
+    word at bits 4i..4i+3, words indexed [k // 8, n] ([LQ] W4A16 section: the
+    packed word is sum_i q_i << 4i, [11, 6, 15, 0, 3, 9, 12, 7] -> 0x7C930F6B;
+    its tiled pseudocode indexes ``Wpacked[k0//8 ..., n0 ...]``).
+
+    q: uint [N, K] with K % 8 == 0.  Returns uint32 [K/8, N].
+    """
+    q = np.asarray(q).astype(np.uint32)
+    N, K = q.shape
+    words = np.zeros((K // 8, N), np.uint32)
+    for i in range(8):
+        words |= (q[:, i::8].T & np.uint32(0xF)) << np.uint32(4 * i)
+    return words
+
+
+def unpack_canonical(words):
+    """Inverse of ``pack_canonical``: shift right by 4i and mask with 0xF."""
+    words = np.asarray(words, np.uint32)
+    K8, N = words.shape
+    q = np.zeros((N, K8 * 8), np.uint8)
+    for i in range(8):
+        q[:, i::8] = ((words >> np.uint32(4 * i)) & np.uint32(0xF)).T
+    return q
+
+
+def dequantize_w4(q, s16, z, group=GROUP):
+    """Explicit dequantization x_hat = s * (q - z) in fp64 ([QK] §9.2;
+    [LQ] linear-quantization section).  Returns float64 [N, K]."""
+    q = np.asarray(q, np.float64)
+    N, K = q.shape
+    g_of_k = np.arange(K) // group
+    s = np.asarray(s16, np.float64)[g_of_k, :].T           # [N, K]
+    zz = np.asarray(z, np.float64)[g_of_k, :].T
+    return s * (q - zz)
+
+
+def w4a16_linear(X, q, s16, z, group=GROUP):
+    """Y64 = X · dequant(W)ᵀ in fp64 (the un-fused "dequantize, then GEMM" of
+    [QK] §9.5, which the fused kernel must reproduce).
+
+    X: float values [M, K] (already on the fp16/bf16 grid).  Returns float64 [M, N].
+    """
+    Wd = dequantize_w4(q, s16, z, group)
+    return np.asarray(X, np.float64) @ Wd.T
