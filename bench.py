@@ -1,0 +1,300 @@
+"""Throughput of the quantized linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-also]
+
+The main line is the W4A16 decode GEMV on the Llama-2-7B-shaped layers
+(M in {1, 4, 16} x (K, N) in {(4096, 4096), (4096, 11008), (11008, 4096)},
+g = 128, fp16 activations with 1% outlier channels).  One step runs all nine
+(M, K, N) cases once.  `value` is the effective bandwidth of a whole step:
+algorithmic bytes (packed weights + fp16 scales + 4-bit zeros + X + Y) over
+the step's wall time, inputs resident in HBM.  Each step reads a different
+copy of the weights (copies rotate so that the working set exceeds 1 GiB, four
+times the 256 MB Infinity Cache), so the weights come from HBM, not cache.
+
+The steps are replayed as HIP graphs (one graph per weight copy, nine
+launches each) to keep launch gaps out of the step; every graph's outputs
+are checked bit-for-bit against eager launches before timing.  Per-kernel
+durations for the roofline object come from a second pass of eager launches,
+each bracketed by HIP events on the launch stream.  The `also` object holds
+the other workloads (70B decode, W8A8 prefill GEMM, W4A16 prefill GEMM) timed
+the same way per kernel.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads as wl
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "i8": 5.0e15}   # dense, published
+METRIC = "W4A16 GEMV effective GB/s (% HBM peak); W8A8/W4A16 GEMM TOPS (% MFMA peak)"
+MALL_DEFEAT_BYTES = 1 << 30
+
+
+def w4a16_bytes(M, K, N, group=128, e=2):
+    """Algorithmic bytes of one W4A16 layer: packed codes, fp16 scales, 4-bit
+    zero points, X and Y (the data the method has to move, not the fp16 weights
+    it avoids)."""
+    return K * N // 2 + (K // group) * N * 2 + (K // group) * N // 2 + M * K * e + M * N * e
+
+
+def _events():
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _prepare_w4(ql, w, K, N, copies):
+    W = wl.weight(w, K, N)
+    wq, s, z = ql.q4_quantize_host(torch.from_numpy(W))
+    blob = ql.q4_pack(wq, s, z, N, K)
+    return W, [blob.to("cuda") for _ in range(copies)]
+
+
+def _copies_for(total_bytes):
+    return max(2, -(-MALL_DEFEAT_BYTES // max(total_bytes, 1)))
+
+
+def time_launches(fn_list, reps, stream):
+    """Eager launches, each bracketed by HIP events on `stream`; returns mean ms per entry."""
+    tot = np.zeros(len(fn_list))
+    pairs = [[_events() for _ in fn_list] for _ in range(reps)]
+    for r in range(reps):
+        for i, fn in enumerate(fn_list):
+            a, b = pairs[r][i]
+            a.record(stream)
+            fn(r)
+            b.record(stream)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for i in range(len(fn_list)):
+            a, b = pairs[r][i]
+            tot[i] += a.elapsed_time(b)
+    return tot / reps
+
+
+def bench_decode(ql, wname, steps, warmup, use_graphs=True):
+    """Runs a W4A16 decode workload; returns a dict of results."""
+    w = wl.WORKLOADS[wname]
+    cases = w.all_cases()
+    shapes = list(w.shapes)
+    blob_bytes = sum(ql.q4_packed_bytes(N, K) for (K, N) in shapes)
+    R = _copies_for(blob_bytes)
+    blobs = {}
+    for (K, N) in shapes:
+        _, blobs[(K, N)] = _prepare_w4(ql, w, K, N, R)
+    X = {c: wl.activations(w, c[0], c[1], c[2]).cuda() for c in cases}
+    Y = {c: torch.empty((c[0], c[2]), dtype=X[c].dtype, device="cuda") for c in cases}
+    ws = {c: torch.zeros(max(ql.q4_gemm_workspace_bytes(*c[:1], c[2], c[1]), 256), dtype=torch.uint8,
+                         device="cuda") for c in cases}
+    stream = torch.cuda.current_stream()
+
+    def launch(c, r):
+        M, K, N = c
+        ql.q4_gemm(X[c], blobs[(K, N)][r], N, Y=Y[c], ws=ws[c])
+
+    def step(r):
+        for c in cases:
+            launch(c, r)
+
+    for r in range(min(R, warmup + 1)):
+        step(r)
+    torch.cuda.synchronize()
+    bytes_step = sum(w4a16_bytes(*c) for c in cases)
+
+    graphs = None
+    if use_graphs:
+        ref = {}
+        for r in range(R):
+            step(r)
+            torch.cuda.synchronize()
+            ref[r] = {c: Y[c].clone() for c in cases}
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for rep in range(2):                      # every replay must equal the eager result
+            for r in range(R):
+                for c in cases:
+                    Y[c].zero_()
+                graphs[r].replay()
+                torch.cuda.synchronize()
+                for c in cases:
+                    if not torch.equal(Y[c], ref[r][c]):
+                        raise RuntimeError(f"graph replay {rep} of copy {r} differs from eager on case {c}")
+
+    run = (lambda i: graphs[i % R].replay()) if graphs else (lambda i: step(i % R))
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    a, b = _events()
+    a.record(stream)
+    for i in range(steps):
+        run(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / steps
+
+    # per-kernel durations (eager, event-bracketed) for the roofline
+    fns = [(lambda r, c=c: launch(c, r % R)) for c in cases]
+    per = time_launches(fns, max(steps, 10), stream)
+    kern_ms = float(per.sum())
+    per_case = []
+    for c, ms in zip(cases, per):
+        gbs = w4a16_bytes(*c) / (ms * 1e-3) / 1e9
+        per_case.append({"M": c[0], "K": c[1], "N": c[2], "us": round(ms * 1e3, 3),
+                         "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+    return {
+        "cases": cases, "bytes_step": bytes_step, "ms_step": ms_step,
+        "value_gbs": bytes_step / (ms_step * 1e-3) / 1e9,
+        "kernel_ms_step": kern_ms, "kernel_gbs": bytes_step / (kern_ms * 1e-3) / 1e9,
+        "per_case": per_case, "copies": R, "graphs": bool(graphs),
+    }
+
+
+def bench_w8a8(ql, reps):
+    w = wl.WORKLOADS["w8a8_prefill"]
+    M, (K, N) = w.Ms[0], w.shapes[0]
+    X = wl.activations(w, M, K, N).cuda()
+    Bq, s_b = ql.i8_quant_weight_host(torch.from_numpy(wl.weight(w, K, N)))
+    adj = ql.i8_azp_adj(Bq)
+    Bq, s_b, adj = Bq.cuda(), s_b.cuda(), adj.cuda()
+    bias = wl.bias(w, N).cuda()
+    Aq, s_a, azp = ql.i8_quant_per_token(X)
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    fq = lambda r: ql.i8_quant_per_token(X)
+    fg = lambda r: ql.i8_gemm_scaled(Aq, Bq, s_a, s_b, azp, adj, bias, out=out)
+    for _ in range(3):
+        fq(0)
+        fg(0)
+    torch.cuda.synchronize()
+    tq, tg = time_launches([fq, fg], reps, stream)
+    ops = 2.0 * M * N * K
+    qbytes = M * K * 2 + M * K + M * 4 + M * 4
+    return {"workload": w.name, "M": M, "K": K, "N": N,
+            "gemm_us": round(tg * 1e3, 2), "gemm_TOPS": round(ops / (tg * 1e-3) / 1e12, 1),
+            "gemm_frac_mfma_i8": round(ops / (tg * 1e-3) / MFMA_PEAK["i8"], 4),
+            "quant_us": round(tq * 1e3, 2), "quant_GBps": round(qbytes / (tq * 1e-3) / 1e9, 1),
+            "end_to_end_us": round((tq + tg) * 1e3, 2)}
+
+
+def bench_w4_prefill(ql, reps):
+    w = wl.WORKLOADS["w4a16_prefill"]
+    M, (K, N) = w.Ms[0], w.shapes[0]
+    _, blobs = _prepare_w4(ql, w, K, N, 1)
+    X = wl.activations(w, M, K, N).cuda()
+    Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
+    f = lambda r: ql.q4_gemm(X, blobs[0], N, Y=Y)
+    for _ in range(2):
+        f(0)
+    torch.cuda.synchronize()
+    (t,) = time_launches([f], reps, torch.cuda.current_stream())
+    ops = 2.0 * M * N * K
+    return {"workload": w.name, "M": M, "K": K, "N": N, "us": round(t * 1e3, 1),
+            "TFLOPS": round(ops / (t * 1e-3) / 1e12, 1), "frac_mfma_bf16": round(ops / (t * 1e-3) / MFMA_PEAK["bf16"], 4)}
+
+
+def cpu_baseline(budget_s=20.0):
+    """The oracle (explicit dequant + fp64 product), untuned, on the host cores,
+    over whole steps of the 7B decode workload until about budget_s seconds."""
+    from oracle import w4a16 as ow4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = wl.WORKLOADS["decode_7b"]
+    cases = w.all_cases()
+    prep = {}
+    for (K, N) in w.shapes:
+        prep[(K, N)] = ow4.quantize_w4(wl.weight(w, K, N))
+    Xs = {c: wl.as_f64(wl.activations(w, *c)) for c in cases}
+    nbytes, t0, done = 0, time.perf_counter(), 0
+    while True:
+        for c in cases:
+            q, s, z = prep[(c[1], c[2])]
+            ow4.w4a16_linear(Xs[c], q, s, z)
+            nbytes += w4a16_bytes(*c)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of the 9 (M, K, N) decode cases of the 7B workload in {dt:.1f} s "
+                      f"(explicit fp64 dequant + fp64 BLAS product per case; quantization untimed)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-graphs", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard "
+              "column-parallel with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import quantized_linear_layers_amd as ql
+    ql.lib()
+    torch.cuda.init()
+    dev = torch.cuda.get_device_properties(0)
+    print(f"# device: {dev.name} ({getattr(dev, 'gcnArchName', '?')}), {dev.multi_processor_count} CUs", flush=True)
+
+    main_res = bench_decode(ql, "decode_7b", args.steps, args.warmup, use_graphs=not args.no_graphs)
+    print(f"# decode_7b: {main_res['value_gbs']:.1f} GB/s per step, kernels {main_res['kernel_gbs']:.1f} GB/s",
+          flush=True)
+    also = {}
+    if not args.no_also:
+        r70 = bench_decode(ql, "decode_70b", max(10, args.steps // 2), args.warmup, use_graphs=not args.no_graphs)
+        also["decode_70b"] = {"workload": wl.WORKLOADS["decode_70b"].name, "step_GBps": round(r70["value_gbs"], 1),
+                              "kernel_GBps": round(r70["kernel_gbs"], 1),
+                              "frac_hbm": round(r70["kernel_gbs"] / HBM_PEAK_GBS, 4), "per_case": r70["per_case"]}
+        print(f"# decode_70b: kernels {r70['kernel_gbs']:.1f} GB/s", flush=True)
+        also["w8a8_prefill"] = bench_w8a8(ql, 20)
+        print(f"# w8a8: {also['w8a8_prefill']}", flush=True)
+        also["w4a16_prefill"] = bench_w4_prefill(ql, 10)
+        print(f"# w4a16 prefill: {also['w4a16_prefill']}", flush=True)
+
+    cpu = None if args.no_cpu else cpu_baseline()
+    achieved = main_res["kernel_gbs"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["value_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0, 0.02) fp32 weights quantized to uint4 g=128; fp16 N(0, 1) "
+                "activations with 1% channels x20)",
+        "config": {"workload": wl.WORKLOADS["decode_7b"].name, "cases_MKN": main_res["cases"], "group": 128,
+                   "bytes_per_step": main_res["bytes_step"], "weight_copies": main_res["copies"],
+                   "hip_graphs": main_res["graphs"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "q4_gemv_kernel", "per_case": main_res["per_case"]},
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,269 @@
+/*
+ * qlinear.h — C ABI of the MI355X (gfx950) quantized linear layer library
+ * (libqlinear.so).
+ *
+ * The layer is Y = X · Wᵀ with dequantization fused into the matrix product,
+ * in two modes:
+ *
+ *   W4A16  packed uint4 weights with one fp16 scale and one uint4 zero point
+ *          per group of 128 input channels; 16-bit activations; fp32
+ *          accumulation; x_fp ≈ s · (x_int − z).
+ *   W8A8   int8 × int8 products accumulated in int32, then a fused epilogue
+ *          out = s_a · s_b · (Dq − azp · azp_adj) + bias before the single store.
+ *
+ * Sources (page title, then the page's own section heading):
+ *   [QK] "第 9 章 量化 Kernel：INT8 / FP8 / INT4" (Quantization kernels:
+ *        INT8 / FP8 / INT4), yangyitao.com CUDA book, chapter 9.
+ *   [LQ] "LLM 与 AIGC 量化：从数值格式到 W4A4" (LLM and AIGC quantization:
+ *        from number formats to W4A4), valdrada.cn.
+ *   [VE] "vLLM W8A8 量化 GEMM 的 CUTLASS Epilogue 设计" (the CUTLASS
+ *        epilogue design of vLLM's W8A8 GEMM), blog.gitcode.com.
+ *
+ * Conventions shared by every entry point
+ *   - Shapes follow [LQ]'s notation: X is [M][K] (M tokens, K input
+ *     channels), W is [N][K] (N output channels, nn.Linear.weight layout),
+ *     Y is [M][N].  All matrices are dense row-major with no padding.
+ *   - Functions whose name ends in _host, and q4_pack / q4_unpack /
+ *     i8_azp_adj, are synchronous CPU functions on host memory.
+ *   - Every other function takes DEVICE pointers (memory of the current HIP
+ *     device) and a hipStream_t passed as `void* stream` (NULL = the null
+ *     stream).  It validates its arguments on the host, then enqueues its
+ *     kernels and returns without synchronizing.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     retains device memory, and keeps no device state between calls.
+ *   - Every function returns a ql_status.  Nothing aborts or throws across
+ *     the ABI.  On a non-OK return nothing was launched and nothing was
+ *     written, and ql_last_error() describes the failure (per thread).
+ *   - Device pointers must be 16-byte aligned.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QL_ABI_VERSION 1
+
+typedef enum {
+  QL_OK = 0,
+  QL_ERR_NULL = -1,         /* a required pointer is NULL                          */
+  QL_ERR_SHAPE = -2,        /* a size is negative, zero where not allowed, or inconsistent */
+  QL_ERR_DTYPE = -3,        /* unknown ql_dtype                                    */
+  QL_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned                    */
+  QL_ERR_UNSUPPORTED = -5,  /* a valid request this build does not implement       */
+  QL_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required          */
+  QL_ERR_HIP = -7,          /* the HIP runtime reported an error at launch          */
+  QL_ERR_RANGE = -8         /* an input value is outside the representable range   */
+} ql_status;
+
+typedef enum { QL_F16 = 0, QL_BF16 = 1 } ql_dtype;
+
+/* Message of the last non-OK return on the calling thread ("" if none). */
+const char* ql_last_error(void);
+
+/* QL_ABI_VERSION of the loaded library. */
+int ql_abi_version(void);
+
+/* =========================================================================
+ * W4A16 — offline weight preparation (host, CPU)
+ * ========================================================================= */
+
+/*
+ * q4_quantize_host — per-group asymmetric round-to-nearest to uint4.
+ *
+ * [QK] §9.3 (granularity: g = 128 consecutive input channels share a scale)
+ * and [LQ] "粒度" (granularity); [LQ] "对称与非对称" (asymmetric uint4 codes
+ * 0..15 with a zero point, the GPTQ/AWQ storage convention); the scale and
+ * zero point of a range from [LQ] "线性量化：一把刻度尺".  For each output
+ * channel n and group g, in IEEE fp32 with round-half-to-even:
+ *     mn = min(min w, 0), mx = max(max w, 0)
+ *     s  = fp16(max(mx − mn, 1e-5) / 15)
+ *     z  = clamp(round(−mn / s), 0, 15)
+ *     q  = clamp(round(w / s) + z, 0, 15)
+ * (the codes use the fp16-rounded scale, so the stored triple is consistent).
+ *
+ * W       [N][K] fp32, host.
+ * wq      [K/8][N] uint32 out: canonical packing, 8 codes along K per word,
+ *         the code of k = 8j + i at bits 4i..4i+3 of wq[j][n] ([LQ] W4A16
+ *         section: [11, 6, 15, 0, 3, 9, 12, 7] packs to 0x7C930F6B).
+ * scales  [K/group][N] fp16 bit patterns out.
+ * zeros   [K/group][N] uint8 out, values 0..15.
+ * Errors: QL_ERR_NULL; QL_ERR_SHAPE unless N > 0, K > 0, K % group == 0;
+ *         QL_ERR_UNSUPPORTED unless group == 128;
+ *         QL_ERR_RANGE if a group's range overflows the fp16 scale or W holds NaN.
+ */
+int q4_quantize_host(const float* W, int N, int K, int group,
+                     uint32_t* wq, uint16_t* scales, uint8_t* zeros);
+
+/*
+ * q4_packed_bytes — size of the device weight blob for an N x K layer.
+ * Returns 0 for invalid sizes (see q4_pack).
+ */
+size_t q4_packed_bytes(int N, int K, int group);
+
+/*
+ * q4_pack — canonical (wq, scales, zeros) to the gfx950 device blob (host).
+ *
+ * The blob keeps the int4 codes packed (the fused kernel reads only packed
+ * codes; [QK] §9.5) in an order chosen so that one 16-byte load per lane
+ * feeds the in-register unpack with no shuffles; kernels of other projects
+ * use other interleaves for the same reason ([LQ] W4A16 section), so blobs
+ * are not interchangeable with other formats.  Layout (N and K padded to
+ * Np = roundup(N, 64), Kp = roundup(K, 256) with code 0, scale 0, zero 0):
+ *   [0, 256)      header: "QL4P", version, N, K, group, Np, Kp
+ *   weights       [Np/64][Kp/32][64 lanes][16 bytes]: lane l of tile t owns
+ *                 output channel 64t + l; its 16 bytes hold 32 consecutive k
+ *                 as 4 words of 8 codes, the code of k = 8j + i sitting at
+ *                 nibble position (i & 1) * 4 + (i >> 1) of word j
+ *   scales        [Np/64][Kp/256][64][2] fp16: groups 2p, 2p+1 of a lane
+ *   zeros         [Np/64][Kp/256][64] bytes: zero of group 2p in the low
+ *                 nibble, of group 2p+1 in the high nibble
+ * (each region starts on a 256-byte boundary).
+ *
+ * packed: host buffer of packed_bytes >= q4_packed_bytes(N, K, group).
+ * Copy it to device memory (any 16-byte-aligned address) for q4_gemm.
+ * Errors: QL_ERR_NULL; QL_ERR_SHAPE as q4_quantize_host; QL_ERR_UNSUPPORTED
+ *         unless group == 128; QL_ERR_WORKSPACE if packed_bytes is too small;
+ *         QL_ERR_RANGE if a code or zero exceeds 15.
+ */
+int q4_pack(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros,
+            int N, int K, int group, void* packed, size_t packed_bytes);
+
+/*
+ * q4_unpack — inverse of q4_pack (host), for round-trip checks.
+ * Errors: as q4_pack; QL_ERR_SHAPE if the blob header disagrees with (N, K, group).
+ */
+int q4_unpack(const void* packed, size_t packed_bytes, int N, int K, int group,
+              uint32_t* wq, uint16_t* scales, uint8_t* zeros);
+
+/* =========================================================================
+ * W4A16 — forward (device)
+ * ========================================================================= */
+
+/*
+ * q4_gemm_workspace_bytes — device scratch q4_gemm needs for (M, N, K):
+ * split-K partial sums and per-tile arrival counters of the decode path.
+ * 0 when no scratch is needed.  The workspace must be zero-filled before its
+ * first use; every call that completes leaves its counters at zero again, so
+ * one workspace may be reused by consecutive calls on one stream (calls that
+ * overlap in time, e.g. on two streams, need separate workspaces).
+ */
+size_t q4_gemm_workspace_bytes(int M, int N, int K, int group);
+
+/*
+ * q4_gemm — Y = X · dequant(W)ᵀ with the dequantization fused into the product.
+ *
+ * Y[m][n] = Σ_k X[m][k] · s[k/128][n] · (q[n][k] − z[k/128][n]), fp32
+ * accumulation, one round-to-nearest-even to x_dtype at the store
+ * ([QK] §9.5 "关键 Kernel: Dequant + GEMM": INT4 stays packed in HBM and
+ * on chip and is expanded in registers right before the multiply; [LQ]
+ * W4A16 section and its tiled pseudocode; the scale rule of [LQ]
+ * "哪些 scale 能提到求和号外面": per-group scales along K are fine because
+ * the weights are expanded before the multiply).
+ *
+ * X       [M][K] fp16 or bf16 (x_dtype), device.
+ * packed  device blob from q4_pack for (N, K, group).
+ * Y       [M][N] out, same dtype as X, device.
+ * workspace / workspace_bytes: see q4_gemm_workspace_bytes (may be NULL / 0
+ *         when that returns 0).
+ * M <= 16 runs the split-K decode kernel; larger M the MFMA GEMM kernel.
+ * M == 0 or N == 0 is a no-op returning QL_OK.
+ * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M, N >= 0, K > 0,
+ *         K % group == 0; QL_ERR_UNSUPPORTED unless group == 128;
+ *         QL_ERR_ALIGN; QL_ERR_WORKSPACE; QL_ERR_HIP.
+ */
+int q4_gemm(const void* X, int x_dtype, int M, int K, int N,
+            const void* packed, int group, void* Y,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* =========================================================================
+ * W8A8
+ * ========================================================================= */
+
+/*
+ * i8_quant_weight_host — symmetric per-output-channel int8 weights (host).
+ * [LQ] "对称与非对称" (s = max|w| / 127, codes −127..127) and [LQ] W8A8
+ * section (weights per channel); [VE] "一、背景" (weights symmetric only).
+ * In IEEE fp32: s_b[n] = max(max_k |W[n][k]|, 1e-5) / 127,
+ *               Bq[n][k] = clamp(round(W[n][k] / s_b[n]), −127, 127).
+ * W [N][K] fp32; Bq [N][K] int8 out (the [N][K] rows are the columns of
+ * the page's column-major b); s_b [N] fp32 out.
+ * Errors: QL_ERR_NULL; QL_ERR_SHAPE unless N > 0, K > 0; QL_ERR_RANGE on NaN/inf.
+ */
+int i8_quant_weight_host(const float* W, int N, int K, int8_t* Bq, float* s_b);
+
+/*
+ * i8_azp_adj — azp_adj[n] = Σ_k Bq[n][k] (host), the row vector 1 · B̂ that
+ * every row of J_a · B̂ equals ([VE] "二、底层线性代数推导" and
+ * "五、azp_adj 的离线预计算": independent of scales and zero points, computed
+ * once when the weights are loaded).  For a per-tensor zero point the caller
+ * multiplies it by z_a itself ([VE] "2.3").
+ * Errors: QL_ERR_NULL; QL_ERR_SHAPE; QL_ERR_RANGE if a sum leaves int32.
+ */
+int i8_azp_adj(const int8_t* Bq, int N, int K, int32_t* azp_adj);
+
+/*
+ * i8_quant_per_token — dynamic per-token int8 activation quantization (device).
+ *
+ * Asymmetric (azp != NULL), per row m in IEEE fp32, round-half-to-even
+ * ([LQ] "线性量化" for (s, z) of a range; [LQ] "校准：静态与动态": per-token
+ * dynamic ranges at run time; int8 range [−128, 127] from [QK] §9.2; azp
+ * int32 per row from [VE] "4.1"):
+ *     mn = min(min_k x, 0), mx = max(max_k x, 0)
+ *     s_a[m] = max(mx − mn, 1e-5) / 255
+ *     azp[m] = −128 − round(mn / s_a[m])
+ *     Aq[m][k] = clamp(round(x / s_a[m]) + azp[m], −128, 127)
+ * Symmetric (azp == NULL): s_a = max(max_k |x|, 1e-5) / 127,
+ *     Aq = clamp(round(x / s_a), −127, 127).
+ * The division is a correctly rounded fp32 division, so codes are bit-exact
+ * with any IEEE implementation of the same steps.
+ *
+ * X [M][K] fp16/bf16; Aq [M][K] int8 out; s_a [M] fp32 out; azp [M] int32
+ * out or NULL.  M == 0 is a no-op.
+ * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M >= 0, K > 0 and
+ *         K % 8 == 0; QL_ERR_ALIGN; QL_ERR_HIP.
+ */
+int i8_quant_per_token(const void* X, int x_dtype, int M, int K,
+                       int8_t* Aq, float* s_a, int32_t* azp, void* stream);
+
+/*
+ * i8_gemm_scaled — int8 GEMM with int32 accumulation and the fused epilogue
+ * (device).
+ *
+ * Dq[m][n] = Σ_k Aq[m][k] · Bq[n][k]                       (int32)
+ * C[m][n]  = Dq − azp[m] · azp_adj[n]   if azp != NULL      ([VE] "2.4")
+ *          = Dq − azp_adj[n]            if azp == NULL, azp_adj != NULL
+ *                                       (azp_adj = z_a · 1·B̂, [VE] "2.3")
+ *          = Dq                         if both NULL        ([VE] "2.1", "2.2")
+ * out[m][n] = s_a[m] · (s_b[n] · float(C)) + bias[n]   (fp32; bias NULL → 0),
+ *             one round-to-nearest-even to out_dtype at the single store
+ * ([LQ] W8A8 section; [VE] "一、背景": fusing the scale and zero-point
+ * correction avoids writing and re-reading the int32 result; [VE] "3.4":
+ * the correction is a rank-1 term, O(M + N) memory).  C is exact while
+ * |C| < 2^31 (the int32 accumulator wraps beyond that).
+ *
+ * Aq [M][K] int8 row-major; Bq [N][K] int8 (each row one output channel;
+ * the page's column-major b).  s_a: s_a_len == 1 (per tensor) or M (per
+ * token); s_b: s_b_len == 1 or N (per channel) ([VE] "4.1").  azp [M] int32
+ * or NULL; azp_adj [N] int32 or NULL; bias [N] of out_dtype or NULL ([VE]
+ * "4.1": bias dtype equals the output dtype).  out [M][N] of out_dtype.
+ * raw_out: optional [M][N] int32 that receives C (for exact checks), or NULL.
+ * M == 0 or N == 0 is a no-op.
+ * Errors: QL_ERR_NULL (also azp without azp_adj); QL_ERR_DTYPE; QL_ERR_SHAPE
+ *         unless M, N >= 0, K > 0, K % 16 == 0, s_a_len in {1, M},
+ *         s_b_len in {1, N}; QL_ERR_ALIGN; QL_ERR_HIP.
+ */
+int i8_gemm_scaled(const int8_t* Aq, const int8_t* Bq, int M, int N, int K,
+                   const float* s_a, int s_a_len, const float* s_b, int s_b_len,
+                   const int32_t* azp, const int32_t* azp_adj, const void* bias,
+                   void* out, int out_dtype, int32_t* raw_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

@@ -1,0 +1,231 @@
+"""Python binding of libqlinear.so (the MI355X quantized linear layer).
+
+Argument marshalling only: every function here checks tensor dtypes, devices
+and shapes, allocates outputs with torch (device memory is torch's), and calls
+the C ABI function of the same name in ``include/qlinear.h``.  All arithmetic
+happens in the library (host C++ for the offline steps, HIP kernels for the
+forward).  There is no fallback: if the library is not built, importing works
+but every call raises.
+"""
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlinear.so")
+
+QL_F16, QL_BF16 = 0, 1
+GROUP = 128
+ABI_VERSION = 1
+
+_lib = None
+
+
+class QLError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QLError(f"{LIB_PATH} is missing: build it with `python -m quantized_linear_layers_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, I, Z = C.c_void_p, C.c_int, C.c_size_t
+        sig = {
+            "ql_last_error": (C.c_char_p, []),
+            "ql_abi_version": (I, []),
+            "q4_quantize_host": (I, [P, I, I, I, P, P, P]),
+            "q4_packed_bytes": (Z, [I, I, I]),
+            "q4_pack": (I, [P, P, P, I, I, I, P, Z]),
+            "q4_unpack": (I, [P, Z, I, I, I, P, P, P]),
+            "q4_gemm_workspace_bytes": (Z, [I, I, I, I]),
+            "q4_gemm": (I, [P, I, I, I, I, P, I, P, P, Z, P]),
+            "i8_quant_weight_host": (I, [P, I, I, P, P]),
+            "i8_azp_adj": (I, [P, I, I, P]),
+            "i8_quant_per_token": (I, [P, I, I, I, P, P, P, P]),
+            "i8_gemm_scaled": (I, [P, P, I, I, I, P, I, P, I, P, P, P, P, I, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        if L.ql_abi_version() != ABI_VERSION:
+            raise QLError(f"libqlinear ABI {L.ql_abi_version()} != {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def _check(rc, fn):
+    if rc != 0:
+        raise QLError(f"{fn} returned {rc}: {lib().ql_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.float16:
+        return QL_F16
+    if dt == torch.bfloat16:
+        return QL_BF16
+    raise QLError(f"unsupported activation dtype {dt}")
+
+
+def _host(t, dtype):
+    if t.device.type != "cpu" or t.dtype != dtype or not t.is_contiguous():
+        raise QLError(f"expected a contiguous CPU {dtype} tensor, got {t.dtype} on {t.device}")
+    return t
+
+
+def _dev(t, dtype=None, name="tensor"):
+    if t.device.type != "cuda" or not t.is_contiguous():
+        raise QLError(f"{name}: expected a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise QLError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t
+
+
+# ---------------------------------------------------------------- W4A16 offline (host)
+
+def q4_quantize_host(W, group=GROUP):
+    """W: CPU fp32 [N, K] -> (wq uint32 [K/8, N] as int32, scales fp16 [K/g, N], zeros uint8 [K/g, N])."""
+    W = _host(W, torch.float32)
+    N, K = W.shape
+    wq = torch.empty((K // 8, N), dtype=torch.int32)
+    scales = torch.empty((K // group, N), dtype=torch.float16)
+    zeros = torch.empty((K // group, N), dtype=torch.uint8)
+    _check(lib().q4_quantize_host(_ptr(W), N, K, group, _ptr(wq), _ptr(scales), _ptr(zeros)), "q4_quantize_host")
+    return wq, scales, zeros
+
+
+def q4_packed_bytes(N, K, group=GROUP):
+    return int(lib().q4_packed_bytes(N, K, group))
+
+
+def q4_pack(wq, scales, zeros, N, K, group=GROUP, device=None):
+    """Canonical host triple -> device blob (uint8 tensor on `device`, CPU if None)."""
+    wq = _host(wq, torch.int32)
+    scales = _host(scales, torch.float16)
+    zeros = _host(zeros, torch.uint8)
+    nb = q4_packed_bytes(N, K, group)
+    if nb == 0:
+        raise QLError(f"q4_pack: invalid shape N={N} K={K} group={group}")
+    blob = torch.empty(nb, dtype=torch.uint8)
+    _check(lib().q4_pack(_ptr(wq), _ptr(scales), _ptr(zeros), N, K, group, _ptr(blob), nb), "q4_pack")
+    return blob if device is None else blob.to(device)
+
+
+def q4_unpack(blob, N, K, group=GROUP):
+    blob = blob.cpu().contiguous()
+    wq = torch.empty((K // 8, N), dtype=torch.int32)
+    scales = torch.empty((K // group, N), dtype=torch.float16)
+    zeros = torch.empty((K // group, N), dtype=torch.uint8)
+    _check(lib().q4_unpack(_ptr(blob), blob.numel(), N, K, group, _ptr(wq), _ptr(scales), _ptr(zeros)), "q4_unpack")
+    return wq, scales, zeros
+
+
+# ---------------------------------------------------------------- W4A16 forward (device)
+
+_ws_cache = {}
+
+
+def q4_gemm_workspace_bytes(M, N, K, group=GROUP):
+    return int(lib().q4_gemm_workspace_bytes(M, N, K, group))
+
+
+def workspace(device, nbytes):
+    """A zero-filled device scratch buffer of at least nbytes, cached per device.
+    The library leaves it zero-filled after every completed call."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def q4_gemm(X, packed, N, group=GROUP, Y=None, ws=None, stream=None):
+    """Y[M, N] = X[M, K] · dequant(W)ᵀ; X fp16/bf16 on the device, packed from q4_pack."""
+    X = _dev(X, name="X")
+    _dev(packed, torch.uint8, "packed")
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    else:
+        _dev(Y, X.dtype, "Y")
+    nb = q4_gemm_workspace_bytes(M, N, K, group)
+    if ws is None and nb:
+        ws = workspace(X.device, nb)
+    _check(lib().q4_gemm(_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), group, _ptr(Y),
+                         _ptr(ws), 0 if ws is None else ws.numel(), _stream(X, stream)), "q4_gemm")
+    return Y
+
+
+# ---------------------------------------------------------------- W8A8
+
+def i8_quant_weight_host(W):
+    """CPU fp32 [N, K] -> (Bq int8 [N, K], s_b fp32 [N])."""
+    W = _host(W, torch.float32)
+    N, K = W.shape
+    Bq = torch.empty((N, K), dtype=torch.int8)
+    s_b = torch.empty(N, dtype=torch.float32)
+    _check(lib().i8_quant_weight_host(_ptr(W), N, K, _ptr(Bq), _ptr(s_b)), "i8_quant_weight_host")
+    return Bq, s_b
+
+
+def i8_azp_adj(Bq):
+    """CPU int8 [N, K] -> int32 [N] row sums."""
+    Bq = _host(Bq, torch.int8)
+    N, K = Bq.shape
+    adj = torch.empty(N, dtype=torch.int32)
+    _check(lib().i8_azp_adj(_ptr(Bq), N, K, _ptr(adj)), "i8_azp_adj")
+    return adj
+
+
+def i8_quant_per_token(X, symmetric=False, stream=None):
+    """X fp16/bf16 [M, K] on the device -> (Aq int8 [M, K], s_a fp32 [M], azp int32 [M] or None)."""
+    X = _dev(X, name="X")
+    M, K = X.shape
+    Aq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    s_a = torch.empty(M, dtype=torch.float32, device=X.device)
+    azp = None if symmetric else torch.empty(M, dtype=torch.int32, device=X.device)
+    _check(lib().i8_quant_per_token(_ptr(X), _dtype_code(X.dtype), M, K, _ptr(Aq), _ptr(s_a), _ptr(azp),
+                                    _stream(X, stream)), "i8_quant_per_token")
+    return Aq, s_a, azp
+
+
+def i8_gemm_scaled(Aq, Bq, s_a, s_b, azp=None, azp_adj=None, bias=None, out_dtype=torch.float16,
+                   raw=False, out=None, stream=None):
+    """out[M, N] = s_a * s_b * (Aq·Bqᵀ - azp * azp_adj) + bias, on the device.
+    With raw=True also returns the int32 corrected accumulator."""
+    _dev(Aq, torch.int8, "Aq")
+    _dev(Bq, torch.int8, "Bq")
+    _dev(s_a, torch.float32, "s_a")
+    _dev(s_b, torch.float32, "s_b")
+    for t, n in ((azp, "azp"), (azp_adj, "azp_adj")):
+        if t is not None:
+            _dev(t, torch.int32, n)
+    if bias is not None:
+        _dev(bias, out_dtype, "bias")
+    M, K = Aq.shape
+    N = Bq.shape[0]
+    if Bq.shape[1] != K:
+        raise QLError("Aq and Bq disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=Aq.device)
+    rawt = torch.empty((M, N), dtype=torch.int32, device=Aq.device) if raw else None
+    _check(lib().i8_gemm_scaled(_ptr(Aq), _ptr(Bq), M, N, K, _ptr(s_a), s_a.numel(), _ptr(s_b), s_b.numel(),
+                                _ptr(azp), _ptr(azp_adj), _ptr(bias), _ptr(out), _dtype_code(out_dtype),
+                                _ptr(rawt), _stream(Aq, stream)), "i8_gemm_scaled")
+    return (out, rawt) if raw else out

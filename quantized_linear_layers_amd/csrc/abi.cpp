@@ -1,0 +1,115 @@
+// The C ABI of libqlinear.so: argument validation on the host, then one or
+// more asynchronous launches on the caller's stream.  No allocation, no
+// synchronization, no device state.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/qlinear.h"
+#include "ql_internal.h"
+
+namespace ql {
+
+static thread_local std::string g_last_error;
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+}  // namespace ql
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return QL_OK;
+  return ql::set_error(QL_ERR_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+}
+
+bool valid_dtype(int d) { return d == QL_F16 || d == QL_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ql_last_error(void) { return ql::g_last_error.c_str(); }
+
+int ql_abi_version(void) { return QL_ABI_VERSION; }
+
+size_t q4_gemm_workspace_bytes(int M, int N, int K, int group) {
+  if (M <= 0 || N <= 0 || K <= 0 || group != ql::kGroup || K % group) return 0;
+  if (M > 16) return 0;
+  return ql::plan_q4_gemv(M, N, K).ws_bytes;
+}
+
+int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed, int group, void* Y,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K <= 0)
+    return ql::set_error(QL_ERR_SHAPE, "q4_gemm: need M >= 0, N >= 0, K > 0 (got %d, %d, %d)", M, N, K);
+  if (group != ql::kGroup)
+    return ql::set_error(QL_ERR_UNSUPPORTED, "q4_gemm: group=%d; this build supports group=128", group);
+  if (K % group) return ql::set_error(QL_ERR_SHAPE, "q4_gemm: K=%d is not a multiple of group=%d", K, group);
+  if (!valid_dtype(x_dtype)) return ql::set_error(QL_ERR_DTYPE, "q4_gemm: x_dtype=%d", x_dtype);
+  if (M == 0 || N == 0) return QL_OK;
+  if (!X || !packed || !Y) return ql::set_error(QL_ERR_NULL, "q4_gemm: NULL X, packed or Y");
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(Y))
+    return ql::set_error(QL_ERR_ALIGN, "q4_gemm: X, packed and Y must be 16-byte aligned");
+  const ql::Q4Layout L = ql::q4_layout(N, K);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = x_dtype == QL_BF16;
+  if (M <= 16) {
+    const ql::GemvPlan P = ql::plan_q4_gemv(M, N, K);
+    if (P.ws_bytes) {
+      if (!workspace) return ql::set_error(QL_ERR_WORKSPACE, "q4_gemm: workspace of %zu bytes required", P.ws_bytes);
+      if (workspace_bytes < P.ws_bytes)
+        return ql::set_error(QL_ERR_WORKSPACE, "q4_gemm: workspace_bytes=%zu < %zu", workspace_bytes, P.ws_bytes);
+      if (!aligned16(workspace)) return ql::set_error(QL_ERR_ALIGN, "q4_gemm: workspace must be 16-byte aligned");
+    }
+    return hip_status("q4_gemm", ql::launch_q4_gemv(X, bf16, M, K, N, static_cast<const uint8_t*>(packed),
+                                                     L, P, workspace, Y, st));
+  }
+  return hip_status("q4_gemm", ql::launch_q4_gemm(X, bf16, M, K, N, static_cast<const uint8_t*>(packed), L, Y, st));
+}
+
+int i8_quant_per_token(const void* X, int x_dtype, int M, int K, int8_t* Aq, float* s_a, int32_t* azp,
+                       void* stream) {
+  if (M < 0 || K <= 0 || K % 8)
+    return ql::set_error(QL_ERR_SHAPE, "i8_quant_per_token: need M >= 0, K > 0, K %% 8 == 0 (got %d, %d)", M, K);
+  if (!valid_dtype(x_dtype)) return ql::set_error(QL_ERR_DTYPE, "i8_quant_per_token: x_dtype=%d", x_dtype);
+  if (M == 0) return QL_OK;
+  if (!X || !Aq || !s_a) return ql::set_error(QL_ERR_NULL, "i8_quant_per_token: NULL X, Aq or s_a");
+  if (!aligned16(X) || !aligned16(Aq) || !aligned16(s_a) || (azp && !aligned16(azp)))
+    return ql::set_error(QL_ERR_ALIGN, "i8_quant_per_token: pointers must be 16-byte aligned");
+  return hip_status("i8_quant_per_token",
+                    ql::launch_i8_quant(X, x_dtype == QL_BF16, M, K, Aq, s_a, azp, static_cast<hipStream_t>(stream)));
+}
+
+int i8_gemm_scaled(const int8_t* Aq, const int8_t* Bq, int M, int N, int K, const float* s_a, int s_a_len,
+                   const float* s_b, int s_b_len, const int32_t* azp, const int32_t* azp_adj, const void* bias,
+                   void* out, int out_dtype, int32_t* raw_out, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 16)
+    return ql::set_error(QL_ERR_SHAPE, "i8_gemm_scaled: need M, N >= 0, K > 0, K %% 16 == 0 (got %d, %d, %d)", M, N, K);
+  if (!valid_dtype(out_dtype)) return ql::set_error(QL_ERR_DTYPE, "i8_gemm_scaled: out_dtype=%d", out_dtype);
+  if (M == 0 || N == 0) return QL_OK;
+  if (s_a_len != 1 && s_a_len != M)
+    return ql::set_error(QL_ERR_SHAPE, "i8_gemm_scaled: s_a_len=%d must be 1 or M=%d", s_a_len, M);
+  if (s_b_len != 1 && s_b_len != N)
+    return ql::set_error(QL_ERR_SHAPE, "i8_gemm_scaled: s_b_len=%d must be 1 or N=%d", s_b_len, N);
+  if (!Aq || !Bq || !s_a || !s_b || !out) return ql::set_error(QL_ERR_NULL, "i8_gemm_scaled: NULL operand");
+  if (azp && !azp_adj) return ql::set_error(QL_ERR_NULL, "i8_gemm_scaled: azp given without azp_adj");
+  const void* ptrs[] = {Aq, Bq, s_a, s_b, azp, azp_adj, bias, out, raw_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return ql::set_error(QL_ERR_ALIGN, "i8_gemm_scaled: pointers must be 16-byte aligned");
+  ql::I8Epi e{s_a, s_a_len != 1, s_b, s_b_len != 1, azp, azp_adj, bias, out, out_dtype == QL_BF16, raw_out};
+  return hip_status("i8_gemm_scaled", ql::launch_i8_gemm(Aq, Bq, M, N, K, e, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

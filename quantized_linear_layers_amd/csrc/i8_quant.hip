@@ -1,0 +1,123 @@
+// Dynamic per-token int8 activation quantization: one workgroup per row.
+//
+// The row's range is found with one reduction ([LQ] "校准：静态与动态":
+// per-token absmax/range at run time costs one extra reduction), then the
+// scale, the int32 zero point and the codes follow the formulas in qlinear.h
+// with IEEE fp32 division and round-half-to-even, so every code is decided
+// exactly as a scalar CPU implementation of the same steps decides it.
+// The row is read from HBM once: up to 8 pieces of 8 values per thread stay
+// in registers between the reduction and the quantization.
+#include <hip/hip_runtime.h>
+
+#include "ql_internal.h"
+
+namespace ql {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRegPieces = 8;     // 8 x 8 values per thread kept in registers (K <= 16384)
+
+__device__ inline float half_lo(uint32_t v, bool bf16) {
+  return bf16 ? __builtin_bit_cast(float, v << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ inline float half_hi(uint32_t v, bool bf16) {
+  return bf16 ? __builtin_bit_cast(float, v & 0xFFFF0000u) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+template <bool BF16, bool ASYM>
+__global__ __launch_bounds__(kThreads) void i8_quant_kernel(const uint16_t* __restrict__ X, int K,
+                                                             int8_t* __restrict__ Aq, float* __restrict__ s_a,
+                                                             int32_t* __restrict__ azp) {
+  __shared__ float red[2][kThreads / 64];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* x = X + (size_t)m * K;
+  const int pieces = K / 8;
+
+  uint4 v[kRegPieces];
+  float mn = 0.0f, mx = 0.0f;       // the range always contains 0
+  auto fold = [&](uint4 p) {
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = half_lo(w[i], BF16), b = half_hi(w[i], BF16);
+      if (ASYM) {
+        mn = fminf(mn, fminf(a, b));
+        mx = fmaxf(mx, fmaxf(a, b));
+      } else {
+        mx = fmaxf(mx, fmaxf(fabsf(a), fabsf(b)));
+      }
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < kRegPieces; ++r) {
+    const int p = tid + r * kThreads;
+    v[r] = p < pieces ? reinterpret_cast<const uint4*>(x)[p] : make_uint4(0, 0, 0, 0);
+    if (p < pieces) fold(v[r]);
+  }
+  for (int p = tid + kRegPieces * kThreads; p < pieces; p += kThreads) fold(reinterpret_cast<const uint4*>(x)[p]);
+
+  // ---- row reduction: wave shuffles, then across the four waves
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = mn;
+    red[1][tid >> 6] = mx;
+  }
+  __syncthreads();
+  mn = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
+  mx = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+
+  float s, z;
+  if (ASYM) {
+    s = fmaxf(mx - mn, 1e-5f) / 255.0f;
+    z = -128.0f - rintf(mn / s);
+  } else {
+    s = fmaxf(mx, 1e-5f) / 127.0f;
+    z = 0.0f;
+  }
+  if (tid == 0) {
+    s_a[m] = s;
+    if (ASYM) azp[m] = (int32_t)z;
+  }
+  const float lo = ASYM ? -128.0f : -127.0f;
+
+  auto quant = [&](uint4 p) -> uint2 {
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+    uint32_t out[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = fminf(fmaxf(rintf(half_lo(w[i], BF16) / s) + z, lo), 127.0f);
+      const float b = fminf(fmaxf(rintf(half_hi(w[i], BF16) / s) + z, lo), 127.0f);
+      const uint32_t qa = (uint32_t)(int32_t)a & 0xFFu, qb = (uint32_t)(int32_t)b & 0xFFu;
+      out[i >> 1] |= (qa | (qb << 8)) << (16 * (i & 1));
+    }
+    return make_uint2(out[0], out[1]);
+  };
+  uint2* q = reinterpret_cast<uint2*>(Aq + (size_t)m * K);
+#pragma unroll
+  for (int r = 0; r < kRegPieces; ++r) {
+    const int p = tid + r * kThreads;
+    if (p < pieces) q[p] = quant(v[r]);
+  }
+  for (int p = tid + kRegPieces * kThreads; p < pieces; p += kThreads) q[p] = quant(reinterpret_cast<const uint4*>(x)[p]);
+}
+
+}  // namespace
+
+hipError_t launch_i8_quant(const void* X, bool bf16, int M, int K, int8_t* Aq, float* s_a, int32_t* azp,
+                           hipStream_t st) {
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  if (bf16) {
+    if (azp) hipLaunchKernelGGL((i8_quant_kernel<true, true>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
+    else hipLaunchKernelGGL((i8_quant_kernel<true, false>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
+  } else {
+    if (azp) hipLaunchKernelGGL((i8_quant_kernel<false, true>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
+    else hipLaunchKernelGGL((i8_quant_kernel<false, false>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ql

@@ -1,0 +1,155 @@
+"""The C ABI on the CPU: the library loads and exports every declared symbol,
+host-side validation returns the documented error codes before any launch,
+and the host (offline) functions are bit-exact with the oracle."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_linear_layers_amd as ql
+import workloads as wl
+from oracle import w4a16 as ow4
+from oracle import w8a8 as ow8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+QL_OK, QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED, QL_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6
+QL_ERR_RANGE = -8
+
+FAKE = C.c_void_p(0x10000)          # aligned, never dereferenced: validation fails first
+FAKE_MIS = C.c_void_p(0x10008)      # 8-byte aligned only
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qlinear.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\**([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ql.lib()
+    names = declared_functions()
+    assert len(names) == 12, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.ql_abi_version() == ql.ABI_VERSION
+
+
+def last_error():
+    return ql.lib().ql_last_error().decode()
+
+
+def test_q4_gemm_validation():
+    L = ql.lib()
+    P = FAKE
+    # K not a multiple of the group
+    assert L.q4_gemm(P, 0, 1, 200, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_SHAPE
+    assert "multiple" in last_error()
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, 64, P, P, 1 << 20, None) == QL_ERR_UNSUPPORTED
+    assert L.q4_gemm(P, 7, 1, 256, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_DTYPE
+    assert L.q4_gemm(P, 0, -1, 256, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_SHAPE
+    assert L.q4_gemm(P, 0, 1, 0, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_SHAPE
+    assert L.q4_gemm(None, 0, 1, 256, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_NULL
+    assert L.q4_gemm(FAKE_MIS, 0, 1, 256, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_ALIGN
+    # empty problems are no-ops
+    assert L.q4_gemm(None, 0, 0, 256, 64, None, 128, None, None, 0, None) == QL_OK
+    assert L.q4_gemm(None, 0, 4, 256, 0, None, 128, None, None, 0, None) == QL_OK
+    # a split-K decode shape needs a workspace
+    M, N, K = 1, 4096, 4096
+    need = L.q4_gemm_workspace_bytes(M, N, K, 128)
+    assert need > 0
+    assert L.q4_gemm(P, 0, M, K, N, P, 128, P, None, 0, None) == QL_ERR_WORKSPACE
+    assert L.q4_gemm(P, 0, M, K, N, P, 128, P, P, need - 1, None) == QL_ERR_WORKSPACE
+    assert L.q4_gemm_workspace_bytes(4096, 4096, 4096, 128) == 0
+
+
+def test_i8_validation():
+    L = ql.lib()
+    P = FAKE
+    assert L.i8_quant_per_token(P, 0, 4, 12, P, P, P, None) == QL_ERR_SHAPE       # K % 8
+    assert L.i8_quant_per_token(P, 3, 4, 16, P, P, P, None) == QL_ERR_DTYPE
+    assert L.i8_quant_per_token(None, 0, 4, 16, P, P, P, None) == QL_ERR_NULL
+    assert L.i8_quant_per_token(P, 0, 0, 16, None, None, None, None) == QL_OK
+    args = dict(Aq=P, Bq=P, M=4, N=8, K=32, s_a=P, sal=4, s_b=P, sbl=8, azp=P, adj=P, bias=P, out=P, od=0, raw=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.i8_gemm_scaled(a["Aq"], a["Bq"], a["M"], a["N"], a["K"], a["s_a"], a["sal"], a["s_b"], a["sbl"],
+                                a["azp"], a["adj"], a["bias"], a["out"], a["od"], a["raw"], None)
+    assert call(K=24) == QL_ERR_SHAPE
+    assert call(sal=2) == QL_ERR_SHAPE
+    assert call(sbl=3) == QL_ERR_SHAPE
+    assert call(od=9) == QL_ERR_DTYPE
+    assert call(adj=None) == QL_ERR_NULL              # azp without azp_adj
+    assert call(s_b=None) == QL_ERR_NULL
+    assert call(bias=FAKE_MIS) == QL_ERR_ALIGN
+    assert call(M=0, Aq=None) == QL_OK
+
+
+# ---------------------------------------------------------------- host functions vs oracle
+
+def _w4_roundtrip(W, group=128):
+    N, K = W.shape
+    wq, s, z = ql.q4_quantize_host(torch.from_numpy(W), group)
+    q_o, s_o, z_o = ow4.quantize_w4(W, group)
+    assert np.array_equal(wq.numpy().view(np.uint32), ow4.pack_canonical(q_o))
+    assert np.array_equal(s.numpy().view(np.uint16), s_o.view(np.uint16))
+    assert np.array_equal(z.numpy(), z_o)
+    blob = ql.q4_pack(wq, s, z, N, K, group)
+    assert blob.numel() == ql.q4_packed_bytes(N, K, group)
+    wq2, s2, z2 = ql.q4_unpack(blob, N, K, group)
+    assert torch.equal(wq2, wq) and torch.equal(s2.view(torch.int16), s.view(torch.int16)) and torch.equal(z2, z)
+    return blob
+
+
+@pytest.mark.parametrize("N,K", [(256, 256), (200, 384), (64, 128), (1, 128)])
+def test_q4_quantize_pack_small(N, K):
+    W = (np.random.default_rng(N * 7 + K).standard_normal((N, K)) * 0.02).astype(np.float32)
+    _w4_roundtrip(W)
+
+
+def test_q4_quantize_workload_layer():
+    w = wl.WORKLOADS["decode_7b"]
+    _w4_roundtrip(wl.weight(w, 4096, 4096))
+
+
+def test_q4_blob_layout_positions():
+    """The documented device layout: code of (n, k) at tile n//64, chunk k//32,
+    lane n%64, word (k%32)//8, nibble position (i&1)*4 + (i>>1), i = k%8."""
+    N, K = 128, 256
+    q = np.random.default_rng(5).integers(0, 16, (N, K)).astype(np.uint8)
+    wq = torch.from_numpy(ow4.pack_canonical(q).view(np.int32))
+    s = torch.zeros((K // 128, N), dtype=torch.float16)
+    z = torch.zeros((K // 128, N), dtype=torch.uint8)
+    blob = ql.q4_pack(wq, s, z, N, K).numpy()
+    Kp = 256
+    for n, k in [(0, 0), (1, 1), (63, 31), (64, 32), (100, 255), (127, 130)]:
+        t, l, c, j, i = n // 64, n % 64, k // 32, (k % 32) // 8, k % 8
+        off = 256 + ((t * (Kp // 32) + c) * 64 + l) * 16 + j * 4
+        word = int(blob[off:off + 4].view(np.uint32)[0])
+        assert (word >> (4 * ((i & 1) * 4 + (i >> 1)))) & 0xF == q[n, k]
+
+
+def test_q4_host_errors():
+    W = torch.zeros((4, 200), dtype=torch.float32)
+    with pytest.raises(ql.QLError, match="-2"):
+        ql.q4_quantize_host(W)
+    W = torch.zeros((4, 256), dtype=torch.float32)
+    W[0, 3] = float("nan")
+    with pytest.raises(ql.QLError, match="-8"):
+        ql.q4_quantize_host(W)
+
+
+def test_i8_weight_prep_vs_oracle():
+    w = wl.WORKLOADS["w8a8_prefill"]
+    W = wl.weight(w, 4096, 4096)
+    Bq, s_b = ql.i8_quant_weight_host(torch.from_numpy(W))
+    Bq_o, s_b_o = ow8.quant_weight_per_channel_sym(W)
+    assert np.array_equal(Bq.numpy(), Bq_o)
+    assert np.array_equal(s_b.numpy().view(np.uint32), s_b_o.view(np.uint32))
+    adj = ql.i8_azp_adj(Bq)
+    assert np.array_equal(adj.numpy(), ow8.azp_adj(Bq_o))

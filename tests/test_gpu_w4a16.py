@@ -1,0 +1,124 @@
+"""W4A16 parity on the GPU: q4_gemm (decode kernel for M <= 16, MFMA GEMM
+above) against the oracle's explicit-dequant fp64 product.
+
+Bar: max|Y_dev - Y64| / max|Y64| <= 1e-2 (Y64 = the oracle's fp64 result
+before rounding to the 16-bit output type).  Expected values are always the
+oracle's own (its own quantization of the same seeded fp32 weights); the
+device side quantizes with the library's host function, which is bit-exact
+with the oracle (tests/test_abi.py).  Layers too big for a full fp64 product
+are checked on sampled output channels and rows, which the oracle computes
+one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_linear_layers_amd as ql
+import workloads as wl
+from oracle import w4a16 as ow4
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+_layers = {}
+
+
+def device_layer(W):
+    key = (W.shape, float(W[0, 0]), float(W[-1, -1]))
+    if key not in _layers:
+        N, K = W.shape
+        wq, s, z = ql.q4_quantize_host(torch.from_numpy(W))
+        _layers[key] = ql.q4_pack(wq, s, z, N, K, device="cuda")
+    return _layers[key]
+
+
+def rel_err(Yd, Y64):
+    return float(np.abs(Yd - Y64).max() / max(np.abs(Y64).max(), 1e-30))
+
+
+def check(W, X, rows=None, cols=None, tol=TOL):
+    """Run the device layer on X and compare the (rows, cols) block with the oracle."""
+    N, K = W.shape
+    blob = device_layer(W)
+    Y = ql.q4_gemm(X.cuda(), blob, N)
+    torch.cuda.synchronize()
+    Yd = wl.as_f64(Y.cpu())
+    rows = np.arange(X.shape[0]) if rows is None else rows
+    cols = np.arange(N) if cols is None else cols
+    q, s, z = ow4.quantize_w4(W[cols])
+    Y64 = ow4.w4a16_linear(wl.as_f64(X)[rows], q, s, z)
+    e = rel_err(Yd[np.ix_(rows, cols)], Y64)
+    assert e <= tol, f"relative error {e:.3e}"
+    assert np.all(np.isfinite(Yd))
+    return e
+
+
+# ---------------------------------------------------------------- the workloads
+
+def test_tiny_gemv():
+    w = wl.WORKLOADS["tiny_gemv"]
+    W = wl.weight(w, 256, 256)
+    X = wl.activations(w, 1, 256, 256)
+    check(W, X)
+
+
+@pytest.mark.parametrize("K,N", wl.WORKLOADS["decode_7b"].shapes)
+@pytest.mark.parametrize("M", wl.WORKLOADS["decode_7b"].Ms)
+def test_decode_7b(M, K, N):
+    w = wl.WORKLOADS["decode_7b"]
+    check(wl.weight(w, K, N), wl.activations(w, M, K, N))
+
+
+@pytest.mark.parametrize("K,N", wl.WORKLOADS["decode_70b"].shapes)
+@pytest.mark.parametrize("M", wl.WORKLOADS["decode_70b"].Ms)
+def test_decode_70b_sampled(M, K, N):
+    w = wl.WORKLOADS["decode_70b"]
+    W = wl.weight(w, K, N)
+    cols = np.sort(np.random.default_rng(K + N + M).choice(N, 384, replace=False))
+    check(W, wl.activations(w, M, K, N), cols=cols)
+
+
+def test_prefill_sampled():
+    w = wl.WORKLOADS["w4a16_prefill"]
+    M, (K, N) = w.Ms[0], w.shapes[0]
+    W = wl.weight(w, K, N)
+    r = np.random.default_rng(3)
+    rows = np.sort(r.choice(M, 96, replace=False))
+    cols = np.sort(r.choice(N, 256, replace=False))
+    check(W, wl.activations(w, M, K, N), rows=rows, cols=cols)
+
+
+# ---------------------------------------------------------------- ragged shapes and edges
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16, 17, 40, 130])
+@pytest.mark.parametrize("K,N", [(128, 72), (384, 200), (1152, 1000), (2560, 64)])
+def test_ragged(M, K, N, dtype):
+    r = np.random.default_rng(M * 1000 + K + N)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
+    check(W, X)
+
+
+def test_workspace_reuse_and_zero_input():
+    """Two calls in a row on one workspace (the arrival counters reset) and
+    an all-zero activation gives exactly zero."""
+    w = wl.WORKLOADS["decode_7b"]
+    W = wl.weight(w, 4096, 11008)
+    X = wl.activations(w, 4, 4096, 11008)
+    e1 = check(W, X)
+    e2 = check(W, X)
+    assert e1 == e2
+    blob = device_layer(W)
+    Y = ql.q4_gemm(torch.zeros((3, 4096), dtype=torch.float16, device="cuda"), blob, 11008)
+    assert torch.count_nonzero(Y).item() == 0
+
+
+def test_large_activation_values():
+    """Outlier-heavy bf16 activations (values up to ~1e4) stay within the bar."""
+    r = np.random.default_rng(99)
+    W = (r.standard_normal((512, 1024)) * 0.02).astype(np.float32)
+    Xf = r.standard_normal((4, 1024)).astype(np.float32)
+    Xf[:, ::97] *= 5000.0
+    check(W, torch.from_numpy(Xf).to(torch.bfloat16))

@@ -1,0 +1,119 @@
+"""W8A8 parity on the GPU.
+
+i8_quant_per_token: codes, zero points and fp32 scales bit-exact with the
+oracle (both decide the codes in IEEE fp32 with round-half-to-even).
+i8_gemm_scaled: the int32 corrected accumulator (raw_out) bit-exact with the
+oracle's exact integer product, the fp16/bf16 output within
+max|out - out64| / max|out64| <= 1e-2.  The GEMM's inputs are the oracle's
+own quantized operands.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_linear_layers_amd as ql
+import workloads as wl
+from oracle import w8a8 as ow8
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def cu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_quant(X, symmetric=False):
+    Aq, s_a, azp = ql.i8_quant_per_token(X.cuda(), symmetric=symmetric)
+    torch.cuda.synchronize()
+    Xf = wl.as_f64(X).astype(np.float32)
+    if symmetric:
+        Aq_o, s_o = ow8.quant_per_token_sym(Xf)
+        assert azp is None
+    else:
+        Aq_o, s_o, azp_o = ow8.quant_per_token_asym(Xf)
+        assert np.array_equal(azp.cpu().numpy(), azp_o)
+    assert np.array_equal(s_a.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(Aq.cpu().numpy(), Aq_o)
+
+
+def check_gemm(Aq, Bq, s_a, s_b, azp=None, adj=None, bias=None, out_dtype=torch.float16):
+    out, raw = ql.i8_gemm_scaled(cu(Aq), cu(Bq), cu(s_a), cu(s_b),
+                                 None if azp is None else cu(azp), None if adj is None else cu(adj),
+                                 None if bias is None else bias.cuda(), out_dtype=out_dtype, raw=True)
+    torch.cuda.synchronize()
+    C, out64 = ow8.w8a8_linear(Aq, Bq, s_a, s_b, azp, adj, None if bias is None else wl.as_f64(bias))
+    assert np.array_equal(raw.cpu().numpy().astype(np.int64), C)
+    od = wl.as_f64(out.cpu())
+    e = float(np.abs(od - out64).max() / np.abs(out64).max())
+    assert e <= TOL, f"relative error {e:.3e}"
+
+
+# ---------------------------------------------------------------- the workload
+
+def test_w8a8_prefill_workload():
+    w = wl.WORKLOADS["w8a8_prefill"]
+    M, (K, N) = w.Ms[0], w.shapes[0]
+    X = wl.activations(w, M, K, N)
+    check_quant(X)
+    Aq, s_a, azp = ow8.quant_per_token_asym(wl.as_f64(X).astype(np.float32))
+    Bq, s_b = ow8.quant_weight_per_channel_sym(wl.weight(w, K, N))
+    check_gemm(Aq, Bq, s_a, s_b, azp, ow8.azp_adj(Bq), wl.bias(w, N))
+
+
+# ---------------------------------------------------------------- variants and edges
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("M,K", [(1, 8), (3, 40), (7, 4096), (5, 20000), (64, 1000)])
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_quant_shapes(M, K, dtype, symmetric):
+    r = np.random.default_rng(M * 31 + K)
+    Xf = (r.standard_normal((M, K)) * 3 + 0.5).astype(np.float32)
+    X = torch.from_numpy(Xf).to(dtype)
+    check_quant(X, symmetric)
+
+
+def test_quant_degenerate_rows():
+    X = torch.zeros((4, 64), dtype=torch.float16)
+    X[1] = 2.0                     # constant positive row: mn = 0
+    X[2] = -3.0                    # constant negative row: mx = 0
+    X[3, 5] = 65504.0              # fp16 max
+    check_quant(X)
+    check_quant(X, symmetric=True)
+
+
+def _operands(M, N, K, seed):
+    r = np.random.default_rng(seed)
+    Xf = (r.standard_normal((M, K)) + 0.3).astype(np.float32)
+    Aq, s_a, azp = ow8.quant_per_token_asym(Xf)
+    Bq, s_b = ow8.quant_weight_per_channel_sym((r.standard_normal((N, K)) * 0.02).astype(np.float32))
+    return Aq, s_a, azp, Bq, s_b
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (5, 40, 48), (130, 72, 96), (256, 384, 512), (300, 260, 1040)])
+def test_gemm_ragged(M, N, K):
+    Aq, s_a, azp, Bq, s_b = _operands(M, N, K, M + N + K)
+    bias = torch.from_numpy(np.random.default_rng(1).standard_normal(N).astype(np.float32) * 0.1).half()
+    check_gemm(Aq, Bq, s_a, s_b, azp, ow8.azp_adj(Bq), bias)
+
+
+def test_gemm_epilogue_variants():
+    M, N, K = 96, 136, 256
+    Aq, s_a, azp, Bq, s_b = _operands(M, N, K, 5)
+    adj = ow8.azp_adj(Bq)
+    check_gemm(Aq, Bq, s_a, s_b)                                   # symmetric, no bias
+    check_gemm(Aq, Bq, s_a[:1], s_b[:1])                           # per-tensor scales
+    check_gemm(Aq, Bq, s_a, s_b, None, (17 * adj).astype(np.int32))   # per-tensor zero point folded in
+    b16 = torch.from_numpy(np.linspace(-1, 1, N).astype(np.float32)).to(torch.bfloat16)
+    check_gemm(Aq, Bq, s_a, s_b, azp, adj, b16, out_dtype=torch.bfloat16)
+
+
+def test_gemm_extreme_codes():
+    """All codes at the int8 extremes: Dq reaches 128 * 127 * K exactly."""
+    M, N, K = 64, 64, 4096
+    Aq = np.full((M, K), -128, np.int8)
+    Bq = np.full((N, K), -127, np.int8)
+    s_a = np.full(M, 1e-3, np.float32)
+    s_b = np.full(N, 1e-4, np.float32)
+    check_gemm(Aq, Bq, s_a, s_b)
