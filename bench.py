@@ -89,13 +89,11 @@ def bench_decode(ql, wname, steps, warmup, use_graphs=True):
         _, blobs[(K, N)] = _prepare_w4(ql, w, K, N, R)
     X = {c: wl.activations(w, c[0], c[1], c[2]).cuda() for c in cases}
     Y = {c: torch.empty((c[0], c[2]), dtype=X[c].dtype, device="cuda") for c in cases}
-    ws = {c: torch.zeros(max(ql.q4_gemm_workspace_bytes(*c[:1], c[2], c[1]), 256), dtype=torch.uint8,
-                         device="cuda") for c in cases}
     stream = torch.cuda.current_stream()
 
     def launch(c, r):
         M, K, N = c
-        ql.q4_gemm(X[c], blobs[(K, N)][r], N, Y=Y[c], ws=ws[c])
+        ql.q4_gemm(X[c], blobs[(K, N)][r], N, Y=Y[c])
 
     def step(r):
         for c in cases:

@@ -55,7 +55,7 @@ typedef enum {
   QL_ERR_DTYPE = -3,        /* unknown ql_dtype                                    */
   QL_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned                    */
   QL_ERR_UNSUPPORTED = -5,  /* a valid request this build does not implement       */
-  QL_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required          */
+  QL_ERR_SIZE = -6,         /* a buffer is smaller than the shape requires         */
   QL_ERR_HIP = -7,          /* the HIP runtime reported an error at launch          */
   QL_ERR_RANGE = -8         /* an input value is outside the representable range   */
 } ql_status;
@@ -127,7 +127,7 @@ size_t q4_packed_bytes(int N, int K, int group);
  * packed: host buffer of packed_bytes >= q4_packed_bytes(N, K, group).
  * Copy it to device memory (any 16-byte-aligned address) for q4_gemm.
  * Errors: QL_ERR_NULL; QL_ERR_SHAPE as q4_quantize_host; QL_ERR_UNSUPPORTED
- *         unless group == 128; QL_ERR_WORKSPACE if packed_bytes is too small;
+ *         unless group == 128; QL_ERR_SIZE if packed_bytes is too small;
  *         QL_ERR_RANGE if a code or zero exceeds 15.
  */
 int q4_pack(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros,
@@ -145,16 +145,6 @@ int q4_unpack(const void* packed, size_t packed_bytes, int N, int K, int group,
  * ========================================================================= */
 
 /*
- * q4_gemm_workspace_bytes — device scratch q4_gemm needs for (M, N, K):
- * split-K partial sums and per-tile arrival counters of the decode path.
- * 0 when no scratch is needed.  The workspace must be zero-filled before its
- * first use; every call that completes leaves its counters at zero again, so
- * one workspace may be reused by consecutive calls on one stream (calls that
- * overlap in time, e.g. on two streams, need separate workspaces).
- */
-size_t q4_gemm_workspace_bytes(int M, int N, int K, int group);
-
-/*
  * q4_gemm — Y = X · dequant(W)ᵀ with the dequantization fused into the product.
  *
  * Y[m][n] = Σ_k X[m][k] · s[k/128][n] · (q[n][k] − z[k/128][n]), fp32
@@ -166,19 +156,19 @@ size_t q4_gemm_workspace_bytes(int M, int N, int K, int group);
  * the weights are expanded before the multiply).
  *
  * X       [M][K] fp16 or bf16 (x_dtype), device.
- * packed  device blob from q4_pack for (N, K, group).
+ * packed  device blob from q4_pack for (N, K, group), of packed_bytes bytes
+ *         (at least q4_packed_bytes(N, K, group)).
  * Y       [M][N] out, same dtype as X, device.
- * workspace / workspace_bytes: see q4_gemm_workspace_bytes (may be NULL / 0
- *         when that returns 0).
- * M <= 16 runs the split-K decode kernel; larger M the MFMA GEMM kernel.
+ * M <= 16 runs the decode kernel (each workgroup owns 16 output channels for
+ * all of K); larger M the LDS-tiled MFMA GEMM.  Neither needs device scratch.
  * M == 0 or N == 0 is a no-op returning QL_OK.
  * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M, N >= 0, K > 0,
  *         K % group == 0; QL_ERR_UNSUPPORTED unless group == 128;
- *         QL_ERR_ALIGN; QL_ERR_WORKSPACE; QL_ERR_HIP.
+ *         QL_ERR_SIZE if packed_bytes < q4_packed_bytes(N, K, group);
+ *         QL_ERR_ALIGN; QL_ERR_HIP.
  */
 int q4_gemm(const void* X, int x_dtype, int M, int K, int N,
-            const void* packed, int group, void* Y,
-            void* workspace, size_t workspace_bytes, void* stream);
+            const void* packed, size_t packed_bytes, int group, void* Y, void* stream);
 
 /* =========================================================================
  * W8A8

@@ -42,8 +42,7 @@ def lib():
             "q4_packed_bytes": (Z, [I, I, I]),
             "q4_pack": (I, [P, P, P, I, I, I, P, Z]),
             "q4_unpack": (I, [P, Z, I, I, I, P, P, P]),
-            "q4_gemm_workspace_bytes": (Z, [I, I, I, I]),
-            "q4_gemm": (I, [P, I, I, I, I, P, I, P, P, Z, P]),
+            "q4_gemm": (I, [P, I, I, I, I, P, Z, I, P, P]),
             "i8_quant_weight_host": (I, [P, I, I, P, P]),
             "i8_azp_adj": (I, [P, I, I, P]),
             "i8_quant_per_token": (I, [P, I, I, I, P, P, P, P]),
@@ -136,26 +135,7 @@ def q4_unpack(blob, N, K, group=GROUP):
 
 # ---------------------------------------------------------------- W4A16 forward (device)
 
-_ws_cache = {}
-
-
-def q4_gemm_workspace_bytes(M, N, K, group=GROUP):
-    return int(lib().q4_gemm_workspace_bytes(M, N, K, group))
-
-
-def workspace(device, nbytes):
-    """A zero-filled device scratch buffer of at least nbytes, cached per device.
-    The library leaves it zero-filled after every completed call."""
-    dev = torch.device(device)
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
-    ws = _ws_cache.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        _ws_cache[key] = ws
-    return ws
-
-
-def q4_gemm(X, packed, N, group=GROUP, Y=None, ws=None, stream=None):
+def q4_gemm(X, packed, N, group=GROUP, Y=None, stream=None):
     """Y[M, N] = X[M, K] · dequant(W)ᵀ; X fp16/bf16 on the device, packed from q4_pack."""
     X = _dev(X, name="X")
     _dev(packed, torch.uint8, "packed")
@@ -164,11 +144,8 @@ def q4_gemm(X, packed, N, group=GROUP, Y=None, ws=None, stream=None):
         Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
     else:
         _dev(Y, X.dtype, "Y")
-    nb = q4_gemm_workspace_bytes(M, N, K, group)
-    if ws is None and nb:
-        ws = workspace(X.device, nb)
-    _check(lib().q4_gemm(_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), group, _ptr(Y),
-                         _ptr(ws), 0 if ws is None else ws.numel(), _stream(X, stream)), "q4_gemm")
+    _check(lib().q4_gemm(_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group, _ptr(Y),
+                         _stream(X, stream)), "q4_gemm")
     return Y
 
 

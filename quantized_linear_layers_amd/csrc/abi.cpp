@@ -44,14 +44,8 @@ const char* ql_last_error(void) { return ql::g_last_error.c_str(); }
 
 int ql_abi_version(void) { return QL_ABI_VERSION; }
 
-size_t q4_gemm_workspace_bytes(int M, int N, int K, int group) {
-  if (M <= 0 || N <= 0 || K <= 0 || group != ql::kGroup || K % group) return 0;
-  if (M > 16) return 0;
-  return ql::plan_q4_gemv(M, N, K).ws_bytes;
-}
-
-int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed, int group, void* Y,
-            void* workspace, size_t workspace_bytes, void* stream) {
+int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed, size_t packed_bytes, int group,
+            void* Y, void* stream) {
   if (M < 0 || N < 0 || K <= 0)
     return ql::set_error(QL_ERR_SHAPE, "q4_gemm: need M >= 0, N >= 0, K > 0 (got %d, %d, %d)", M, N, K);
   if (group != ql::kGroup)
@@ -63,18 +57,14 @@ int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed,
   if (!aligned16(X) || !aligned16(packed) || !aligned16(Y))
     return ql::set_error(QL_ERR_ALIGN, "q4_gemm: X, packed and Y must be 16-byte aligned");
   const ql::Q4Layout L = ql::q4_layout(N, K);
+  if (packed_bytes < L.bytes)
+    return ql::set_error(QL_ERR_SIZE, "q4_gemm: packed_bytes=%zu < %zu for N=%d K=%d", packed_bytes, L.bytes, N, K);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = x_dtype == QL_BF16;
   if (M <= 16) {
     const ql::GemvPlan P = ql::plan_q4_gemv(M, N, K);
-    if (P.ws_bytes) {
-      if (!workspace) return ql::set_error(QL_ERR_WORKSPACE, "q4_gemm: workspace of %zu bytes required", P.ws_bytes);
-      if (workspace_bytes < P.ws_bytes)
-        return ql::set_error(QL_ERR_WORKSPACE, "q4_gemm: workspace_bytes=%zu < %zu", workspace_bytes, P.ws_bytes);
-      if (!aligned16(workspace)) return ql::set_error(QL_ERR_ALIGN, "q4_gemm: workspace must be 16-byte aligned");
-    }
     return hip_status("q4_gemm", ql::launch_q4_gemv(X, bf16, M, K, N, static_cast<const uint8_t*>(packed),
-                                                     L, P, workspace, Y, st));
+                                                     L, P, Y, st));
   }
   return hip_status("q4_gemm", ql::launch_q4_gemm(X, bf16, M, K, N, static_cast<const uint8_t*>(packed), L, Y, st));
 }

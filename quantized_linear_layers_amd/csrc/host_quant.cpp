@@ -126,7 +126,7 @@ int q4_pack(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros, in
   if (int e = check_q4_shape("q4_pack", N, K, group)) return e;
   const ql::Q4Layout L = ql::q4_layout(N, K);
   if (packed_bytes < L.bytes)
-    return ql::set_error(QL_ERR_WORKSPACE, "q4_pack: packed_bytes=%zu < %zu", packed_bytes, L.bytes);
+    return ql::set_error(QL_ERR_SIZE, "q4_pack: packed_bytes=%zu < %zu", packed_bytes, L.bytes);
   const int G = K / group;
   for (int g = 0; g < G; ++g)
     for (int n = 0; n < N; ++n)
@@ -161,7 +161,7 @@ int q4_unpack(const void* packed, size_t packed_bytes, int N, int K, int group, 
   if (int e = check_q4_shape("q4_unpack", N, K, group)) return e;
   const ql::Q4Layout L = ql::q4_layout(N, K);
   if (packed_bytes < L.bytes)
-    return ql::set_error(QL_ERR_WORKSPACE, "q4_unpack: packed_bytes=%zu < %zu", packed_bytes, L.bytes);
+    return ql::set_error(QL_ERR_SIZE, "q4_unpack: packed_bytes=%zu < %zu", packed_bytes, L.bytes);
   const uint8_t* in = static_cast<const uint8_t*>(packed);
   BlobHeader h;
   memcpy(&h, in, sizeof h);

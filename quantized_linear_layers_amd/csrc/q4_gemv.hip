@@ -1,29 +1,34 @@
 // W4A16 decode kernel (M <= 16): Y[m][n] = sum_k X[m][k] * s * (q - z).
 //
-// The step that dominates decode is streaming the packed weights from HBM
-// once per token ([QK] §9.1: batch-1 decode reads every weight once; [LQ]
-// "带宽与算力：Roofline": at a few tokens the arithmetic intensity is about
-// the token count, far below the ridge).  So this kernel is built around the
-// weight stream:
-//   * lane l of a wave owns output channel 64t + l of layout tile t and reads
-//     its 32 consecutive k as one 16-byte load; 64 lanes read 1 KB
-//     contiguous, and consecutive workgroups walk consecutive memory;
-//   * the codes are expanded in registers ([QK] §9.5, §9.6): a nibble ORed
-//     into the low mantissa bits of fp16 1024.0 (0x6400) or bf16 128.0
-//     (0x4300) is the exact number 1024 + q (128 + q) with one AND-OR per
-//     pair of weights; for fp16 the mask 0x00F000F0 gives 1024 + 16q for the
-//     next pair without a shift;
-//   * the offsets and the zero point are not subtracted per weight: per group
-//     the kernel accumulates sum x*(off + q) with packed dot products and
-//     removes (off + z) * sum x once per group (the zero-point expansion of
-//     [LQ] W8A8 section / [VE] "二", applied per group), then applies the
-//     group scale, so the inner loop is one AND-OR plus one dot2 per pair;
-//   * X of the workgroup's K range is staged once in LDS and read as
-//     broadcast (every lane reads the same address); per-(row, group) sums
-//     of X are formed while staging;
-//   * the four waves of a workgroup split the K range and reduce in LDS;
-//     workgroups split K further and the last one to arrive on a column
-//     tile adds the fp32 partials in split order (deterministic) and stores Y.
+// Decode is bound by streaming the packed weights from HBM once per token
+// ([QK] §9.1: batch-1 decode reads every weight once per token; [LQ]
+// "带宽与算力：Roofline": with a few tokens the arithmetic intensity is about
+// the token count, far below the ridge point), so the kernel is organised
+// around that stream and keeps everything else off the critical path:
+//
+//   * a workgroup owns 16 * NT output channels for the whole of K, so no
+//     partial sums ever leave the workgroup (cross-workgroup reductions need
+//     device-scope cache write-backs on this multi-XCD part, which cost far
+//     more than the layer itself); NT (1, 2 or 4) is the largest that still
+//     gives every compute unit a workgroup;
+//   * lane l of a wave reads output channel l % 16 of each of its NT 16-column
+//     slices, K-block l / 16: one 16-byte load per lane and slice covers 4
+//     consecutive 32-channel chunks x 16 channels = one 128-wide group,
+//     256-byte contiguous runs in the packed blob;
+//   * the activation fragment of a group is loaded once and used for all NT
+//     slices, which keeps activation loads from crowding out weight loads;
+//   * the codes stay packed until they are in registers ([QK] §9.5): an AND
+//     with 0x000F000F and an OR with the bit pattern of fp16 1024.0 (0x6400)
+//     or bf16 128.0 (0x4300) turns a pair of nibbles into the exact pair
+//     (off + q0, off + q1) ([QK] §9.6);
+//   * the 16-bit products and their fp32 sums run on the matrix unit
+//     (v_mfma_f32_16x16x32_{f16,bf16}, one row per token, up to 16 tokens),
+//     which leaves the vector ALU to the unpacking; the same A operand times
+//     a constant B = -(off + z) in a second accumulator chain removes the
+//     offset and the zero point exactly (the zero-point expansion of [LQ]'s
+//     W8A8 section and [VE] "二", applied per group), and the group scale is
+//     applied once per group to the 4 accumulators of a lane;
+//   * the waves of a workgroup split K and add their 16 x 16 tiles in LDS.
 #include <hip/hip_runtime.h>
 
 #include "ql_internal.h"
@@ -31,8 +36,9 @@
 namespace ql {
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct GemvArgs {
   const uint16_t* X;
@@ -40,274 +46,193 @@ struct GemvArgs {
   const uint4* W;          // [Np/64][Kp/32][64] chunks
   const uint32_t* S;       // [Np/64][Kp/256][64] scale pairs
   const uint8_t* Z;        // [Np/64][Kp/256][64] zero pairs
-  int kw;                  // K per wave (multiple of 256)
-  int splits;              // workgroups along K per tile
-  float* part;             // [splits][M][Np]
-  unsigned* cnt;           // [Np/64]
   uint16_t* Y;             // [M][N]
 };
 
-__device__ inline float dot2_f16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
-}
-__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
-}
-__device__ inline float h2f(uint32_t bits16) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-__device__ inline float lo_f(uint32_t v, bool bf16) {
-  return bf16 ? __builtin_bit_cast(float, v << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
-}
-__device__ inline float hi_f(uint32_t v, bool bf16) {
-  return bf16 ? __builtin_bit_cast(float, v & 0xFFFF0000u) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-__device__ inline uint16_t to_out(float y, bool bf16) {
-  return bf16 ? __builtin_bit_cast(uint16_t, (__bf16)y) : __builtin_bit_cast(uint16_t, (_Float16)y);
+template <bool BF16>
+__device__ inline f32x4 mfma(const uint4& a, const uint4& b, const f32x4& c) {
+  if (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-template <int MT, bool BF16>
-__device__ inline void group_dot(const uint4 (&w)[4], const uint16_t* xs, int xstride, int xk, float (&acc_a)[MT],
-                                 float (&acc_b)[MT]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t ww[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t v = ww[j];
-      uint32_t p0, p1, p2, p3;
-      if (BF16) {
-        p0 = (v & 0x000F000Fu) | 0x43004300u;
-        p1 = ((v >> 4) & 0x000F000Fu) | 0x43004300u;
-        p2 = ((v >> 8) & 0x000F000Fu) | 0x43004300u;
-        p3 = ((v >> 12) & 0x000F000Fu) | 0x43004300u;
-      } else {
-        const uint32_t v8 = v >> 8;
-        p0 = (v & 0x000F000Fu) | 0x64006400u;    // k 0,1  -> 1024 + q
-        p1 = (v & 0x00F000F0u) | 0x64006400u;    // k 2,3  -> 1024 + 16 q
-        p2 = (v8 & 0x000F000Fu) | 0x64006400u;   // k 4,5  -> 1024 + q
-        p3 = (v8 & 0x00F000F0u) | 0x64006400u;   // k 6,7  -> 1024 + 16 q
-      }
-      const int k = xk + c * 32 + j * 8;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const uint4 x = *reinterpret_cast<const uint4*>(xs + m * xstride + k);
-        if (BF16) {
-          acc_a[m] = dot2_bf16(x.x, p0, acc_a[m]);
-          acc_a[m] = dot2_bf16(x.y, p1, acc_a[m]);
-          acc_a[m] = dot2_bf16(x.z, p2, acc_a[m]);
-          acc_a[m] = dot2_bf16(x.w, p3, acc_a[m]);
-        } else {
-          acc_a[m] = dot2_f16(x.x, p0, acc_a[m]);
-          acc_b[m] = dot2_f16(x.y, p1, acc_b[m]);
-          acc_a[m] = dot2_f16(x.z, p2, acc_a[m]);
-          acc_b[m] = dot2_f16(x.w, p3, acc_b[m]);
-        }
-      }
-    }
-  }
+// word of 8 codes (code of k = 2i at bits 4i, of k = 2i + 1 at bits 16 + 4i)
+// -> 4 registers of 16-bit pairs (off + q_{2i}, off + q_{2i+1})
+template <bool BF16>
+__device__ inline uint4 unpack8(uint32_t w) {
+  const uint32_t magic = BF16 ? 0x43004300u : 0x64006400u;
+  return make_uint4((w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic, ((w >> 8) & 0x000F000Fu) | magic,
+                    ((w >> 12) & 0x000F000Fu) | magic);
 }
 
-template <int MT, bool BF16>
-__global__ __launch_bounds__(256) void q4_gemv_kernel(GemvArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int kwg = 4 * a.kw;                 // K range of the workgroup
-  const int ngw = kwg / kGroup;             // groups of the workgroup
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                      // [MT][kwg]
-  float* csum = reinterpret_cast<float*>(smem + (size_t)MT * kwg * 2);    // [MT][ngw][2]
-  float* red = csum + MT * ngw * 2;                                        // [4][MT][64]
+template <bool BF16>
+__device__ inline uint32_t neg_offset_pair(uint32_t z) {
+  const float v = -((BF16 ? 128.0f : 1024.0f) + (float)z);   // exact in both 16-bit types
+  const uint32_t h = BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+  return h | (h << 16);
+}
 
-  const int tile = blockIdx.x / a.splits;
-  const int split = blockIdx.x % a.splits;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kb = split * kwg;
-  const int kend = min(kb + kwg, a.Kp);
-  const int k0 = kb + wave * a.kw;
-  const int npairs = max(0, (min(k0 + a.kw, kend) - k0) / kPairK);
-
-  // ---- issue the first weight loads before anything else (latency hiding)
+// NT: 16-column slices per wave; U: groups per step (NT * U weight loads of
+// 16 bytes per lane per step, next step's in flight while a step computes)
+template <bool BF16, int NT, int U>
+__global__ __launch_bounds__(512) void q4_gemv_kernel(GemvArgs a) {
+  __shared__ f32x4 red[8][NT][64];
+  const int nw = blockDim.x >> 6;
+  // the wave index is uniform; saying so keeps the K loop a scalar loop
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int cl = lane & 15, blk = lane >> 4;
   const int ck = a.Kp / kChunkK, pk = a.Kp / kPairK;
-  const uint4* wp = a.W + ((size_t)tile * ck + k0 / kChunkK) * kTileN + lane;
-  const uint32_t* sp = a.S + ((size_t)tile * pk + k0 / kPairK) * kTileN + lane;
-  const uint8_t* zp = a.Z + ((size_t)tile * pk + k0 / kPairK) * kTileN + lane;
-  uint4 bufA[8], bufB[8];
-  uint32_t sA = 0, sB = 0, zA = 0, zB = 0;
-  if (npairs > 0) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) bufA[c] = wp[c * kTileN];
-    sA = sp[0];
-    zA = zp[0];
-  }
+  const int G = a.K / kGroup;
+  const int gpw = (G + nw - 1) / nw;
+  const int g0 = min(G, wave * gpw), g1 = min(G, g0 + gpw);
+  const int gl = max(G - 1, 0);
 
-  // ---- stage X[0:MT][kb:kb+kwg] in LDS and form per-(row, group) sums
-  {
-    const int per_row = kwg / 8;                 // 16-byte pieces per row
-    const int total = MT * per_row;
-    for (int idx = threadIdx.x; idx < total; idx += 256) {
-      const int m = idx / per_row, kc = idx % per_row;
-      const int k = kb + kc * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < a.M && k < a.K) v = *reinterpret_cast<const uint4*>(a.X + (size_t)m * a.K + k);
-      *reinterpret_cast<uint4*>(xs + m * kwg + kc * 8) = v;
-      // k offsets 0,1,4,5 of every 8 are the "1024 + q" pairs, 2,3,6,7 the "1024 + 16 q" pairs
-      float sa = lo_f(v.x, BF16) + hi_f(v.x, BF16) + lo_f(v.z, BF16) + hi_f(v.z, BF16);
-      float sb = lo_f(v.y, BF16) + hi_f(v.y, BF16) + lo_f(v.w, BF16) + hi_f(v.w, BF16);
+  const uint4* wp[NT];
+  const uint32_t* sp[NT];
+  const uint8_t* zp[NT];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        sa += __shfl_xor(sa, o, 16);
-        sb += __shfl_xor(sb, o, 16);
-      }
-      if ((kc & 15) == 0) {
-        const int gi = kc / 16;
-        float c1, c2;
-        if (BF16) {
-          c2 = sa + sb;
-          c1 = 128.0f * c2;
-        } else {
-          c1 = 1024.0f * sa + 64.0f * sb;
-          c2 = sa + sb;
-        }
-        csum[(m * ngw + gi) * 2 + 0] = c1;
-        csum[(m * ngw + gi) * 2 + 1] = c2;
+  for (int t = 0; t < NT; ++t) {
+    const int slice = blockIdx.x * NT + t;                  // 16-column slice
+    const int tile = slice >> 2, sub = slice & 3;           // 64-column layout tile
+    wp[t] = a.W + ((size_t)tile * ck + blk) * kTileN + sub * 16 + cl;   // + 4*64*g for group g
+    sp[t] = a.S + (size_t)tile * pk * kTileN + sub * 16 + cl;           // + 64*(g/2)
+    zp[t] = a.Z + (size_t)tile * pk * kTileN + sub * 16 + cl;
+  }
+  const bool row_ok = cl < a.M;                                           // A-operand row of this lane
+  const uint32_t rmask = row_ok ? 0xFFFFFFFFu : 0u;
+  const uint16_t* xp = a.X + (size_t)(row_ok ? cl : 0) * a.K + blk * kChunkK;   // + 128*g + 8*j
+
+  // All loads are branch-free (indices clamped into the layer, unused values
+  // discarded) and issued in the order they are consumed, so the in-order
+  // vector-memory counter only ever waits for data that is needed next:
+  // weights run one step ahead of their use, and a step's activations, scales
+  // and zero points are issued before the next step's weights.
+  auto load_w = [&](int t, int g) { return wp[t][(size_t)min(g, gl) * 4 * kTileN]; };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto step = [&](int gs, const uint4 (&wcur)[U][NT], uint4 (&wnxt)[U][NT]) {
+    uint4 x[U][4];
+    uint32_t sw[U][NT], zw[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = min(gs + u, gl);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[u][j] = *reinterpret_cast<const uint4*>(xp + (size_t)g * kGroup + 8 * j);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        sw[u][t] = sp[t][(size_t)(g >> 1) * kTileN];
+        zw[u][t] = zp[t][(size_t)(g >> 1) * kTileN];
       }
     }
-  }
-  __syncthreads();
-
-  // ---- main loop: one pair of groups (8 chunks, 256 k) per step, next pair prefetched
-  float y[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) y[m] = 0.0f;
-
-  auto consume = [&](const uint4 (&buf)[8], uint32_t sdw, uint32_t zb, int p) {
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float acc_a[MT], acc_b[MT];
+      for (int t = 0; t < NT; ++t) wnxt[u][t] = load_w(t, gs + U + u);
+    // keep the loads above ahead of the arithmetic below (the scheduler would
+    // otherwise sink them to save registers and serialize their latency)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc_a[m] = acc_b[m] = 0.0f;
-      const uint4 w4[4] = {buf[h * 4 + 0], buf[h * 4 + 1], buf[h * 4 + 2], buf[h * 4 + 3]};
-      const int xk = wave * a.kw + p * kPairK + h * kGroup;     // offset in the staged X
-      group_dot<MT, BF16>(w4, xs, kwg, xk, acc_a, acc_b);
-      const float s = h2f(sdw >> (16 * h));
-      const float z = (float)((zb >> (4 * h)) & 0xFu);
-      const int gi = xk / kGroup;
+    for (int u = 0; u < U; ++u) {
+      // straight-line for every u: a group past the wave's range gets scale 0;
+      // masks are arithmetic, not selects (a select of a loaded value would
+      // become a branch around the load)
+      const int g = gs + u;
+      const float valid = g < g1 ? 1.0f : 0.0f;
+      uint4 xa[4];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const float c1 = csum[(m * ngw + gi) * 2 + 0];
-        const float c2 = csum[(m * ngw + gi) * 2 + 1];
-        const float t = BF16 ? (acc_a[m] - c1 - z * c2) : (acc_a[m] + 0.0625f * acc_b[m] - c1 - z * c2);
-        y[m] += s * t;
+      for (int j = 0; j < 4; ++j)
+        xa[j] = make_uint4(x[u][j].x & rmask, x[u][j].y & rmask, x[u][j].z & rmask, x[u][j].w & rmask);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw[u][t] >> (16 * (g & 1)))) * valid;
+        const uint32_t nz = neg_offset_pair<BF16>((zw[u][t] >> (4 * (g & 1))) & 0xFu);
+        const uint4 bz = make_uint4(nz, nz, nz, nz);
+        const uint32_t ww[4] = {wcur[u][t].x, wcur[u][t].y, wcur[u][t].z, wcur[u][t].w};
+        f32x4 t0 = {0.0f, 0.0f, 0.0f, 0.0f}, t1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          t0 = mfma<BF16>(xa[j], unpack8<BF16>(ww[j]), t0);
+          t1 = mfma<BF16>(xa[j], bz, t1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][i] += s * (t0[i] + t1[i]);
       }
     }
   };
 
-  for (int p = 0; p < npairs; p += 2) {
-    if (p + 1 < npairs) {
+  uint4 wa[U][NT], wb[U][NT];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) bufB[c] = wp[((p + 1) * 8 + c) * kTileN];
-      sB = sp[(p + 1) * kTileN];
-      zB = zp[(p + 1) * kTileN];
-    }
-    consume(bufA, sA, zA, p);
-    if (p + 1 < npairs) {
-      if (p + 2 < npairs) {
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) bufA[c] = wp[((p + 2) * 8 + c) * kTileN];
-        sA = sp[(p + 2) * kTileN];
-        zA = zp[(p + 2) * kTileN];
-      }
-      consume(bufB, sB, zB, p + 1);
-    }
+    for (int t = 0; t < NT; ++t) wa[u][t] = load_w(t, g0 + u);
+  // two steps per iteration with the weight buffers swapping roles, so no
+  // register copy ever waits on a prefetch
+  for (int gs = g0; gs < g1;) {
+    step(gs, wa, wb);
+    gs += U;
+    if (gs >= g1) break;
+    step(gs, wb, wa);
+    gs += U;
   }
 
-  // ---- reduce the four waves
+  // ---- add the waves' tiles; lane l holds rows 4*(l/16) + i of column l % 16
 #pragma unroll
-  for (int m = 0; m < MT; ++m) red[(wave * MT + m) * 64 + lane] = y[m];
+  for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
   if (wave != 0) return;
+  for (int w = 1; w < nw; ++w)
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-    y[m] = ((red[(0 * MT + m) * 64 + lane] + red[(1 * MT + m) * 64 + lane]) + red[(2 * MT + m) * 64 + lane]) +
-           red[(3 * MT + m) * 64 + lane];
-
-  const int n = tile * kTileN + lane;
-  if (a.splits == 1) {
-    if (n < a.N)
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 o = red[w][t][lane];
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < a.M) a.Y[(size_t)m * a.N + n] = to_out(y[m], BF16);
-    return;
+      for (int i = 0; i < 4; ++i) acc[t][i] += o[i];
+    }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int n = (blockIdx.x * NT + t) * 16 + cl;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * blk + i;
+      if (m < a.M)
+        a.Y[(size_t)m * a.N + n] = BF16 ? __builtin_bit_cast(uint16_t, (__bf16)acc[t][i])
+                                        : __builtin_bit_cast(uint16_t, (_Float16)acc[t][i]);
+    }
   }
-
-  // ---- split-K: publish the partial, the last workgroup of the tile combines
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-    if (m < a.M) a.part[((size_t)split * a.M + m) * a.Np + n] = y[m];
-  __threadfence();
-  unsigned prev = 0;
-  if (lane == 0)
-    prev = __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0);
-  if (prev != (unsigned)(a.splits - 1)) return;
-  __threadfence();
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (m >= a.M) break;
-    float acc = 0.0f;
-    for (int s = 0; s < a.splits; ++s) acc += a.part[((size_t)s * a.M + m) * a.Np + n];
-    if (n < a.N) a.Y[(size_t)m * a.N + n] = to_out(acc, BF16);
-  }
-  if (lane == 0) a.cnt[tile] = 0u;
-}
-
-template <int MT, bool BF16>
-hipError_t launch_mt(const GemvArgs& a, int ntiles, hipStream_t st) {
-  const int kwg = 4 * a.kw;
-  const size_t lds = (size_t)MT * kwg * 2 + (size_t)MT * (kwg / kGroup) * 2 * 4 + (size_t)4 * MT * 64 * 4;
-  hipLaunchKernelGGL((q4_gemv_kernel<MT, BF16>), dim3(ntiles * a.splits), dim3(256), lds, st, a);
-  return hipGetLastError();
 }
 
 template <bool BF16>
-hipError_t launch_dtype(const GemvArgs& a, int mt, int ntiles, hipStream_t st) {
-  switch (mt) {
-    case 1: return launch_mt<1, BF16>(a, ntiles, st);
-    case 2: return launch_mt<2, BF16>(a, ntiles, st);
-    case 4: return launch_mt<4, BF16>(a, ntiles, st);
-    case 8: return launch_mt<8, BF16>(a, ntiles, st);
-    default: return launch_mt<16, BF16>(a, ntiles, st);
+hipError_t launch_dtype(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
+  const dim3 grid(a.Np / (16 * P.nt)), block(64 * P.waves);
+  switch (P.nt) {
+    case 4: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 4, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 2, 2>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 1, 4>), grid, block, 0, st, a); break;
   }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 GemvPlan plan_q4_gemv(int M, int N, int K) {
+  (void)M;
+  (void)K;
   GemvPlan P;
-  P.mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
   const Q4Layout L = q4_layout(N, K);
-  const int ntiles = L.Np / kTileN;
-  // X staged per workgroup: MT * 4 * kw * 2 bytes, kept <= 32 KB
-  int max_kw = (4096 / P.mt) / kPairK * kPairK;
-  if (max_kw < kPairK) max_kw = kPairK;
-  const int target_wgs = 1024;
-  const int max_splits = (L.Kp + 4 * kPairK - 1) / (4 * kPairK);
-  int splits = (target_wgs + ntiles - 1) / ntiles;
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int kw = (L.Kp + 4 * splits - 1) / (4 * splits);
-  kw = (kw + kPairK - 1) / kPairK * kPairK;
-  if (kw > max_kw) kw = max_kw;
-  splits = (L.Kp + 4 * kw - 1) / (4 * kw);
-  P.kw = kw;
-  P.splits = splits;
-  P.ws_bytes = 0;
-  if (splits > 1)
-    P.ws_bytes = round_up((size_t)ntiles * 4, 256) + (size_t)splits * M * L.Np * 4;
+  const int slices = L.Np / 16;
+  // widest column block that still leaves a workgroup for every compute unit
+  P.nt = (slices / 4 >= 256) ? 4 : (slices / 2 >= 256) ? 2 : 1;
+  const int wgs = slices / P.nt;
+  P.waves = wgs >= 1024 ? 4 : 8;
   return P;
 }
 
 hipError_t launch_q4_gemv(const void* X, bool bf16, int M, int K, int N, const uint8_t* blob, const Q4Layout& L,
-                          const GemvPlan& P, void* ws, void* Y, hipStream_t st) {
+                          const GemvPlan& P, void* Y, hipStream_t st) {
   GemvArgs a;
   a.X = static_cast<const uint16_t*>(X);
   a.M = M;
@@ -318,14 +243,8 @@ hipError_t launch_q4_gemv(const void* X, bool bf16, int M, int K, int N, const u
   a.W = reinterpret_cast<const uint4*>(blob + L.w_off);
   a.S = reinterpret_cast<const uint32_t*>(blob + L.s_off);
   a.Z = blob + L.z_off;
-  a.kw = P.kw;
-  a.splits = P.splits;
-  const int ntiles = L.Np / kTileN;
-  a.cnt = static_cast<unsigned*>(ws);
-  a.part = P.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + round_up((size_t)ntiles * 4, 256))
-                        : nullptr;
   a.Y = static_cast<uint16_t*>(Y);
-  return bf16 ? launch_dtype<true>(a, P.mt, ntiles, st) : launch_dtype<false>(a, P.mt, ntiles, st);
+  return bf16 ? launch_dtype<true>(a, P, st) : launch_dtype<false>(a, P, st);
 }
 
 }  // namespace ql

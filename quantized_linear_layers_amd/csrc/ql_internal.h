@@ -52,17 +52,15 @@ inline int nib_pos(int i) { return (i & 1) * 4 + (i >> 1); }
 
 // ---------------------------------------------------------------- launch plans
 struct GemvPlan {
-  int mt;          // compiled row-tile (1, 2, 4, 8, 16)
-  int kw;          // K per wave (multiple of 256)
-  int splits;      // workgroups along K per column tile
-  size_t ws_bytes; // partials + counters
+  int nt;          // 16-column slices per workgroup (1, 2 or 4)
+  int waves;       // waves per workgroup; they split K
 };
 
 GemvPlan plan_q4_gemv(int M, int N, int K);
 
 hipError_t launch_q4_gemv(const void* X, bool bf16, int M, int K, int N,
                           const uint8_t* blob, const Q4Layout& L, const GemvPlan& P,
-                          void* ws, void* Y, hipStream_t st);
+                          void* Y, hipStream_t st);
 
 hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N,
                           const uint8_t* blob, const Q4Layout& L, void* Y, hipStream_t st);

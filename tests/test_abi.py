@@ -17,11 +17,12 @@ from oracle import w8a8 as ow8
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-QL_OK, QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED, QL_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6
+QL_OK, QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED, QL_ERR_SIZE = 0, -1, -2, -3, -4, -5, -6
 QL_ERR_RANGE = -8
 
 FAKE = C.c_void_p(0x10000)          # aligned, never dereferenced: validation fails first
 FAKE_MIS = C.c_void_p(0x10008)      # 8-byte aligned only
+BIG = 1 << 40                       # a blob size that passes the size check
 
 
 def declared_functions():
@@ -33,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -47,24 +48,22 @@ def test_q4_gemm_validation():
     L = ql.lib()
     P = FAKE
     # K not a multiple of the group
-    assert L.q4_gemm(P, 0, 1, 200, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_SHAPE
+    assert L.q4_gemm(P, 0, 1, 200, 64, P, BIG, 128, P, None) == QL_ERR_SHAPE
     assert "multiple" in last_error()
-    assert L.q4_gemm(P, 0, 1, 256, 64, P, 64, P, P, 1 << 20, None) == QL_ERR_UNSUPPORTED
-    assert L.q4_gemm(P, 7, 1, 256, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_DTYPE
-    assert L.q4_gemm(P, 0, -1, 256, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_SHAPE
-    assert L.q4_gemm(P, 0, 1, 0, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_SHAPE
-    assert L.q4_gemm(None, 0, 1, 256, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_NULL
-    assert L.q4_gemm(FAKE_MIS, 0, 1, 256, 64, P, 128, P, P, 1 << 20, None) == QL_ERR_ALIGN
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 64, P, None) == QL_ERR_UNSUPPORTED
+    assert L.q4_gemm(P, 7, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_DTYPE
+    assert L.q4_gemm(P, 0, -1, 256, 64, P, BIG, 128, P, None) == QL_ERR_SHAPE
+    assert L.q4_gemm(P, 0, 1, 0, 64, P, BIG, 128, P, None) == QL_ERR_SHAPE
+    assert L.q4_gemm(None, 0, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_NULL
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 128, None, None) == QL_ERR_NULL
+    assert L.q4_gemm(FAKE_MIS, 0, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_ALIGN
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 128, FAKE_MIS, None) == QL_ERR_ALIGN
+    # a blob smaller than the layout of (N, K) is rejected
+    need = L.q4_packed_bytes(64, 256, 128)
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, need - 1, 128, P, None) == QL_ERR_SIZE
     # empty problems are no-ops
-    assert L.q4_gemm(None, 0, 0, 256, 64, None, 128, None, None, 0, None) == QL_OK
-    assert L.q4_gemm(None, 0, 4, 256, 0, None, 128, None, None, 0, None) == QL_OK
-    # a split-K decode shape needs a workspace
-    M, N, K = 1, 4096, 4096
-    need = L.q4_gemm_workspace_bytes(M, N, K, 128)
-    assert need > 0
-    assert L.q4_gemm(P, 0, M, K, N, P, 128, P, None, 0, None) == QL_ERR_WORKSPACE
-    assert L.q4_gemm(P, 0, M, K, N, P, 128, P, P, need - 1, None) == QL_ERR_WORKSPACE
-    assert L.q4_gemm_workspace_bytes(4096, 4096, 4096, 128) == 0
+    assert L.q4_gemm(None, 0, 0, 256, 64, None, BIG, 128, None, None) == QL_OK
+    assert L.q4_gemm(None, 0, 4, 256, 0, None, BIG, 128, None, None) == QL_OK
 
 
 def test_i8_validation():

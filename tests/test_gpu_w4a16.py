@@ -101,9 +101,9 @@ def test_ragged(M, K, N, dtype):
     check(W, X)
 
 
-def test_workspace_reuse_and_zero_input():
-    """Two calls in a row on one workspace (the arrival counters reset) and
-    an all-zero activation gives exactly zero."""
+def test_repeat_call_and_zero_input():
+    """Two calls in a row give identical results, and an all-zero activation
+    gives exactly zero."""
     w = wl.WORKLOADS["decode_7b"]
     W = wl.weight(w, 4096, 11008)
     X = wl.activations(w, 4, 4096, 11008)
@@ -122,3 +122,20 @@ def test_large_activation_values():
     Xf = r.standard_normal((4, 1024)).astype(np.float32)
     Xf[:, ::97] *= 5000.0
     check(W, torch.from_numpy(Xf).to(torch.bfloat16))
+
+
+def test_alternating_shapes_are_deterministic():
+    """Layers of different tile counts called alternately give bit-identical
+    results on every repetition (no state carried between calls)."""
+    r = np.random.default_rng(17)
+    shapes = [(4096, 11008), (8192, 4096), (2048, 640)]
+    Ws = [(r.standard_normal((N, K)) * 0.02).astype(np.float32) for (K, N) in shapes]
+    Xs = [torch.from_numpy(r.standard_normal((2, K)).astype(np.float32)).half() for (K, _) in shapes]
+    first = []
+    for rep in range(3):
+        for i, (W, X) in enumerate(zip(Ws, Xs)):
+            e = check(W, X)
+            if rep == 0:
+                first.append(e)
+            else:
+                assert e == first[i]
