@@ -114,15 +114,18 @@ size_t q4_packed_bytes(int N, int K, int group);
  * use other interleaves for the same reason ([LQ] W4A16 section), so blobs
  * are not interchangeable with other formats.  Layout (N and K padded to
  * Np = roundup(N, 64), Kp = roundup(K, 256) with code 0, scale 0, zero 0):
- *   [0, 256)      header: "QL4P", version, N, K, group, Np, Kp
- *   weights       [Np/64][Kp/32][64 lanes][16 bytes]: lane l of tile t owns
- *                 output channel 64t + l; its 16 bytes hold 32 consecutive k
- *                 as 4 words of 8 codes, the code of k = 8j + i sitting at
- *                 nibble position (i & 1) * 4 + (i >> 1) of word j
- *   scales        [Np/64][Kp/256][64][2] fp16: groups 2p, 2p+1 of a lane
- *   zeros         [Np/64][Kp/256][64] bytes: zero of group 2p in the low
- *                 nibble, of group 2p+1 in the high nibble
- * (each region starts on a 256-byte boundary).
+ *   [0, 256)      header: "QL4P", version 2, N, K, group, Np, Kp
+ *   weights       [Kp/32][Np][16 bytes]: row c holds, for each output channel
+ *                 n, its 32 codes of k in [32c, 32c + 32) as 4 words of 8
+ *                 codes, the code of k = 32c + 8j + i sitting at nibble
+ *                 position (i & 1) * 4 + (i >> 1) of word j (so that one AND
+ *                 with 0x000F000F after a shift by 4p yields the codes of
+ *                 k = 8j + 2p and 8j + 2p + 1 as two 16-bit lanes)
+ *   scales        [Kp/256][Np][2] fp16: the scales of groups 2p and 2p + 1
+ *   zeros         [Kp/256][Np] bytes: zero of group 2p in the low nibble,
+ *                 of group 2p + 1 in the high nibble
+ * (each region starts on a 256-byte boundary).  The rows are chunk-major so
+ * that all output channels at one K position are contiguous in memory.
  *
  * packed: host buffer of packed_bytes >= q4_packed_bytes(N, K, group).
  * Copy it to device memory (any 16-byte-aligned address) for q4_gemm.

@@ -62,18 +62,16 @@ int check_q4_shape(const char* fn, int N, int K, int group) {
   return QL_OK;
 }
 
+// chunk-major device layout: row c of 32-channel chunks holds one 16-byte
+// chunk per output channel; scale / zero rows hold one group pair per channel
 inline size_t w_byte(const ql::Q4Layout& L, int n, int k) {
-  const int t = n / ql::kTileN, l = n % ql::kTileN, c = k / ql::kChunkK, j = (k % ql::kChunkK) / 8;
-  return L.w_off + (((size_t)t * (L.Kp / ql::kChunkK) + c) * ql::kTileN + l) * 16 + (size_t)j * 4;
+  const int c = k / ql::kChunkK, j = (k % ql::kChunkK) / 8;
+  return L.w_off + ((size_t)c * L.Np + n) * 16 + (size_t)j * 4;
 }
 inline size_t s_byte(const ql::Q4Layout& L, int n, int g) {
-  const int t = n / ql::kTileN, l = n % ql::kTileN;
-  return L.s_off + (((size_t)t * (L.Kp / ql::kPairK) + g / 2) * ql::kTileN + l) * 4 + (size_t)(g % 2) * 2;
+  return L.s_off + ((size_t)(g / 2) * L.Np + n) * 4 + (size_t)(g % 2) * 2;
 }
-inline size_t z_byte(const ql::Q4Layout& L, int n, int g) {
-  const int t = n / ql::kTileN, l = n % ql::kTileN;
-  return L.z_off + ((size_t)t * (L.Kp / ql::kPairK) + g / 2) * ql::kTileN + l;
-}
+inline size_t z_byte(const ql::Q4Layout& L, int n, int g) { return L.z_off + (size_t)(g / 2) * L.Np + n; }
 
 }  // namespace
 

@@ -23,7 +23,7 @@ constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int APAD = 8;                       // halves of padding per X row in LDS
 constexpr int AROW = BK + APAD;               // LDS row length of the X tile (halves)
 constexpr int A_TILE = BM * AROW;             // halves per X buffer
-constexpr int B_TILE = (BN / kTileN) * (BK / kChunkK) * kTileN * 16;   // bytes per W buffer
+constexpr int B_TILE = (BK / kChunkK) * BN * 16;   // bytes per W buffer: [chunk][column] x 16 bytes
 
 struct GemmArgs {
   const uint16_t* X;
@@ -65,7 +65,6 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
   const int ntn = (a.N + BN - 1) / BN;
   const int m0 = (blockIdx.x / ntn) * BM, n0 = (blockIdx.x % ntn) * BN;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  const int ck = a.Kp / kChunkK, pk = a.Kp / kPairK;
   const int nkb = a.K / BK;
 
   // ---- global -> register staging of one k-block
@@ -81,10 +80,10 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int idx = tid + i * 256;          // 0 .. 511: 2 layout tiles x 4 chunks x 64 lanes
-      const int lt = idx >> 8, c = (idx >> 6) & 3, l = idx & 63;
-      const int t = n0 / kTileN + lt;
-      rb[i] = (t * kTileN < a.Np) ? a.W[((size_t)t * ck + kb * 4 + c) * kTileN + l] : make_uint4(0, 0, 0, 0);
+      const int idx = tid + i * 256;          // 0 .. 511: 4 chunks x 128 columns
+      const int c = idx >> 7, col = idx & 127;
+      const int n = n0 + col;
+      rb[i] = n < a.Np ? a.W[(size_t)(kb * 4 + c) * a.Np + n] : make_uint4(0, 0, 0, 0);
     }
   };
   auto store_block = [&](int buf) {
@@ -120,11 +119,11 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int n = n0 + wn + nt * 32 + l32;
-      const int t = n / kTileN, l = n % kTileN, g = kb;
+      const int g = kb;
       float sv = 0.0f, zv = 0.0f;
       if (n < a.Np) {
-        const uint32_t sp = a.S[((size_t)t * pk + g / 2) * kTileN + l];
-        const uint32_t zp = a.Z[((size_t)t * pk + g / 2) * kTileN + l];
+        const uint32_t sp = a.S[(size_t)(g / 2) * a.Np + n];
+        const uint32_t zp = a.Z[(size_t)(g / 2) * a.Np + n];
         sv = (float)__builtin_bit_cast(_Float16, (uint16_t)(sp >> (16 * (g & 1))));
         zv = (float)((zp >> (4 * (g & 1))) & 0xFu);
       }
@@ -141,9 +140,8 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int c = wn + nt * 32 + l32;            // column inside the workgroup tile
-        const int lt = c / kTileN, cl = c % kTileN;
         const int chunk = ks >> 1, j = (ks & 1) * 2 + half;
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(&bs[buf][((lt * 4 + chunk) * kTileN + cl) * 16 + j * 4]);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(&bs[buf][(chunk * BN + c) * 16 + j * 4]);
         bf[nt] = dequant8(w, s[nt], nzs[nt], BF16);
       }
 #pragma unroll

@@ -13,8 +13,10 @@
 //     gives every compute unit a workgroup;
 //   * lane l of a wave reads output channel l % 16 of each of its NT 16-column
 //     slices, K-block l / 16: one 16-byte load per lane and slice covers 4
-//     consecutive 32-channel chunks x 16 channels = one 128-wide group,
-//     256-byte contiguous runs in the packed blob;
+//     consecutive 32-channel chunks x 16 channels = one 128-wide group, four
+//     256-byte runs of the chunk-major blob, where all channels at one K
+//     position are contiguous, so the waves of all workgroups that are at the
+//     same point of K read one contiguous window (what HBM streams best);
 //   * the activation fragment of a group is loaded once and used for all NT
 //     slices, which keeps activation loads from crowding out weight loads;
 //   * the codes stay packed until they are in registers ([QK] §9.5): an AND
@@ -43,9 +45,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct GemvArgs {
   const uint16_t* X;
   int M, K, N, Np, Kp;
-  const uint4* W;          // [Np/64][Kp/32][64] chunks
-  const uint32_t* S;       // [Np/64][Kp/256][64] scale pairs
-  const uint8_t* Z;        // [Np/64][Kp/256][64] zero pairs
+  const uint4* W;          // [Kp/32][Np] chunks
+  const uint32_t* S;       // [Kp/256][Np] scale pairs
+  const uint8_t* Z;        // [Kp/256][Np] zero pairs
   uint16_t* Y;             // [M][N]
 };
 
@@ -73,8 +75,16 @@ __device__ inline uint32_t neg_offset_pair(uint32_t z) {
   return h | (h << 16);
 }
 
-// NT: 16-column slices per wave; U: groups per step (NT * U weight loads of
-// 16 bytes per lane per step, next step's in flight while a step computes)
+// NT: 16-column slices per wave; U: groups per step (even, so a step covers
+// whole pairs of groups and their shared scale / zero words)
+template <int NT, int U>
+struct StepBuf {
+  uint4 w[U][NT];          // one 16-byte chunk per group and slice
+  uint4 x[U][4];           // activation fragments of each group (shared by the slices)
+  uint32_t s[U / 2][NT];   // fp16 scales of a pair of groups
+  uint32_t z[U / 2][NT];   // zero points of a pair of groups (two nibbles)
+};
+
 template <bool BF16, int NT, int U>
 __global__ __launch_bounds__(512) void q4_gemv_kernel(GemvArgs a) {
   __shared__ f32x4 red[8][NT][64];
@@ -82,76 +92,72 @@ __global__ __launch_bounds__(512) void q4_gemv_kernel(GemvArgs a) {
   // the wave index is uniform; saying so keeps the K loop a scalar loop
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int cl = lane & 15, blk = lane >> 4;
-  const int ck = a.Kp / kChunkK, pk = a.Kp / kPairK;
   const int G = a.K / kGroup;
-  const int gpw = (G + nw - 1) / nw;
+  const int gpw = ((G + nw - 1) / nw + U - 1) / U * U;          // groups per wave, whole steps
   const int g0 = min(G, wave * gpw), g1 = min(G, g0 + gpw);
   const int gl = max(G - 1, 0);
 
   const uint4* wp[NT];
   const uint32_t* sp[NT];
   const uint8_t* zp[NT];
+  const size_t np = a.Np;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int slice = blockIdx.x * NT + t;                  // 16-column slice
-    const int tile = slice >> 2, sub = slice & 3;           // 64-column layout tile
-    wp[t] = a.W + ((size_t)tile * ck + blk) * kTileN + sub * 16 + cl;   // + 4*64*g for group g
-    sp[t] = a.S + (size_t)tile * pk * kTileN + sub * 16 + cl;           // + 64*(g/2)
-    zp[t] = a.Z + (size_t)tile * pk * kTileN + sub * 16 + cl;
+    const int n = (blockIdx.x * NT + t) * 16 + cl;          // output channel of this lane in slice t
+    wp[t] = a.W + (size_t)blk * np + n;                     // + 4*Np*g for group g
+    sp[t] = a.S + n;                                        // + Np*(g/2)
+    zp[t] = a.Z + n;
   }
   const bool row_ok = cl < a.M;                                           // A-operand row of this lane
   const uint32_t rmask = row_ok ? 0xFFFFFFFFu : 0u;
   const uint16_t* xp = a.X + (size_t)(row_ok ? cl : 0) * a.K + blk * kChunkK;   // + 128*g + 8*j
 
-  // All loads are branch-free (indices clamped into the layer, unused values
-  // discarded) and issued in the order they are consumed, so the in-order
-  // vector-memory counter only ever waits for data that is needed next:
-  // weights run one step ahead of their use, and a step's activations, scales
-  // and zero points are issued before the next step's weights.
-  auto load_w = [&](int t, int g) { return wp[t][(size_t)min(g, gl) * 4 * kTileN]; };
+  // All loads are branch-free (indices clamped into the layer, values past the
+  // wave's range discarded) and a whole step ahead of their use: a step first
+  // issues every load of the next step, then computes on data issued one step
+  // earlier, so the in-order vector-memory counter never waits on a prefetch.
+  auto issue = [&](int gs, StepBuf<NT, U>& b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = min(gs + u, gl);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) b.w[u][t] = wp[t][(size_t)g * 4 * np];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b.x[u][j] = *reinterpret_cast<const uint4*>(xp + (size_t)g * kGroup + 8 * j);
+    }
+#pragma unroll
+    for (int p = 0; p < U / 2; ++p) {
+      const int pr = min(gs + 2 * p, gl) >> 1;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        b.s[p][t] = sp[t][(size_t)pr * np];
+        b.z[p][t] = zp[t][(size_t)pr * np];
+      }
+    }
+  };
 
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto step = [&](int gs, const uint4 (&wcur)[U][NT], uint4 (&wnxt)[U][NT]) {
-    uint4 x[U][4];
-    uint32_t sw[U][NT], zw[U][NT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = min(gs + u, gl);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[u][j] = *reinterpret_cast<const uint4*>(xp + (size_t)g * kGroup + 8 * j);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        sw[u][t] = sp[t][(size_t)(g >> 1) * kTileN];
-        zw[u][t] = zp[t][(size_t)(g >> 1) * kTileN];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) wnxt[u][t] = load_w(t, gs + U + u);
-    // keep the loads above ahead of the arithmetic below (the scheduler would
-    // otherwise sink them to save registers and serialize their latency)
-    __builtin_amdgcn_sched_barrier(0);
+  auto compute = [&](int gs, const StepBuf<NT, U>& b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // straight-line for every u: a group past the wave's range gets scale 0;
       // masks are arithmetic, not selects (a select of a loaded value would
       // become a branch around the load)
-      const int g = gs + u;
-      const float valid = g < g1 ? 1.0f : 0.0f;
+      const float valid = gs + u < g1 ? 1.0f : 0.0f;
       uint4 xa[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xa[j] = make_uint4(x[u][j].x & rmask, x[u][j].y & rmask, x[u][j].z & rmask, x[u][j].w & rmask);
+        xa[j] = make_uint4(b.x[u][j].x & rmask, b.x[u][j].y & rmask, b.x[u][j].z & rmask, b.x[u][j].w & rmask);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw[u][t] >> (16 * (g & 1)))) * valid;
-        const uint32_t nz = neg_offset_pair<BF16>((zw[u][t] >> (4 * (g & 1))) & 0xFu);
+        const int h = u & 1;                                   // steps start on even groups
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(b.s[u >> 1][t] >> (16 * h))) * valid;
+        const uint32_t nz = neg_offset_pair<BF16>((b.z[u >> 1][t] >> (4 * h)) & 0xFu);
         const uint4 bz = make_uint4(nz, nz, nz, nz);
-        const uint32_t ww[4] = {wcur[u][t].x, wcur[u][t].y, wcur[u][t].z, wcur[u][t].w};
+        const uint32_t ww[4] = {b.w[u][t].x, b.w[u][t].y, b.w[u][t].z, b.w[u][t].w};
         f32x4 t0 = {0.0f, 0.0f, 0.0f, 0.0f}, t1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -164,18 +170,19 @@ __global__ __launch_bounds__(512) void q4_gemv_kernel(GemvArgs a) {
     }
   };
 
-  uint4 wa[U][NT], wb[U][NT];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) wa[u][t] = load_w(t, g0 + u);
-  // two steps per iteration with the weight buffers swapping roles, so no
-  // register copy ever waits on a prefetch
+  StepBuf<NT, U> ba, bb;
+  issue(g0, ba);
+  // two steps per iteration with the buffers swapping roles, so no register
+  // copy ever waits on a prefetch
   for (int gs = g0; gs < g1;) {
-    step(gs, wa, wb);
+    issue(gs + U, bb);
+    __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the arithmetic
+    compute(gs, ba);
     gs += U;
     if (gs >= g1) break;
-    step(gs, wb, wa);
+    issue(gs + U, ba);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(gs, bb);
     gs += U;
   }
 
@@ -209,9 +216,9 @@ template <bool BF16>
 hipError_t launch_dtype(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
   const dim3 grid(a.Np / (16 * P.nt)), block(64 * P.waves);
   switch (P.nt) {
-    case 4: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 4, 1>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 4, 2>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 2, 2>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 1, 4>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 1, 2>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -224,10 +231,12 @@ GemvPlan plan_q4_gemv(int M, int N, int K) {
   GemvPlan P;
   const Q4Layout L = q4_layout(N, K);
   const int slices = L.Np / 16;
-  // widest column block that still leaves a workgroup for every compute unit
+  // widest column block that still leaves a workgroup for every compute unit;
+  // four waves per workgroup (measured on the Llama-2 7B / 70B layer shapes:
+  // fewer concurrent weight streams per compute unit keep HBM busier than
+  // more, as for a plain streaming read)
   P.nt = (slices / 4 >= 256) ? 4 : (slices / 2 >= 256) ? 2 : 1;
-  const int wgs = slices / P.nt;
-  P.waves = wgs >= 1024 ? 4 : 8;
+  P.waves = 4;
   return P;
 }
 

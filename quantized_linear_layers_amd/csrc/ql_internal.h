@@ -11,15 +11,16 @@ namespace ql {
 int set_error(int code, const char* fmt, ...);
 
 // ---------------------------------------------------------------- W4 device blob layout
-// One layout tile is 64 output channels (one per lane of a wave); K is cut in
-// 32-channel chunks of 16 bytes per lane; scales and zeros are stored per pair
-// of 128-channel groups.
+// Chunk-major: K is cut in 32-channel chunks; row c holds, for every output
+// channel n, the 16 bytes of its 32 codes of chunk c (so all channels at one K
+// position are contiguous).  Scales and zero points are stored the same way,
+// one row per pair of 128-channel groups.  N is padded to kTileN.
 constexpr int kTileN = 64;
 constexpr int kChunkK = 32;
 constexpr int kGroup = 128;
 constexpr int kPairK = 256;          // two groups: K granularity of the blob
 constexpr uint32_t kMagic = 0x50344C51u;   // "QL4P"
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
 
 struct Q4Layout {
   int N, K, Np, Kp;

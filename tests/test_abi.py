@@ -117,20 +117,32 @@ def test_q4_quantize_workload_layer():
 
 
 def test_q4_blob_layout_positions():
-    """The documented device layout: code of (n, k) at tile n//64, chunk k//32,
-    lane n%64, word (k%32)//8, nibble position (i&1)*4 + (i>>1), i = k%8."""
-    N, K = 128, 256
+    """The documented chunk-major device layout: the code of (n, k) sits in row
+    k // 32 at column n (16 bytes each), word (k % 32) // 8, nibble position
+    (i & 1) * 4 + (i >> 1) with i = k % 8; scales and zeros one row per pair of
+    groups."""
+    N, K = 72, 384                     # Np = 128, Kp = 512
     q = np.random.default_rng(5).integers(0, 16, (N, K)).astype(np.uint8)
     wq = torch.from_numpy(ow4.pack_canonical(q).view(np.int32))
-    s = torch.zeros((K // 128, N), dtype=torch.float16)
-    z = torch.zeros((K // 128, N), dtype=torch.uint8)
+    s = torch.from_numpy((np.arange(3 * N).reshape(3, N) * 0.001 + 0.01).astype(np.float16))
+    z = torch.from_numpy(np.random.default_rng(6).integers(0, 16, (3, N)).astype(np.uint8))
     blob = ql.q4_pack(wq, s, z, N, K).numpy()
-    Kp = 256
-    for n, k in [(0, 0), (1, 1), (63, 31), (64, 32), (100, 255), (127, 130)]:
-        t, l, c, j, i = n // 64, n % 64, k // 32, (k % 32) // 8, k % 8
-        off = 256 + ((t * (Kp // 32) + c) * 64 + l) * 16 + j * 4
+    Np, Kp = 128, 512
+    hdr = blob[:28].view(np.int32)
+    assert hdr[1] == 2 and list(hdr[2:7]) == [N, K, 128, Np, Kp]
+    w_off = 256
+    s_off = w_off + Np * Kp // 2
+    z_off = s_off + (Kp // 256) * Np * 4
+    for n, k in [(0, 0), (1, 1), (63, 31), (64, 32), (71, 383), (5, 130), (70, 255)]:
+        c, j, i = k // 32, (k % 32) // 8, k % 8
+        off = w_off + (c * Np + n) * 16 + j * 4
         word = int(blob[off:off + 4].view(np.uint32)[0])
         assert (word >> (4 * ((i & 1) * 4 + (i >> 1)))) & 0xF == q[n, k]
+    for n, g in [(0, 0), (3, 1), (71, 2)]:
+        so = s_off + ((g // 2) * Np + n) * 4 + (g % 2) * 2
+        assert blob[so:so + 2].view(np.float16)[0] == s[g, n].numpy()
+        zb = int(blob[z_off + (g // 2) * Np + n])
+        assert (zb >> (4 * (g % 2))) & 0xF == z[g, n]
 
 
 def test_q4_host_errors():
