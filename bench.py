@@ -11,13 +11,16 @@ the step's wall time, inputs resident in HBM.  Each step reads a different
 copy of the weights (copies rotate so that the working set exceeds 1 GiB, four
 times the 256 MB Infinity Cache), so the weights come from HBM, not cache.
 
-The steps are replayed as HIP graphs (one graph per weight copy, nine
-launches each) to keep launch gaps out of the step; every graph's outputs
-are checked bit-for-bit against eager launches before timing.  Per-kernel
-durations for the roofline object come from a second pass of eager launches,
-each bracketed by HIP events on the launch stream.  The `also` object holds
-the other workloads (70B decode, W8A8 prefill GEMM, W4A16 prefill GEMM) timed
-the same way per kernel.
+The steps are launched on one stream with their arguments marshalled once
+(--graphs replays them as HIP graphs instead, one graph per weight copy, after
+checking every graph's outputs bit-for-bit against eager launches; on this
+stack graph replay of these short kernels measured slower than stream
+launches).  The step contains only the decode kernel, so the roofline
+object's mean launch duration is the timed region's elapsed time (HIP events
+on the launch stream) over its launches.  `per_case_eager` adds a second pass of eager launches,
+each bracketed by HIP events (which adds the event overhead to each figure).
+The `also` object holds the other workloads (70B decode, W8A8 prefill GEMM,
+W4A16 prefill GEMM).
 """
 
 import argparse
@@ -35,6 +38,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "i8": 5.0e15}   # dense, published
 METRIC = "W4A16 GEMV effective GB/s (% HBM peak); W8A8/W4A16 GEMM TOPS (% MFMA peak)"
 MALL_DEFEAT_BYTES = 1 << 30
+
+# HBM traffic of the decode kernel per launch (mean over the nine cases of a
+# step), from two counter runs (FETCH_SIZE, then WRITE_SIZE) each scaled by
+# what the same counter reads for a plain device copy of known size in the
+# same run.  It belongs to one version of the kernel source: when the source
+# hash differs, the figure is stale and `traffic` is reported as null.
+TRAFFIC = {"source_sha256": "da8e171ba218a270af66a1ee6ed615db6461c57465ef06b5e42e2166d3111fa2",
+           "bytes_per_launch": 19395555}
 
 
 def w4a16_bytes(M, K, N, group=128, e=2):
@@ -59,6 +70,28 @@ def _copies_for(total_bytes):
     return max(2, -(-MALL_DEFEAT_BYTES // max(total_bytes, 1)))
 
 
+def _kernel_source_sha():
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_linear_layers_amd", "csrc",
+                       "q4_gemv.hip")
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of `mib` MiB, three times: the reference
+    the byte counters are scaled by (it reads and writes exactly that much)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# copy calibration: {n} bytes read and written per copy, 3 copies", flush=True)
+    del src, dst
+
+
 def time_launches(fn_list, reps, stream):
     """Eager launches, each bracketed by HIP events on `stream`; returns mean ms per entry."""
     tot = np.zeros(len(fn_list))
@@ -77,7 +110,7 @@ def time_launches(fn_list, reps, stream):
     return tot / reps
 
 
-def bench_decode(ql, wname, steps, warmup, use_graphs=True):
+def bench_decode(ql, wname, steps, warmup, use_graphs=False):
     """Runs a W4A16 decode workload; returns a dict of results."""
     w = wl.WORKLOADS[wname]
     cases = w.all_cases()
@@ -90,14 +123,21 @@ def bench_decode(ql, wname, steps, warmup, use_graphs=True):
     X = {c: wl.activations(w, c[0], c[1], c[2]).cuda() for c in cases}
     Y = {c: torch.empty((c[0], c[2]), dtype=X[c].dtype, device="cuda") for c in cases}
     stream = torch.cuda.current_stream()
+    # launchers with the arguments marshalled once (the host cost of a
+    # launch must stay below the kernel's few microseconds)
+    launchers = [[ql.q4_gemm_launcher(X[c], blobs[(c[1], c[2])][r], c[2], Y[c]) for c in cases] for r in range(R)]
 
     def launch(c, r):
         M, K, N = c
         ql.q4_gemm(X[c], blobs[(K, N)][r], N, Y=Y[c])
 
     def step(r):
-        for c in cases:
-            launch(c, r)
+        if use_graphs:            # capture runs on its own stream: marshal per call
+            for c in cases:
+                launch(c, r)
+        else:
+            for f in launchers[r]:
+                f()
 
     for r in range(min(R, warmup + 1)):
         step(r)
@@ -239,7 +279,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-also", action="store_true")
-    ap.add_argument("--no-graphs", action="store_true")
+    ap.add_argument("--graphs", action="store_true", help="replay the decode steps as HIP graphs")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard "
@@ -251,12 +293,14 @@ def main():
     dev = torch.cuda.get_device_properties(0)
     print(f"# device: {dev.name} ({getattr(dev, 'gcnArchName', '?')}), {dev.multi_processor_count} CUs", flush=True)
 
-    main_res = bench_decode(ql, "decode_7b", args.steps, args.warmup, use_graphs=not args.no_graphs)
+    if args.copy_calib > 0:
+        copy_calibration(args.copy_calib)
+    main_res = bench_decode(ql, "decode_7b", args.steps, args.warmup, use_graphs=args.graphs)
     print(f"# decode_7b: {main_res['value_gbs']:.1f} GB/s per step, kernels {main_res['kernel_gbs']:.1f} GB/s",
           flush=True)
     also = {}
     if not args.no_also:
-        r70 = bench_decode(ql, "decode_70b", max(10, args.steps // 2), args.warmup, use_graphs=not args.no_graphs)
+        r70 = bench_decode(ql, "decode_70b", max(10, args.steps // 2), args.warmup, use_graphs=args.graphs)
         also["decode_70b"] = {"workload": wl.WORKLOADS["decode_70b"].name, "step_GBps": round(r70["value_gbs"], 1),
                               "kernel_GBps": round(r70["kernel_gbs"], 1),
                               "frac_hbm": round(r70["kernel_gbs"] / HBM_PEAK_GBS, 4), "per_case": r70["per_case"]}
@@ -267,7 +311,14 @@ def main():
         print(f"# w4a16 prefill: {also['w4a16_prefill']}", flush=True)
 
     cpu = None if args.no_cpu else cpu_baseline()
-    achieved = main_res["kernel_gbs"]
+    # the step is nothing but the decode kernel's launches: its mean launch
+    # duration is the timed region's elapsed time over the launches in it
+    launches = len(main_res["cases"])
+    launch_ms = main_res["ms_step"] / launches
+    achieved = main_res["bytes_step"] / launches / (launch_ms * 1e-3) / 1e9
+    traffic = None
+    if TRAFFIC is not None and TRAFFIC["source_sha256"] == _kernel_source_sha():
+        traffic = TRAFFIC["bytes_per_launch"]
     line = {
         "metric": METRIC,
         "value": round(main_res["value_gbs"], 2),
@@ -286,8 +337,11 @@ def main():
                    "bytes_per_step": main_res["bytes_step"], "weight_copies": main_res["copies"],
                    "hip_graphs": main_res["graphs"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "q4_gemv_kernel", "per_case": main_res["per_case"]},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "q4_gemv_kernel",
+                     "algorithmic_bytes_per_launch": round(main_res["bytes_step"] / launches),
+                     "launch_us_mean": round(launch_ms * 1e3, 3),
+                     "per_case_eager": main_res["per_case"]},
         "cpu_baseline": cpu,
         "also": also,
     }

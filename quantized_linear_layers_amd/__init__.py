@@ -149,6 +149,28 @@ def q4_gemm(X, packed, N, group=GROUP, Y=None, stream=None):
     return Y
 
 
+def q4_gemm_launcher(X, packed, N, Y, group=GROUP, stream=None):
+    """Checks the operands of q4_gemm once and returns a callable that
+    launches it again on the same buffers with the arguments already
+    marshalled (for tight launch loops: the C entry point still validates
+    every call)."""
+    X = _dev(X, name="X")
+    _dev(packed, torch.uint8, "packed")
+    _dev(Y, X.dtype, "Y")
+    M, K = X.shape
+    if tuple(Y.shape) != (M, N):
+        raise QLError(f"q4_gemm: Y has shape {tuple(Y.shape)}, expected {(M, N)}")
+    f = lib().q4_gemm
+    args = (_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group, _ptr(Y), _stream(X, stream))
+
+    def launch():
+        rc = f(*args)
+        if rc != 0:
+            _check(rc, "q4_gemm")
+
+    return launch
+
+
 # ---------------------------------------------------------------- W8A8
 
 def i8_quant_weight_host(W):

@@ -54,12 +54,6 @@ struct I8Args {
 // logical piece touch 8 different 16-byte bank groups
 __device__ inline int swz(int r, int p) { return r * BK + ((p ^ ((r >> 1) & 3)) << 4); }
 
-// One wave's share of filling a slot: 16 blocks of 1 KB (8 rows x 128 bytes)
-// per operand, 4 per wave.  Lane l of a block writes LDS bytes 16 l .. 16 l + 15
-// of the block, i.e. row l / 8 and stored piece l % 8, which holds logical
-// piece (l % 8) ^ (row & 7).  Addresses of rows or k beyond the matrix are
-// clamped to the first element (a valid load whose data is never used: see
-// mma_block).
 // issues one 16-byte global -> LDS load per lane (lane i writes lds + 16 i)
 __device__ inline void load_lds16(const int8_t* src, int8_t* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -70,9 +64,12 @@ __device__ inline void load_lds16(const int8_t* src, int8_t* lds) {
 #endif
 }
 
-// Per-lane source rows of the 4 + 4 loads a wave issues per slot fill: rows
-// past M or N are clamped to the last row (valid loads whose data only reaches
-// outputs that are never stored).
+// One wave's share of filling a slot: the slot holds 8 blocks of 1 KB
+// (16 rows x 64 bytes) per operand, kFills = 2 per wave.  Lane l of a block
+// writes LDS bytes 16 l .. 16 l + 15 of the block, i.e. row l / 4 and stored
+// piece l % 4, which holds logical piece (l % 4) ^ ((row >> 1) & 3).  Rows
+// past M or N are clamped to the last row (valid loads whose data only
+// reaches outputs that are never stored).
 constexpr int kFills = kSlot / 1024 / 4;         // 1 KB blocks per operand per wave and slot fill
 
 struct FillPlan {

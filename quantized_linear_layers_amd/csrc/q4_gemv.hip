@@ -17,8 +17,14 @@
 //     256-byte runs of the chunk-major blob, where all channels at one K
 //     position are contiguous, so the waves of all workgroups that are at the
 //     same point of K read one contiguous window (what HBM streams best);
-//   * the activation fragment of a group is loaded once and used for all NT
-//     slices, which keeps activation loads from crowding out weight loads;
+//   * every operand of a group (the NT weight chunks, their scale and zero
+//     words and the activation rows the tokens need: 4, 8 or 16 of them) is
+//     copied straight from global memory into a per-wave ring of D LDS slots
+//     (global_load_lds, no register staging), D - 1 groups ahead of the group
+//     being multiplied; all copies are the same kind of vector-memory
+//     operation, so one counter wait per group covers them and nothing else
+//     waits on the prefetch; the activation rows of a group are read from LDS
+//     once and used for all NT slices;
 //   * the codes stay packed until they are in registers ([QK] §9.5): an AND
 //     with 0x000F000F and an OR with the bit pattern of fp16 1024.0 (0x6400)
 //     or bf16 128.0 (0x4300) turns a pair of nibbles into the exact pair
@@ -35,12 +41,17 @@
 
 #include "ql_internal.h"
 
+#ifdef QL_GEMV_SWEEP
+#include <cstdlib>
+#endif
+
 namespace ql {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemvArgs {
   const uint16_t* X;
@@ -75,132 +86,284 @@ __device__ inline uint32_t neg_offset_pair(uint32_t z) {
   return h | (h << 16);
 }
 
-// NT: 16-column slices per wave; U: groups per step (even, so a step covers
-// whole pairs of groups and their shared scale / zero words)
-template <int NT, int U>
-struct StepBuf {
-  uint4 w[U][NT];          // one 16-byte chunk per group and slice
-  uint4 x[U][4];           // activation fragments of each group (shared by the slices)
-  uint32_t s[U / 2][NT];   // fp16 scales of a pair of groups
-  uint32_t z[U / 2][NT];   // zero points of a pair of groups (two nibbles)
+// issues one 16-byte global -> LDS copy per lane (lane i writes lds + 16 i)
+__device__ inline void load_lds16(const void* src, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#else
+  (void)src;
+  (void)lds;
+#endif
+}
+
+// issues one 4-byte global -> LDS copy per lane (lane i writes lds + 4 i)
+__device__ inline void load_lds4(const void* src, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+#else
+  (void)src;
+  (void)lds;
+#endif
+}
+
+// waits until at most N of this wave's vector-memory operations are in flight
+template <int N>
+__device__ inline void wait_vm() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // gfx9 s_waitcnt: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maximum
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+#endif
+}
+
+// LDS read of one 16-byte activation fragment at byte address addr.
+// Inline assembly keeps the compiler's conservative tracking of in-flight
+// LDS copies (it would wait for every outstanding load, including the next
+// step's prefetch) out of the loop; the ordering is enforced explicitly by
+// wait_vm before the reads and lds_wait before the fragments are used.
+// waits until at most k groups of L copies each are in flight (0 <= k < D)
+template <int D, int L>
+__device__ inline void wait_groups(int k) {
+  static_assert(D <= 9, "ring depth");
+  switch (k) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<L>(); break;
+    case 2: if constexpr (D > 2) wait_vm<2 * L>(); break;
+    case 3: if constexpr (D > 3) wait_vm<3 * L>(); break;
+    case 4: if constexpr (D > 4) wait_vm<4 * L>(); break;
+    case 5: if constexpr (D > 5) wait_vm<5 * L>(); break;
+    case 6: if constexpr (D > 6) wait_vm<6 * L>(); break;
+    case 7: if constexpr (D > 7) wait_vm<7 * L>(); break;
+    default: wait_vm<0>(); break;
+  }
+}
+
+__device__ inline u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+#else
+  v = u32x4{addr, 0, 0, 0};   // host pass only (never executed)
+#endif
+  return v;
+}
+__device__ inline void lds_wait() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
+}
+// makes the value depend on the preceding lds_wait
+__device__ inline void after_wait(u32x4& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#endif
+}
+
+__device__ inline uint32_t lds_read4(uint32_t addr) {
+  uint32_t v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+#else
+  v = addr;   // host pass only (never executed)
+#endif
+  return v;
+}
+__device__ inline void after_wait(uint32_t& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#endif
+}
+
+// One step of one wave = one 128-wide group: the staging slot holds, in this
+// order, the NT weight chunks (1 KB each, lane l's 16 bytes at 16 l), the
+// scale-pair words and the zero-point words of the workgroup's 16 * NT
+// channels (256 B each: lane l copies the word of slice (l / 16) % NT,
+// channel l % 16) and 4 * MB activation rows of the group (1 KB per 4 rows).
+template <int NT, int MB>
+struct Slot {
+  static constexpr int kW = 0;
+  static constexpr int kS = NT * 1024;
+  static constexpr int kZ = kS + 256;
+  static constexpr int kX = kZ + 256;
+  static constexpr int kBytes = kX + MB * 1024;
+  static constexpr int kLoads = NT + 2 + MB;      // copies a wave issues per step
+  static constexpr int kRows = 4 * MB;
 };
 
-template <bool BF16, int NT, int U>
-__global__ __launch_bounds__(512) void q4_gemv_kernel(GemvArgs a) {
-  __shared__ f32x4 red[8][NT][64];
-  const int nw = blockDim.x >> 6;
+#ifndef QL_GEMV_LDS_BUDGET
+#define QL_GEMV_LDS_BUDGET (60 * 1024)
+#endif
+// Depth of each wave's ring of staging slots: as deep as the workgroup's LDS
+// budget allows (D - 1 groups of copies in flight while one group is
+// multiplied), at least 2 and at most 9.  Measured on the Llama-2 7B / 70B
+// decode layers with weights streamed from HBM: 8 waves per workgroup with
+// 1 - 2 groups in flight each stream best; deeper rings (more copies in flight
+// per compute unit, fewer workgroups per compute unit) are slower, as for a
+// plain streaming read.
+template <int NT, int MB, int NW>
+constexpr int ring_depth() {
+  const int d = QL_GEMV_LDS_BUDGET / (NW * Slot<NT, MB>::kBytes);
+  return d > 9 ? 9 : d < 2 ? 2 : d;
+}
+
+// NT: 16-column slices per workgroup; MB: blocks of 4 activation rows staged
+// per group (4 * MB >= M); NW: waves per workgroup (they split K).
+template <bool BF16, int NT, int MB, int NW>
+__global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
+  using SL = Slot<NT, MB>;
+  constexpr int D = ring_depth<NT, MB, NW>();
+  constexpr int kWaveBytes = D * SL::kBytes;
+  static_assert(kWaveBytes >= NT * 64 * 16, "the reduction reuses a wave's staging area");
+  static_assert(NT == 1 || NT == 2 || NT == 4, "slices per workgroup");
+  __shared__ __align__(1024) uint8_t lds_all[NW * kWaveBytes];
+
   // the wave index is uniform; saying so keeps the K loop a scalar loop
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int cl = lane & 15, blk = lane >> 4;
   const int G = a.K / kGroup;
-  const int gpw = ((G + nw - 1) / nw + U - 1) / U * U;          // groups per wave, whole steps
+  const int gpw = (G + NW - 1) / NW;                             // groups per wave
   const int g0 = min(G, wave * gpw), g1 = min(G, g0 + gpw);
-  const int gl = max(G - 1, 0);
+  uint8_t* ring = lds_all + wave * kWaveBytes;
+  // Column block of this workgroup.  Workgroups are dealt round-robin to the
+  // 8 XCDs, each with its own L2; neighbouring blocks share the 128-byte lines
+  // of the scale and zero-point rows, so consecutive blocks go to one XCD
+  // (otherwise up to 8 L2s would each fetch the same line).
+  const int full = gridDim.x & ~7;
+  const int cb = (int)blockIdx.x < full ? (blockIdx.x & 7) * (full >> 3) + (blockIdx.x >> 3) : blockIdx.x;
 
-  const uint4* wp[NT];
-  const uint32_t* sp[NT];
-  const uint8_t* zp[NT];
+  // global sources of this lane's copies
+  const uint4* wsrc[NT];
   const size_t np = a.Np;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int n = (blockIdx.x * NT + t) * 16 + cl;          // output channel of this lane in slice t
-    wp[t] = a.W + (size_t)blk * np + n;                     // + 4*Np*g for group g
-    sp[t] = a.S + n;                                        // + Np*(g/2)
-    zp[t] = a.Z + n;
+    const int n = (cb * NT + t) * 16 + cl;                  // output channel of this lane in slice t
+    wsrc[t] = a.W + (size_t)blk * np + n;                   // + 4*Np*g for group g
   }
-  const bool row_ok = cl < a.M;                                           // A-operand row of this lane
-  const uint32_t rmask = row_ok ? 0xFFFFFFFFu : 0u;
-  const uint16_t* xp = a.X + (size_t)(row_ok ? cl : 0) * a.K + blk * kChunkK;   // + 128*g + 8*j
+  // scale and zero words: lane l copies those of slice (l / 16) % NT, channel
+  // l % 16; the zero-point byte of a channel is read as the aligned word
+  // holding it
+  const int nsz = (cb * NT + (blk % NT)) * 16 + cl;
+  const uint32_t* ssrc = a.S + nsz;                                          // + Np*(g/2)
+  const uint32_t* zsrc = reinterpret_cast<const uint32_t*>(a.Z + (nsz & ~3));   // + Np/4 words per pair
+  const int zshift = 8 * (cl & 3);                          // channel bases are multiples of 16
+  // Activation rows: lane l copies row r = 4b + l/16 of block b into stored
+  // piece l % 16, which holds the row's logical 16-byte piece (l % 16) ^ r
+  // (rows at or past M repeat row M - 1: a valid load; those rows are zeroed
+  // when read).
+  const uint16_t* xsrc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int r = 4 * b + blk;
+    xsrc[b] = a.X + (size_t)min(r, a.M - 1) * a.K + ((cl ^ r) & 15) * 8;   // + 128*g
+  }
 
-  // All loads are branch-free (indices clamped into the layer, values past the
-  // wave's range discarded) and a whole step ahead of their use: a step first
-  // issues every load of the next step, then computes on data issued one step
-  // earlier, so the in-order vector-memory counter never waits on a prefetch.
-  auto issue = [&](int gs, StepBuf<NT, U>& b) {
+  // LDS byte addresses of this lane's reads inside slot 0
+  typedef __attribute__((address_space(3))) uint8_t* lds_ptr;
+  const uint32_t rbase = (uint32_t)(uintptr_t)(lds_ptr)ring;
+  const uint32_t w_rd = rbase + SL::kW + lane * 16;
+  const uint32_t s_rd = rbase + SL::kS + cl * 4;          // + 64 * t for slice t
+  const uint32_t z_rd = rbase + SL::kZ + cl * 4;
+  // A operand of the 16x16x32 MFMA: lane l supplies row l % 16, k values
+  // 8 * (l / 16) .. +8 of each 32-wide k step j, i.e. logical piece 4*blk + j
+  const int rr = min(cl, SL::kRows - 1);
+  const uint32_t rmask = cl < a.M ? 0xFFFFFFFFu : 0u;
+  uint32_t x_rd[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = min(gs + u, gl);
+  for (int j = 0; j < 4; ++j) x_rd[j] = rbase + SL::kX + rr * 256 + (((4 * blk + j) ^ rr) & 15) * 16;
+
+  // the copies of group g (inside the wave's range) into ring slot `slot`
+  auto issue = [&](int g, int slot) {
+    uint8_t* dst = ring + slot * SL::kBytes;
+    const int pr = g >> 1;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) b.w[u][t] = wp[t][(size_t)g * 4 * np];
+    for (int t = 0; t < NT; ++t) load_lds16(wsrc[t] + (size_t)g * 4 * np, dst + SL::kW + t * 1024);
+    load_lds4(ssrc + (size_t)pr * np, dst + SL::kS);
+    load_lds4(zsrc + (size_t)pr * (np / 4), dst + SL::kZ);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b.x[u][j] = *reinterpret_cast<const uint4*>(xp + (size_t)g * kGroup + 8 * j);
-    }
-#pragma unroll
-    for (int p = 0; p < U / 2; ++p) {
-      const int pr = min(gs + 2 * p, gl) >> 1;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        b.s[p][t] = sp[t][(size_t)pr * np];
-        b.z[p][t] = zp[t][(size_t)pr * np];
-      }
-    }
+    for (int b = 0; b < MB; ++b) load_lds16(xsrc[b] + (size_t)g * kGroup, dst + SL::kX + b * 1024);
   };
 
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int gs, const StepBuf<NT, U>& b) {
+  auto compute = [&](int g, int slot) {
+    const uint32_t so = slot * SL::kBytes;
+    u32x4 xa[4], wv[NT];
+    uint32_t sv[NT], zv[NT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // straight-line for every u: a group past the wave's range gets scale 0;
-      // masks are arithmetic, not selects (a select of a loaded value would
-      // become a branch around the load)
-      const float valid = gs + u < g1 ? 1.0f : 0.0f;
-      uint4 xa[4];
+    for (int j = 0; j < 4; ++j) xa[j] = lds_read16(x_rd[j] + so);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xa[j] = make_uint4(b.x[u][j].x & rmask, b.x[u][j].y & rmask, b.x[u][j].z & rmask, b.x[u][j].w & rmask);
+    for (int t = 0; t < NT; ++t) {
+      wv[t] = lds_read16(w_rd + so + t * 1024);
+      sv[t] = lds_read4(s_rd + so + t * 64);
+      zv[t] = lds_read4(z_rd + so + t * 64);
+    }
+    lds_wait();
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int h = u & 1;                                   // steps start on even groups
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(b.s[u >> 1][t] >> (16 * h))) * valid;
-        const uint32_t nz = neg_offset_pair<BF16>((b.z[u >> 1][t] >> (4 * h)) & 0xFu);
-        const uint4 bz = make_uint4(nz, nz, nz, nz);
-        const uint32_t ww[4] = {b.w[u][t].x, b.w[u][t].y, b.w[u][t].z, b.w[u][t].w};
-        f32x4 t0 = {0.0f, 0.0f, 0.0f, 0.0f}, t1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 4; ++j) {
+      after_wait(xa[j]);
+      xa[j] &= rmask;
+    }
+    const int h = g & 1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          t0 = mfma<BF16>(xa[j], unpack8<BF16>(ww[j]), t0);
-          t1 = mfma<BF16>(xa[j], bz, t1);
-        }
+    for (int t = 0; t < NT; ++t) {
+      after_wait(wv[t]);
+      after_wait(sv[t]);
+      after_wait(zv[t]);
+      const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[t] >> (16 * h)));
+      const uint32_t nz = neg_offset_pair<BF16>((zv[t] >> (zshift + 4 * h)) & 0xFu);
+      const uint4 bz = make_uint4(nz, nz, nz, nz);
+      f32x4 t0 = {0.0f, 0.0f, 0.0f, 0.0f}, t1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] += s * (t0[i] + t1[i]);
+      for (int j = 0; j < 4; ++j) {
+        const uint4 x = __builtin_bit_cast(uint4, xa[j]);
+        t0 = mfma<BF16>(x, unpack8<BF16>(wv[t][j]), t0);
+        t1 = mfma<BF16>(x, bz, t1);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] += s * (t0[i] + t1[i]);
     }
   };
 
-  StepBuf<NT, U> ba, bb;
-  issue(g0, ba);
-  // two steps per iteration with the buffers swapping roles, so no register
-  // copy ever waits on a prefetch
-  for (int gs = g0; gs < g1;) {
-    issue(gs + U, bb);
-    __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the arithmetic
-    compute(gs, ba);
-    gs += U;
-    if (gs >= g1) break;
-    issue(gs + U, ba);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(gs, bb);
-    gs += U;
-  }
-
-  // ---- add the waves' tiles; lane l holds rows 4*(l/16) + i of column l % 16
+  // prologue: groups g0 .. g0 + D - 2 in flight (those inside the range)
 #pragma unroll
-  for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
+  for (int i = 0; i < D - 1; ++i)
+    if (g0 + i < g1) issue(g0 + i, i);
+  int slot = 0;
+  for (int g = g0; g < g1; ++g) {
+    // refill the slot the previous group was read from (its reads finished
+    // before its arithmetic) with group g + D - 1, then wait until group g's
+    // copies have landed: the groups issued after it may stay in flight
+    if (g + D - 1 < g1) {
+      issue(g + D - 1, slot == 0 ? D - 1 : slot - 1);
+      wait_vm<(D - 1) * SL::kLoads>();
+    } else {
+      wait_groups<D, SL::kLoads>(g1 - 1 - g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(g, slot);
+    __builtin_amdgcn_sched_barrier(0);
+    slot = slot == D - 1 ? 0 : slot + 1;
+  }
+  wait_vm<0>();                           // no copy may still target the staging area
+
+  // ---- add the waves' tiles (each in its own staging area); lane l holds
+  // rows 4*(l/16) + i of column l % 16
+  f32x4* red = reinterpret_cast<f32x4*>(ring);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) red[t * 64 + lane] = acc[t];
   __syncthreads();
   if (wave != 0) return;
-  for (int w = 1; w < nw; ++w)
+  for (int w = 1; w < NW; ++w)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const f32x4 o = red[w][t][lane];
+      const f32x4 o = reinterpret_cast<const f32x4*>(lds_all + w * kWaveBytes)[t * 64 + lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[t][i] += o[i];
     }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int n = (blockIdx.x * NT + t) * 16 + cl;
+    const int n = (cb * NT + t) * 16 + cl;
     if (n >= a.N) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -212,15 +375,31 @@ __global__ __launch_bounds__(512) void q4_gemv_kernel(GemvArgs a) {
   }
 }
 
+template <bool BF16, int NT, int MB>
+hipError_t launch_cfg(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
+  const dim3 grid(a.Np / (16 * NT));
+  if (P.waves == 8)
+    hipLaunchKernelGGL((q4_gemv_kernel<BF16, NT, MB, 8>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((q4_gemv_kernel<BF16, NT, MB, 4>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int NT>
+hipError_t launch_nt(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
+  // activation rows staged per group: 4, 8 or 16
+  if (a.M <= 4) return launch_cfg<BF16, NT, 1>(a, P, st);
+  if (a.M <= 8) return launch_cfg<BF16, NT, 2>(a, P, st);
+  return launch_cfg<BF16, NT, 4>(a, P, st);
+}
+
 template <bool BF16>
 hipError_t launch_dtype(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
-  const dim3 grid(a.Np / (16 * P.nt)), block(64 * P.waves);
   switch (P.nt) {
-    case 4: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 4, 2>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 2, 2>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((q4_gemv_kernel<BF16, 1, 2>), grid, block, 0, st, a); break;
+    case 4: return launch_nt<BF16, 4>(a, P, st);
+    case 2: return launch_nt<BF16, 2>(a, P, st);
+    default: return launch_nt<BF16, 1>(a, P, st);
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -232,11 +411,13 @@ GemvPlan plan_q4_gemv(int M, int N, int K) {
   const Q4Layout L = q4_layout(N, K);
   const int slices = L.Np / 16;
   // widest column block that still leaves a workgroup for every compute unit;
-  // four waves per workgroup (measured on the Llama-2 7B / 70B layer shapes:
-  // fewer concurrent weight streams per compute unit keep HBM busier than
-  // more, as for a plain streaming read)
+  // eight waves per workgroup, splitting K
   P.nt = (slices / 4 >= 256) ? 4 : (slices / 2 >= 256) ? 2 : 1;
-  P.waves = 4;
+  P.waves = 8;
+#ifdef QL_GEMV_SWEEP
+  if (const char* e = getenv("QL_NT")) { int v = atoi(e); if (v == 1 || v == 2 || v == 4) P.nt = v; }
+  if (const char* e = getenv("QL_W")) { int v = atoi(e); if (v == 4 || v == 8) P.waves = v; }
+#endif
   return P;
 }
 
