@@ -1,14 +1,34 @@
-// W4A16 GEMM for large M (prefill): Y = X · dequant(W)ᵀ on bf16/fp16 MFMA.
+// W4A16 GEMM for large M (prefill): Y = X · dequant(W)ᵀ on 16-bit MFMA.
 //
-// Structure ([QK] §9.5 and the tiled pseudocode of [LQ]'s W4A16 section):
-// each workgroup owns a BM x BN tile of Y and walks K one 128-wide group at
-// a time; the X tile and the still-packed W tile are staged in LDS (double
-// buffered, the next k-block's global loads in flight during the current
-// block's MFMAs); each wave reads its packed codes from LDS, expands them to
-// 16-bit floats in registers with the group's scale and zero point, and feeds
-// v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation.  The scale and zero
-// of a group are constant over a k-block, so they are loaded once per block.
+// With many tokens the layer is compute-bound ([LQ] "带宽与算力：Roofline":
+// the arithmetic intensity grows with the token count), and the dequant is
+// extra vector work competing with the matrix unit ([LQ] W4A16 section: at
+// large batch a naive W4A16 kernel can lose to fp16).  The kernel therefore
+// spends the vector ALU on nothing but the dequant and amortizes each
+// dequantized weight over as many tokens as the register file allows:
+//
+//   * a workgroup owns a 256 x 256 tile of Y; each of its 4 waves owns all
+//     256 rows x 64 columns (8 x 2 tiles of v_mfma_f32_32x32x16_{bf16,f16},
+//     256 fp32 accumulators per lane), so every weight a wave dequantizes
+//     feeds 8 MFMAs and no weight is dequantized twice in a workgroup;
+//   * K advances in blocks of 64 through a ring of 3 LDS stages filled by
+//     global_load_lds (no register staging), two blocks ahead: the X tile
+//     (shared by the 4 waves; 16-byte pieces XOR-swizzled by row so the MFMA
+//     operand reads spread over the banks), and per wave its still-packed
+//     weight chunks and the group's scale and zero-point words;
+//   * the codes stay packed until they are in registers ([QK] §9.5) and are
+//     expanded there with the group's scale and zero point to
+//     s * (q - z) (exact in fp32: both products are exact and so is their
+//     difference), rounded once to the MFMA's 16-bit type ([LQ] W4A16
+//     section: dequant of a K tile with the tile's group scale, then the
+//     product);
+//   * inside a 32-wide chunk the two MFMA k-steps take k values in the order
+//     (lane half h, step s) -> 8 * (2h + s) .. +8, for X and W alike; a
+//     consistent permutation of k leaves every dot product unchanged, and it
+//     lets each lane read its 8 codes of both steps as one 8-byte word pair.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "ql_internal.h"
 
@@ -18,168 +38,359 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int APAD = 8;                       // halves of padding per X row in LDS
-constexpr int AROW = BK + APAD;               // LDS row length of the X tile (halves)
-constexpr int A_TILE = BM * AROW;             // halves per X buffer
-constexpr int B_TILE = (BK / kChunkK) * BN * 16;   // bytes per W buffer: [chunk][column] x 16 bytes
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kWaves = 4;                       // wave w: all BM rows x columns 64w .. 64w+63
+constexpr int kStages = 3;
+constexpr int kATile = BM * BK * 2;             // X tile of one stage: 256 rows x 128 bytes
+constexpr int kBWave = 2 * 64 * 16;             // packed weights of one wave: 2 chunks x 64 columns x 16 B
+constexpr int kSZWave = 2 * 256;                // scale words, then zero-point words, of one wave
+constexpr int kBOff = kATile;
+constexpr int kSZOff = kBOff + kWaves * kBWave;
+constexpr int kStage = kSZOff + kWaves * kSZWave;           // 43008 bytes
+constexpr int kAFills = kATile / 1024 / kWaves;             // 1 KB X blocks per wave and stage
+constexpr int kLoads = kAFills + 2 + 2;                     // copies per wave and stage
+
+__shared__ __align__(1024) uint8_t g_lds[kStages * kStage];
 
 struct GemmArgs {
   const uint16_t* X;
-  int M, K, N, Np, Kp;
-  const uint4* W;
-  const uint32_t* S;
-  const uint8_t* Z;
+  int M, K, N, Np;
+  const uint4* W;          // [Kp/32][Np] chunks
+  const uint32_t* S;       // [Kp/256][Np] scale pairs
+  const uint8_t* Z;        // [Kp/256][Np] zero pairs
   uint16_t* Y;
 };
 
-__device__ inline uint32_t pack2(float lo, float hi, bool bf16) {
-  if (bf16) {
-    const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo), b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-    return a | (b << 16);
-  }
-  const uint32_t a = __builtin_bit_cast(uint16_t, (_Float16)lo), b = __builtin_bit_cast(uint16_t, (_Float16)hi);
-  return a | (b << 16);
+// ---- global -> LDS copies and counter waits
+__device__ inline void load_lds16(const void* src, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#else
+  (void)src;
+  (void)lds;
+#endif
+}
+__device__ inline void load_lds4(const void* src, uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+#else
+  (void)src;
+  (void)lds;
+#endif
+}
+template <int N>
+__device__ inline void wait_vm() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+#endif
+}
+// waits until at most N of this wave's LDS reads are in flight
+template <int N>
+__device__ inline void wait_lgkm() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | ((0x3F >> 4) << 14) | (0x7 << 4) | ((N & 0xF) << 8));
+#endif
 }
 
-// 8 codes of one word (k offsets 0..7, code of k = 2i at bits 4i, of k = 2i+1
-// at bits 16 + 4i) -> 8 dequantized 16-bit values s * (q - z), as 4 pairs.
-__device__ inline uint4 dequant8(uint32_t w, float s, float nzs, bool bf16) {
-  uint32_t r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = fmaf((float)((w >> (4 * i)) & 0xFu), s, nzs);
-    const float hi = fmaf((float)((w >> (16 + 4 * i)) & 0xFu), s, nzs);
-    r[i] = pack2(lo, hi, bf16);
+// LDS reads as inline assembly (the compiler would otherwise wait for every
+// in-flight LDS copy before each read, including the prefetch of later
+// stages); the order is enforced by wait_vm + s_barrier before a stage is
+// read and wait_lgkm + after_wait before the values are used.
+template <int OFF>
+__device__ inline u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+#else
+  v = u32x4{addr, OFF, 0, 0};
+#endif
+  return v;
+}
+template <int OFF>
+__device__ inline u32x2 lds_read8(uint32_t addr) {
+  u32x2 v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+#else
+  v = u32x2{addr, OFF};
+#endif
+  return v;
+}
+template <int OFF>
+__device__ inline uint32_t lds_read4(uint32_t addr) {
+  uint32_t v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+#else
+  v = addr + OFF;
+#endif
+  return v;
+}
+template <typename T>
+__device__ inline void after_wait(T& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#else
+  (void)v;
+#endif
+}
+
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
-  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> one register of two 16-bit values (round to nearest even)
+template <bool BF16>
+__device__ inline uint32_t pack2(float lo, float hi) {
+  if constexpr (BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+
+// hides a value from the optimizer (keeps the byte-lane form of the split
+// nibbles, which converts to float in one instruction per byte)
+__device__ inline uint32_t opaque(uint32_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#endif
+  return v;
+}
+
+// One word of 8 codes (code i at nibble position (i & 1) * 4 + (i >> 1)) ->
+// the MFMA B operand of 8 consecutive k: register r = (k 2r, k 2r + 1), each
+// s * (q - z) rounded once to the 16-bit type.  Splitting the word into its
+// low and high nibbles puts codes 0, 4, 1, 5 and 2, 6, 3, 7 in byte lanes,
+// which convert to float one byte at a time.
+template <bool BF16>
+__device__ inline u32x4 dequant8(uint32_t w, float s, float nzs) {
+  const uint32_t lo = opaque(w & 0x0F0F0F0Fu), hi = opaque((w >> 4) & 0x0F0F0F0Fu);
+  const float c0 = (float)(lo & 0xFFu), c4 = (float)((lo >> 8) & 0xFFu);
+  const float c1 = (float)((lo >> 16) & 0xFFu), c5 = (float)(lo >> 24);
+  const float c2 = (float)(hi & 0xFFu), c6 = (float)((hi >> 8) & 0xFFu);
+  const float c3 = (float)((hi >> 16) & 0xFFu), c7 = (float)(hi >> 24);
+  return u32x4{pack2<BF16>(fmaf(c0, s, nzs), fmaf(c1, s, nzs)), pack2<BF16>(fmaf(c2, s, nzs), fmaf(c3, s, nzs)),
+               pack2<BF16>(fmaf(c4, s, nzs), fmaf(c5, s, nzs)), pack2<BF16>(fmaf(c6, s, nzs), fmaf(c7, s, nzs))};
+}
+
+template <bool BF16>
+__device__ inline f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+}
+
+// Workgroup -> tile.  Workgroups are dealt round-robin to the 8 XCDs; when
+// the tile count allows, each XCD gets a contiguous run of a grouped order
+// (4 tile rows at a time), so the tiles an XCD works on at once share X rows
+// and weight columns in its L2.
+__device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
+  const int T = tm * tn;
+  const int t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  constexpr int GM = 4;
+  const int gsize = GM * tn;
+  const int first = (t / gsize) * GM;
+  const int gm = min(tm - first, GM);
+  mt = first + (t % gsize) % gm;
+  nt = (t % gsize) / gm;
+}
+
+// Per-lane sources and LDS destinations of one wave's copies for a stage.
+struct FillPlan {
+  const uint16_t* x[kAFills];   // X row of each 1 KB block (+ the lane's logical piece)
+  int xdst[kAFills];            // byte offset of the block inside the stage
+  const uint4* w;               // weight chunk column of lane l (chunk index added per block)
+  const uint32_t* s;            // scale word column of lane l
+  const uint32_t* z;            // aligned word holding lane l's zero-point byte
+  int wdst, szdst;              // byte offsets of the wave's weight and scale/zero areas
+};
+
+template <int S>
+__device__ inline void fill(const FillPlan& f, int kb, size_t np) {
+  uint8_t* st = g_lds + S * kStage;
+#pragma unroll
+  for (int i = 0; i < kAFills; ++i) load_lds16(f.x[i] + (size_t)kb * BK, st + f.xdst[i]);
+  load_lds16(f.w + (size_t)(2 * kb) * np, st + f.wdst);
+  load_lds16(f.w + (size_t)(2 * kb + 1) * np, st + f.wdst + 1024);
+  const int pr = kb >> 2;                                   // pair of groups of this k block
+  load_lds4(f.s + (size_t)pr * np, st + f.szdst);
+  load_lds4(f.z + (size_t)pr * (np / 4), st + f.szdst + 256);
+}
+
+template <bool BF16>
+struct Frag {
+  f32x16 acc[8][2];
+};
+
+// Multiplies stage S (k block kb) into the accumulators.
+//   xrd[j]: LDS address (stage 0) of the lane's X piece for k step j of the
+//           block (j = 2c + s); + 4096 per 32-row tile, + kStage per stage
+//   wrd:    LDS address (stage 0) of the lane's 8-byte word pair of chunk 0
+//   szrd:   LDS address (stage 0) of the lane's scale word of column tile 0
+template <bool BF16, int S>
+__device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd,
+                               int zshift) {
+  constexpr int SO = S * kStage;
+  const uint32_t wst = wrd + SO, szst = szrd + SO;
+  // packed words (2 chunks x 2 column tiles) and this group's scale / zero
+  u32x2 wv[2][2];
+  uint32_t sv[2], zv[2];
+  static_for<0, 2>([&](auto C) {
+    static_for<0, 2>([&](auto T) { wv[C][T] = lds_read8<C * 1024 + T * 512>(wst); });
+  });
+  static_for<0, 2>([&](auto T) {
+    sv[T] = lds_read4<T * 128>(szst);
+    zv[T] = lds_read4<256 + T * 128>(szst);
+  });
+  u32x4 xa[2][8];
+  static_for<0, 8>([&](auto MT) { xa[0][MT] = lds_read16<MT * 4096>(xrd[0] + SO); });
+  wait_lgkm<8>();                                // words, scales, zeros landed
+  const int h = (kb >> 1) & 1;                   // group of the block inside its pair
+  float s[2], nzs[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    after_wait(wv[0][t]);
+    after_wait(wv[1][t]);
+    after_wait(sv[t]);
+    after_wait(zv[t]);
+    s[t] = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[t] >> (16 * h)));
+    nzs[t] = -(float)((zv[t] >> (zshift + 4 * h)) & 0xFu) * s[t];
+  }
+  static_for<0, 4>([&](auto J) {
+    constexpr int j = J;
+    constexpr int cur = j & 1;
+    // B operands of step j: chunk j / 2, word j % 2 of the lane's pair
+    u32x4 b[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) b[t] = dequant8<BF16>(wv[j >> 1][t][j & 1], s[t], nzs[t]);
+    if constexpr (j < 3) {
+      static_for<0, 8>([&](auto MT) { xa[cur ^ 1][MT] = lds_read16<MT * 4096>(xrd[j + 1] + SO); });
+      wait_lgkm<8>();
+    } else {
+      wait_lgkm<0>();
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      after_wait(xa[cur][mt]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) fr.acc[mt][t] = mfma<BF16>(xa[cur][mt], b[t], fr.acc[mt][t]);
+    }
+  });
+}
+
+template <bool BF16, int S>
+__device__ inline void kstep(Frag<BF16>& fr, const FillPlan& f, int kb, int nkb, size_t np,
+                             const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd, int zshift) {
+  // this wave's copies of block kb have landed once only the next block's remain
+  wait_vm<(kStages - 2) * kLoads>();
+  __builtin_amdgcn_s_barrier();   // every wave's copies of block kb landed; block kb - 1 fully read
+  constexpr int F = (S + kStages - 1) % kStages;
+  fill<F>(f, min(kb + kStages - 1, nkb - 1), np);
+  compute<BF16, S>(fr, kb, xrd, wrd, szrd, zshift);
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t as[2][A_TILE];
-  __shared__ __align__(16) uint8_t bs[2][B_TILE];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ntn = (a.N + BN - 1) / BN;
-  const int m0 = (blockIdx.x / ntn) * BM, n0 = (blockIdx.x % ntn) * BN;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int mtile, ntile;
+  tile_of(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, mtile, ntile);
+  const int m0 = mtile * BM, n0 = ntile * BN;
+  const int nw0 = n0 + 64 * wave;                 // first column of this wave
   const int nkb = a.K / BK;
+  const size_t np = a.Np;
 
-  // ---- global -> register staging of one k-block
-  uint4 ra[8], rb[2];
-  auto load_block = [&](int kb) {
-    const int k0 = kb * BK;
+  // ---- copy plan.  X: the stage's 32 blocks of 1 KB (8 rows x 128 bytes),
+  // kAFills per wave; lane l writes row 8b + l / 8, stored piece l % 8,
+  // which holds logical piece (l % 8) ^ (row & 7).  Rows past M repeat row
+  // M - 1 and columns past Np repeat column Np - 1 (valid loads whose results
+  // only reach outputs that are never stored).
+  FillPlan f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + i * 256;          // 0 .. 2047: 128 rows x 16 pieces of 8 halves
-      const int r = idx >> 4, c = idx & 15;
-      const int m = m0 + r;
-      ra[i] = m < a.M ? *reinterpret_cast<const uint4*>(a.X + (size_t)m * a.K + k0 + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + i * 256;          // 0 .. 511: 4 chunks x 128 columns
-      const int c = idx >> 7, col = idx & 127;
-      const int n = n0 + col;
-      rb[i] = n < a.Np ? a.W[(size_t)(kb * 4 + c) * a.Np + n] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + i * 256;
-      const int r = idx >> 4, c = idx & 15;
-      *reinterpret_cast<uint4*>(&as[buf][r * AROW + c * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(&bs[buf][(tid + i * 256) * 16]) = rb[i];
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  load_block(0);
-  store_block(0);
-  __syncthreads();
-
-  const int half = lane >> 5, l32 = lane & 31;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) load_block(kb + 1);
-
-    // scale and zero of this group for the wave's two 32-column MFMA tiles
-    float s[2], nzs[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int n = n0 + wn + nt * 32 + l32;
-      const int g = kb;
-      float sv = 0.0f, zv = 0.0f;
-      if (n < a.Np) {
-        const uint32_t sp = a.S[(size_t)(g / 2) * a.Np + n];
-        const uint32_t zp = a.Z[(size_t)(g / 2) * a.Np + n];
-        sv = (float)__builtin_bit_cast(_Float16, (uint16_t)(sp >> (16 * (g & 1))));
-        zv = (float)((zp >> (4 * (g & 1))) & 0xFu);
-      }
-      s[nt] = sv;
-      nzs[nt] = -zv * sv;
-    }
-
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      uint4 af[2], bf[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        af[mt] = *reinterpret_cast<const uint4*>(&as[buf][(wm + mt * 32 + l32) * AROW + ks * 16 + half * 8]);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int c = wn + nt * 32 + l32;            // column inside the workgroup tile
-        const int chunk = ks >> 1, j = (ks & 1) * 2 + half;
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(&bs[buf][(chunk * BN + c) * 16 + j * 4]);
-        bf[nt] = dequant8(w, s[nt], nzs[nt], BF16);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          if (BF16)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[mt]),
-                                                                  __builtin_bit_cast(bf16x8, bf[nt]), acc[mt][nt], 0, 0, 0);
-          else
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[mt]),
-                                                                 __builtin_bit_cast(f16x8, bf[nt]), acc[mt][nt], 0, 0, 0);
-        }
-    }
-    __syncthreads();
-    if (kb + 1 < nkb) {
-      store_block(buf ^ 1);
-      __syncthreads();
-    }
+  for (int i = 0; i < kAFills; ++i) {
+    const int blk = wave * kAFills + i;
+    const int r = blk * 8 + (lane >> 3);
+    const int m = min(m0 + r, a.M - 1);
+    f.x[i] = a.X + (size_t)m * a.K + ((lane & 7) ^ (r & 7)) * 8;
+    f.xdst[i] = blk * 1024;
   }
+  const int ncol = min(nw0 + lane, a.Np - 1);
+  f.w = a.W + ncol;
+  f.s = a.S + ncol;
+  f.z = reinterpret_cast<const uint32_t*>(a.Z + (ncol & ~3));
+  f.wdst = kBOff + wave * kBWave;
+  f.szdst = kSZOff + wave * kSZWave;
+
+  // ---- read addresses (stage 0)
+  typedef __attribute__((address_space(3))) uint8_t* lds_ptr;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_ptr)g_lds;
+  const int half = lane >> 5, l32 = lane & 31;
+  uint32_t xrd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // step j = 2c + s takes k 32c + 8 * (2 * half + s) .. +8: logical piece 4c + 2*half + s
+    const int p = 4 * (j >> 1) + 2 * half + (j & 1);
+    xrd[j] = base + l32 * 128 + ((p ^ (l32 & 7)) * 16);
+  }
+  const uint32_t wrd = base + f.wdst + l32 * 16 + half * 8;      // + 512 per column tile, + 1024 per chunk
+  const uint32_t szrd = base + f.szdst + l32 * 4;                // + 128 per column tile
+  const int zshift = 8 * (l32 & 3);                              // the column's byte inside its word
+
+  Frag<BF16> fr;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) fr.acc[i][t][e] = 0.0f;
+
+  // prologue: blocks 0 .. kStages - 2 in flight (clamped to the last block)
+  fill<0>(f, 0, np);
+  fill<1>(f, min(1, nkb - 1), np);
+
+  int kb = 0;
+  for (; kb + kStages <= nkb; kb += kStages) {
+    kstep<BF16, 0>(fr, f, kb, nkb, np, xrd, wrd, szrd, zshift);
+    kstep<BF16, 1>(fr, f, kb + 1, nkb, np, xrd, wrd, szrd, zshift);
+    kstep<BF16, 2>(fr, f, kb + 2, nkb, np, xrd, wrd, szrd, zshift);
+  }
+  if (kb < nkb) {
+    kstep<BF16, 0>(fr, f, kb, nkb, np, xrd, wrd, szrd, zshift);
+    if (kb + 1 < nkb) kstep<BF16, 1>(fr, f, kb + 1, nkb, np, xrd, wrd, szrd, zshift);
+  }
+  wait_vm<0>();                                  // no copy may still target LDS at exit
 
   // ---- store: acc element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int t = 0; t < 2; ++t) {
+    const int n = nw0 + 32 * t + l32;
+    if (n >= a.N) continue;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int n = n0 + wn + nt * 32 + l32;
-      if (n >= a.N) continue;
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm + mt * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const int m = m0 + 32 * mt + 8 * (e >> 2) + 4 * half + (e & 3);
         if (m < a.M) {
-          const float v = acc[mt][nt][e];
+          const float v = fr.acc[mt][t][e];
           a.Y[(size_t)m * a.N + n] =
               BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
         }
       }
-    }
+  }
 }
 
 }  // namespace
@@ -192,16 +403,15 @@ hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const u
   a.K = K;
   a.N = N;
   a.Np = L.Np;
-  a.Kp = L.Kp;
   a.W = reinterpret_cast<const uint4*>(blob + L.w_off);
   a.S = reinterpret_cast<const uint32_t*>(blob + L.s_off);
   a.Z = blob + L.z_off;
   a.Y = static_cast<uint16_t*>(Y);
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (bf16)
-    hipLaunchKernelGGL(q4_gemm_kernel<true>, dim3(tiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(q4_gemm_kernel<true>, dim3(tiles), dim3(64 * kWaves), 0, st, a);
   else
-    hipLaunchKernelGGL(q4_gemm_kernel<false>, dim3(tiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(q4_gemm_kernel<false>, dim3(tiles), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError();
 }
 
