@@ -258,7 +258,7 @@ __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4],
   });
   u32x4 xa[2][8];
   static_for<0, 8>([&](auto MT) { xa[0][MT] = lds_read16<MT * 4096>(xrd[0] + SO); });
-  wait_lgkm<8>();                                // words, scales, zeros landed
+  wait_lgkm<0>();                                // words, scales, zeros and step 0's X landed
   const int h = (kb >> 1) & 1;                   // group of the block inside its pair
   float s[2], nzs[2];
 #pragma unroll
@@ -270,24 +270,38 @@ __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4],
     s[t] = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[t] >> (16 * h)));
     nzs[t] = -(float)((zv[t] >> (zshift + 4 * h)) & 0xFu) * s[t];
   }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) after_wait(xa[0][mt]);
+  // B operands of step j: chunk j / 2, word j % 2 of the lane's pair
+  u32x4 b[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) b[0][t] = dequant8<BF16>(wv[0][t][0], s[t], nzs[t]);
   static_for<0, 4>([&](auto J) {
     constexpr int j = J;
     constexpr int cur = j & 1;
-    // B operands of step j: chunk j / 2, word j % 2 of the lane's pair
-    u32x4 b[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) b[t] = dequant8<BF16>(wv[j >> 1][t][j & 1], s[t], nzs[t]);
-    if constexpr (j < 3) {
+    // X of step j + 1 in flight while step j multiplies
+    if constexpr (j < 3)
       static_for<0, 8>([&](auto MT) { xa[cur ^ 1][MT] = lds_read16<MT * 4096>(xrd[j + 1] + SO); });
-      wait_lgkm<8>();
-    } else {
-      wait_lgkm<0>();
+    // one scheduling region: the 16 MFMAs of step j interleaved with the
+    // dequant of step j + 1 (vector ALU work in the shadow of the matrix unit)
+    if constexpr (j < 3) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) b[cur ^ 1][t] = dequant8<BF16>(wv[(j + 1) >> 1][t][(j + 1) & 1], s[t], nzs[t]);
     }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      after_wait(xa[cur][mt]);
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) fr.acc[mt][t] = mfma<BF16>(xa[cur][mt], b[t], fr.acc[mt][t]);
+      for (int t = 0; t < 2; ++t) fr.acc[mt][t] = mfma<BF16>(xa[cur][mt], b[cur][t], fr.acc[mt][t]);
+    if constexpr (j < 3) {
+#if defined(__HIP_DEVICE_COMPILE__)
+      static_for<0, 16>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+      });
+#endif
+      wait_lgkm<0>();
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) after_wait(xa[cur ^ 1][mt]);
     }
   });
 }
@@ -316,7 +330,9 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
 
   // ---- copy plan.  X: the stage's 32 blocks of 1 KB (8 rows x 128 bytes),
   // kAFills per wave; lane l writes row 8b + l / 8, stored piece l % 8,
-  // which holds logical piece (l % 8) ^ (row & 7).  Rows past M repeat row
+  // which holds logical piece (l % 8) ^ ((row >> 1) & 7): the 16 rows one
+  // operand read serves at a time then touch 16 different 16-byte bank groups
+  // (two consecutive 128-byte rows span the 64 banks once).  Rows past M repeat row
   // M - 1 and columns past Np repeat column Np - 1 (valid loads whose results
   // only reach outputs that are never stored).
   FillPlan f;
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
     const int blk = wave * kAFills + i;
     const int r = blk * 8 + (lane >> 3);
     const int m = min(m0 + r, a.M - 1);
-    f.x[i] = a.X + (size_t)m * a.K + ((lane & 7) ^ (r & 7)) * 8;
+    f.x[i] = a.X + (size_t)m * a.K + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
     f.xdst[i] = blk * 1024;
   }
   const int ncol = min(nw0 + lane, a.Np - 1);
@@ -344,7 +360,7 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
   for (int j = 0; j < 4; ++j) {
     // step j = 2c + s takes k 32c + 8 * (2 * half + s) .. +8: logical piece 4c + 2*half + s
     const int p = 4 * (j >> 1) + 2 * half + (j & 1);
-    xrd[j] = base + l32 * 128 + ((p ^ (l32 & 7)) * 16);
+    xrd[j] = base + l32 * 128 + ((p ^ ((l32 >> 1) & 7)) * 16);
   }
   const uint32_t wrd = base + f.wdst + l32 * 16 + half * 8;      // + 512 per column tile, + 1024 per chunk
   const uint32_t szrd = base + f.szdst + l32 * 4;                // + 128 per column tile
