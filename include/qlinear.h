@@ -162,11 +162,12 @@ int q4_unpack(const void* packed, size_t packed_bytes, int N, int K, int group,
  * packed  device blob from q4_pack for (N, K, group), of packed_bytes bytes
  *         (at least q4_packed_bytes(N, K, group)).
  * Y       [M][N] out, same dtype as X, device.
- * M <= 16 runs the decode kernel (each workgroup owns 16 output channels for
- * all of K); larger M the LDS-tiled MFMA GEMM.  Neither needs device scratch.
- * M == 0 or N == 0 is a no-op returning QL_OK.
+ * M <= 16 runs the decode kernel (each workgroup owns 16 * NT output
+ * channels for all of K); larger M the LDS-tiled MFMA GEMM.  Neither needs
+ * device scratch.  M == 0 or N == 0 is a no-op returning QL_OK.
  * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M, N >= 0, K > 0,
- *         K % group == 0; QL_ERR_UNSUPPORTED unless group == 128;
+ *         K % group == 0; QL_ERR_UNSUPPORTED unless group == 128, and for
+ *         M > 16 when X (M*K*2 bytes) or the blob exceeds 4 GiB;
  *         QL_ERR_SIZE if packed_bytes < q4_packed_bytes(N, K, group);
  *         QL_ERR_ALIGN; QL_ERR_HIP.
  */

@@ -66,6 +66,10 @@ int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed,
     return hip_status("q4_gemm", ql::launch_q4_gemv(X, bf16, M, K, N, static_cast<const uint8_t*>(packed),
                                                      L, P, Y, st));
   }
+  // the large-M kernel addresses X and the weights with 32-bit byte offsets
+  if ((size_t)M * K * 2 > 0xFFFFFFFFu || L.bytes > 0xFFFFFFFFu)
+    return ql::set_error(QL_ERR_UNSUPPORTED, "q4_gemm: M*K*2 = %zu bytes or a packed blob of %zu bytes exceeds 4 GiB",
+                         (size_t)M * K * 2, L.bytes);
   return hip_status("q4_gemm", ql::launch_q4_gemm(X, bf16, M, K, N, static_cast<const uint8_t*>(packed), L, Y, st));
 }
 

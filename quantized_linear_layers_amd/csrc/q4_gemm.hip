@@ -41,17 +41,24 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#ifndef QL_GEMM_WM
+#define QL_GEMM_WM 1
+#endif
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kWaves = 4;                       // wave w: all BM rows x columns 64w .. 64w+63
+constexpr int kWM = QL_GEMM_WM;                 // waves along M
+constexpr int kWN = 4;                          // waves along N: wave (wm, wn) owns rows
+constexpr int kWaves = kWM * kWN;               //   wm * BM / kWM .. +BM / kWM, columns 64 wn .. +64
+constexpr int kMT = BM / 32 / kWM;              // 32-row MFMA tiles per wave
 constexpr int kStages = 3;
 constexpr int kATile = BM * BK * 2;             // X tile of one stage: 256 rows x 128 bytes
-constexpr int kBWave = 2 * 64 * 16;             // packed weights of one wave: 2 chunks x 64 columns x 16 B
-constexpr int kSZWave = 2 * 256;                // scale words, then zero-point words, of one wave
+constexpr int kBSlice = 2 * 64 * 16;            // packed weights of a 64-column slice: 2 chunks x 64 x 16 B
+constexpr int kSZSlice = 2 * 256;               // scale words, then zero-point words, of a slice
 constexpr int kBOff = kATile;
-constexpr int kSZOff = kBOff + kWaves * kBWave;
-constexpr int kStage = kSZOff + kWaves * kSZWave;           // 43008 bytes
+constexpr int kSZOff = kBOff + kWN * kBSlice;
+constexpr int kStage = kSZOff + kWN * kSZSlice;             // 43008 bytes
 constexpr int kAFills = kATile / 1024 / kWaves;             // 1 KB X blocks per wave and stage
-constexpr int kLoads = kAFills + 2 + 2;                     // copies per wave and stage
+constexpr int kSliceLoads = 2 / kWM;                        // chunk copies (and scale/zero copies) per wave
+constexpr int kLoads = kAFills + 2 * kSliceLoads;           // copies per wave and stage
 
 __shared__ __align__(1024) uint8_t g_lds[kStages * kStage];
 
@@ -210,30 +217,43 @@ __device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
 }
 
 // Per-lane sources and LDS destinations of one wave's copies for a stage.
+// The waves of one 64-column slice share its weight chunks and its scale and
+// zero-point words: with kWM waves per slice, wave wm copies chunk c = wm (or
+// both chunks when kWM = 1) and the scale words (wm = 0) or the zero-point
+// words (wm = 1).
+// Sources are kept as 32-bit byte offsets from the (uniform) base pointers,
+// one register each; every operand is far below 4 GiB.
 struct FillPlan {
-  const uint16_t* x[kAFills];   // X row of each 1 KB block (+ the lane's logical piece)
+  uint32_t x[kAFills];          // X row of each 1 KB block (+ the lane's logical piece)
   int xdst[kAFills];            // byte offset of the block inside the stage
-  const uint4* w;               // weight chunk column of lane l (chunk index added per block)
-  const uint32_t* s;            // scale word column of lane l
-  const uint32_t* z;            // aligned word holding lane l's zero-point byte
-  int wdst, szdst;              // byte offsets of the wave's weight and scale/zero areas
+  uint32_t w;                   // weight chunk column of lane l (chunk row added per block)
+  uint32_t sz[kSliceLoads];     // scale word of lane l / aligned word holding its zero byte
+  int wdst, szdst;              // byte offsets of the slice's weight and scale/zero areas
+  int c0;                       // first chunk (and scale/zero array) this wave copies
 };
 
 template <int S>
-__device__ inline void fill(const FillPlan& f, int kb, size_t np) {
+__device__ inline void fill(const GemmArgs& a, const FillPlan& f, int kb) {
   uint8_t* st = g_lds + S * kStage;
+  const char* xb = reinterpret_cast<const char*>(a.X);
+  const char* wb = reinterpret_cast<const char*>(a.W);
 #pragma unroll
-  for (int i = 0; i < kAFills; ++i) load_lds16(f.x[i] + (size_t)kb * BK, st + f.xdst[i]);
-  load_lds16(f.w + (size_t)(2 * kb) * np, st + f.wdst);
-  load_lds16(f.w + (size_t)(2 * kb + 1) * np, st + f.wdst + 1024);
-  const int pr = kb >> 2;                                   // pair of groups of this k block
-  load_lds4(f.s + (size_t)pr * np, st + f.szdst);
-  load_lds4(f.z + (size_t)pr * (np / 4), st + f.szdst + 256);
+  for (int i = 0; i < kAFills; ++i) load_lds16(xb + f.x[i] + (uint32_t)kb * (BK * 2), st + f.xdst[i]);
+  const uint32_t pr = kb >> 2;                              // pair of groups of this k block
+  const uint32_t np = a.Np;
+#pragma unroll
+  for (int i = 0; i < kSliceLoads; ++i) {
+    const int c = f.c0 + i;
+    load_lds16(wb + f.w + (uint32_t)(2 * kb + c) * np * 16, st + f.wdst + c * 1024);
+    // scale rows hold one word per column, zero rows one byte per column
+    const char* szb = c == 0 ? reinterpret_cast<const char*>(a.S) : reinterpret_cast<const char*>(a.Z);
+    load_lds4(szb + f.sz[i] + pr * (c == 0 ? np * 4 : np), st + f.szdst + c * 256);
+  }
 }
 
 template <bool BF16>
 struct Frag {
-  f32x16 acc[8][2];
+  f32x16 acc[kMT][2];
 };
 
 // Multiplies stage S (k block kb) into the accumulators.
@@ -256,8 +276,8 @@ __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4],
     sv[T] = lds_read4<T * 128>(szst);
     zv[T] = lds_read4<256 + T * 128>(szst);
   });
-  u32x4 xa[2][8];
-  static_for<0, 8>([&](auto MT) { xa[0][MT] = lds_read16<MT * 4096>(xrd[0] + SO); });
+  u32x4 xa[2][kMT];
+  static_for<0, kMT>([&](auto MT) { xa[0][MT] = lds_read16<MT * 4096>(xrd[0] + SO); });
   wait_lgkm<0>();                                // words, scales, zeros and step 0's X landed
   const int h = (kb >> 1) & 1;                   // group of the block inside its pair
   float s[2], nzs[2];
@@ -271,7 +291,7 @@ __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4],
     nzs[t] = -(float)((zv[t] >> (zshift + 4 * h)) & 0xFu) * s[t];
   }
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) after_wait(xa[0][mt]);
+  for (int mt = 0; mt < kMT; ++mt) after_wait(xa[0][mt]);
   // B operands of step j: chunk j / 2, word j % 2 of the lane's pair
   u32x4 b[2][2];
 #pragma unroll
@@ -281,7 +301,7 @@ __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4],
     constexpr int cur = j & 1;
     // X of step j + 1 in flight while step j multiplies
     if constexpr (j < 3)
-      static_for<0, 8>([&](auto MT) { xa[cur ^ 1][MT] = lds_read16<MT * 4096>(xrd[j + 1] + SO); });
+      static_for<0, kMT>([&](auto MT) { xa[cur ^ 1][MT] = lds_read16<MT * 4096>(xrd[j + 1] + SO); });
     // one scheduling region: the 16 MFMAs of step j interleaved with the
     // dequant of step j + 1 (vector ALU work in the shadow of the matrix unit)
     if constexpr (j < 3) {
@@ -289,42 +309,44 @@ __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4],
       for (int t = 0; t < 2; ++t) b[cur ^ 1][t] = dequant8<BF16>(wv[(j + 1) >> 1][t][(j + 1) & 1], s[t], nzs[t]);
     }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int t = 0; t < 2; ++t) fr.acc[mt][t] = mfma<BF16>(xa[cur][mt], b[cur][t], fr.acc[mt][t]);
     if constexpr (j < 3) {
 #if defined(__HIP_DEVICE_COMPILE__)
-      static_for<0, 16>([&](auto) {
+      static_for<0, 2 * kMT>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
       });
 #endif
       wait_lgkm<0>();
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) after_wait(xa[cur ^ 1][mt]);
+      for (int mt = 0; mt < kMT; ++mt) after_wait(xa[cur ^ 1][mt]);
     }
   });
 }
 
 template <bool BF16, int S>
-__device__ inline void kstep(Frag<BF16>& fr, const FillPlan& f, int kb, int nkb, size_t np,
+__device__ inline void kstep(Frag<BF16>& fr, const GemmArgs& a, const FillPlan& f, int kb, int nkb,
                              const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd, int zshift) {
   // this wave's copies of block kb have landed once only the next block's remain
   wait_vm<(kStages - 2) * kLoads>();
   __builtin_amdgcn_s_barrier();   // every wave's copies of block kb landed; block kb - 1 fully read
   constexpr int F = (S + kStages - 1) % kStages;
-  fill<F>(f, min(kb + kStages - 1, nkb - 1), np);
+  fill<F>(a, f, min(kb + kStages - 1, nkb - 1));
   compute<BF16, S>(fr, kb, xrd, wrd, szrd, zshift);
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int mtile, ntile;
   tile_of(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, mtile, ntile);
   const int m0 = mtile * BM, n0 = ntile * BN;
-  const int nw0 = n0 + 64 * wave;                 // first column of this wave
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int nw0 = n0 + 64 * wn;                   // first column of this wave
+  const int mw0 = m0 + wm * (BM / kWM);           // first row of this wave
   const int nkb = a.K / BK;
   const size_t np = a.Np;
 
@@ -341,15 +363,16 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
     const int blk = wave * kAFills + i;
     const int r = blk * 8 + (lane >> 3);
     const int m = min(m0 + r, a.M - 1);
-    f.x[i] = a.X + (size_t)m * a.K + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+    f.x[i] = ((uint32_t)m * a.K + ((lane & 7) ^ ((r >> 1) & 7)) * 8) * 2;
     f.xdst[i] = blk * 1024;
   }
   const int ncol = min(nw0 + lane, a.Np - 1);
-  f.w = a.W + ncol;
-  f.s = a.S + ncol;
-  f.z = reinterpret_cast<const uint32_t*>(a.Z + (ncol & ~3));
-  f.wdst = kBOff + wave * kBWave;
-  f.szdst = kSZOff + wave * kSZWave;
+  f.w = (uint32_t)ncol * 16;
+  f.c0 = (kWM == 1) ? 0 : wm;
+#pragma unroll
+  for (int i = 0; i < kSliceLoads; ++i) f.sz[i] = (f.c0 + i) == 0 ? (uint32_t)ncol * 4 : (uint32_t)(ncol & ~3);
+  f.wdst = kBOff + wn * kBSlice;
+  f.szdst = kSZOff + wn * kSZSlice;
 
   // ---- read addresses (stage 0)
   typedef __attribute__((address_space(3))) uint8_t* lds_ptr;
@@ -360,7 +383,7 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
   for (int j = 0; j < 4; ++j) {
     // step j = 2c + s takes k 32c + 8 * (2 * half + s) .. +8: logical piece 4c + 2*half + s
     const int p = 4 * (j >> 1) + 2 * half + (j & 1);
-    xrd[j] = base + l32 * 128 + ((p ^ ((l32 >> 1) & 7)) * 16);
+    xrd[j] = base + (wm * (BM / kWM) + l32) * 128 + ((p ^ ((l32 >> 1) & 7)) * 16);
   }
   const uint32_t wrd = base + f.wdst + l32 * 16 + half * 8;      // + 512 per column tile, + 1024 per chunk
   const uint32_t szrd = base + f.szdst + l32 * 4;                // + 128 per column tile
@@ -368,25 +391,25 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
 
   Frag<BF16> fr;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kMT; ++i)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) fr.acc[i][t][e] = 0.0f;
 
   // prologue: blocks 0 .. kStages - 2 in flight (clamped to the last block)
-  fill<0>(f, 0, np);
-  fill<1>(f, min(1, nkb - 1), np);
+  fill<0>(a, f, 0);
+  fill<1>(a, f, min(1, nkb - 1));
 
   int kb = 0;
   for (; kb + kStages <= nkb; kb += kStages) {
-    kstep<BF16, 0>(fr, f, kb, nkb, np, xrd, wrd, szrd, zshift);
-    kstep<BF16, 1>(fr, f, kb + 1, nkb, np, xrd, wrd, szrd, zshift);
-    kstep<BF16, 2>(fr, f, kb + 2, nkb, np, xrd, wrd, szrd, zshift);
+    kstep<BF16, 0>(fr, a, f, kb, nkb, xrd, wrd, szrd, zshift);
+    kstep<BF16, 1>(fr, a, f, kb + 1, nkb, xrd, wrd, szrd, zshift);
+    kstep<BF16, 2>(fr, a, f, kb + 2, nkb, xrd, wrd, szrd, zshift);
   }
   if (kb < nkb) {
-    kstep<BF16, 0>(fr, f, kb, nkb, np, xrd, wrd, szrd, zshift);
-    if (kb + 1 < nkb) kstep<BF16, 1>(fr, f, kb + 1, nkb, np, xrd, wrd, szrd, zshift);
+    kstep<BF16, 0>(fr, a, f, kb, nkb, xrd, wrd, szrd, zshift);
+    if (kb + 1 < nkb) kstep<BF16, 1>(fr, a, f, kb + 1, nkb, xrd, wrd, szrd, zshift);
   }
   wait_vm<0>();                                  // no copy may still target LDS at exit
 
@@ -396,10 +419,10 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(GemmArgs a) {
     const int n = nw0 + 32 * t + l32;
     if (n >= a.N) continue;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + 32 * mt + 8 * (e >> 2) + 4 * half + (e & 3);
+        const int m = mw0 + 32 * mt + 8 * (e >> 2) + 4 * half + (e & 3);
         if (m < a.M) {
           const float v = fr.acc[mt][t][e];
           a.Y[(size_t)m * a.N + n] =
