@@ -5,17 +5,20 @@
 // per-token zero point is a rank-1 correction azp[m] * azp_adj[n], applied
 // element-wise with O(M + N) extra memory).
 //
-// Each workgroup (4 waves, 2 x 2 waves of 64 x 64) owns a 128 x 128 tile and
-// walks K in blocks of 64 bytes through a ring of kStages LDS slots (64 KB, so
-// that two workgroups share a compute unit and hide each other's waits).  The
-// slots are filled straight from global memory by global_load_lds_dwordx4
-// (no register staging), kStages - 1 blocks ahead of the block being
-// multiplied, so the L2 / Infinity-cache latency of an operand block is
-// hidden behind the MFMAs of the blocks before it.  Each slot is its own LDS
-// object and the K loop is unrolled by kStages, so every LDS read names the
-// slot it depends on and waits only for that slot's loads.  Rows of a slot
-// are 64 bytes (4 pieces of 16 bytes) stored with the piece index XORed by
-// row bits, so the rows one MFMA operand read touches spread over the banks.
+// Each workgroup (8 waves, 4 x 2 waves of 64 x 64: two waves per SIMD, so one
+// multiplies while the other waits) owns a 256 x 128 tile and walks K in
+// blocks of 64 bytes through a ring of kStages LDS slots of 24 KB (one
+// workgroup per compute unit).  The slots are filled straight from global
+// memory by global_load_lds_dwordx4 (no register staging), kStages - 1 blocks
+// ahead of the block being multiplied: each block is 32 MFMAs per SIMD, so
+// about 5000 matrix-core cycles of lookahead cover the latency of operand
+// blocks that miss the L2.  Per 32-byte k step a wave reads 2 + 2 operand
+// fragments for 4 MFMAs (1 KB per MFMA: about half the LDS read bandwidth at
+// full MFMA rate).  The epilogue stages each wave's outputs in LDS and writes
+// them as 16-byte row pieces (full cache lines per store instruction).
+// Rows of a slot are 64 bytes (4 pieces of 16 bytes) stored with the piece
+// index XORed by row bits, so the 16 rows one operand read serves at a time
+// fall on 16 different 16-byte bank groups.
 #include <hip/hip_runtime.h>
 
 #include "ql_internal.h"
@@ -26,21 +29,22 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;       // BK in bytes (int8 elements)
-constexpr int kStages = 4;
-constexpr int kSlot = BM * BK;                   // bytes of one operand tile (A and B are the same size)
+#ifndef QL_I8_WAVES
+#define QL_I8_WAVES 8
+#endif
+constexpr int BM = 256, BN = 128, BK = 64;       // BK in bytes (int8 elements)
+constexpr int kWaves = QL_I8_WAVES;              // (BM / (32 kMT)) x 2 waves; wave (wm, wn) owns
+constexpr int kMT = 16 / kWaves, kNT = 2;        //   32 kMT rows x 64 columns (32 x 32 MFMA tiles)
+constexpr int kStages = 6;
+constexpr int kASlot = BM * BK;                  // 16 KB
+constexpr int kBSlot = BN * BK;                  // 8 KB
+constexpr int kSlot = kASlot + kBSlot;           // 24 KB
 constexpr int kPieces = BK / 16;                 // 16-byte pieces per row
+constexpr int kAFills = kASlot / 1024 / kWaves;  // 1 KB blocks of A per wave and slot
+constexpr int kBFills = kBSlot / 1024 / kWaves;  // 1 KB blocks of B per wave and slot
+constexpr int kLoads = kAFills + kBFills;        // copies per wave and slot
 
-// one LDS object per stage holding the A tile then the B tile
-__shared__ __align__(1024) int8_t st0[2 * kSlot], st1[2 * kSlot], st2[2 * kSlot], st3[2 * kSlot];
-
-template <int S>
-__device__ inline int8_t* slot_a() {
-  if constexpr (S == 0) return st0; else if constexpr (S == 1) return st1; else if constexpr (S == 2) return st2;
-  else return st3;
-}
-template <int S>
-__device__ inline int8_t* slot_b() { return slot_a<S>() + kSlot; }
+__shared__ __align__(1024) int8_t g_lds[kStages * kSlot];
 
 struct I8Args {
   const int8_t* A;
@@ -49,10 +53,10 @@ struct I8Args {
   I8Epi e;
 };
 
-// byte offset of logical 16-byte piece p of row r inside a slot: the piece
-// index is XORed with bits 1..2 of the row, so 8 consecutive rows read at one
-// logical piece touch 8 different 16-byte bank groups
-__device__ inline int swz(int r, int p) { return r * BK + ((p ^ ((r >> 1) & 3)) << 4); }
+// byte offset of logical 16-byte piece p of row r inside an operand tile: four
+// 64-byte rows span the 64 banks once, and the piece index is XORed with bits
+// 2..3 of the row
+__device__ inline int swz(int r, int p) { return r * BK + ((p ^ ((r >> 2) & 3)) << 4); }
 
 // issues one 16-byte global -> LDS load per lane (lane i writes lds + 16 i)
 __device__ inline void load_lds16(const int8_t* src, int8_t* lds) {
@@ -64,32 +68,28 @@ __device__ inline void load_lds16(const int8_t* src, int8_t* lds) {
 #endif
 }
 
-// One wave's share of filling a slot: the slot holds 8 blocks of 1 KB
-// (16 rows x 64 bytes) per operand, kFills = 2 per wave.  Lane l of a block
-// writes LDS bytes 16 l .. 16 l + 15 of the block, i.e. row l / 4 and stored
-// piece l % 4, which holds logical piece (l % 4) ^ ((row >> 1) & 3).  Rows
-// past M or N are clamped to the last row (valid loads whose data only
-// reaches outputs that are never stored).
-constexpr int kFills = kSlot / 1024 / 4;         // 1 KB blocks per operand per wave and slot fill
-
+// One wave's share of filling a slot: 1 KB blocks of 16 rows x 64 bytes,
+// kAFills of A and kBFills of B.  Lane l of a block writes LDS bytes
+// 16 l .. 16 l + 15 of the block, i.e. row l / 4 and stored piece l % 4, which
+// holds logical piece (l % 4) ^ ((row >> 2) & 3).  Rows past M or N are
+// clamped to the last row (valid loads whose data only reaches outputs that
+// are never stored).
 struct FillPlan {
-  const int8_t* a[kFills];
-  const int8_t* b[kFills];
-  int p16[kFills];     // byte offset of this lane's logical piece inside a K block
-  int dst[kFills];     // byte offset of the lane's 1 KB destination block inside a slot
+  const int8_t* src[kLoads];   // row of each block
+  int p16[kLoads];             // byte offset of this lane's logical piece inside a K block
+  int dst[kLoads];             // byte offset of the lane's 1 KB destination block inside a slot
 };
 
 __device__ inline FillPlan make_fill_plan(const I8Args& a, int m0, int n0, int wave, int lane) {
   FillPlan f;
 #pragma unroll
-  for (int i = 0; i < kFills; ++i) {
-    const int blkid = wave * kFills + i;           // 1 KB block of the slot
-    const int r = blkid * (1024 / BK) + lane / kPieces;
-    const int m = min(m0 + r, a.M - 1), n = min(n0 + r, a.N - 1);
-    f.a[i] = a.A + (size_t)m * a.K;
-    f.b[i] = a.B + (size_t)n * a.K;
-    f.p16[i] = ((lane % kPieces) ^ ((r >> 1) & 3)) * 16;
-    f.dst[i] = blkid * 1024;
+  for (int i = 0; i < kLoads; ++i) {
+    const bool is_a = i < kAFills;
+    const int blk = is_a ? wave * kAFills + i : wave * kBFills + (i - kAFills);
+    const int r = blk * (1024 / BK) + lane / kPieces;
+    f.src[i] = is_a ? a.A + (size_t)min(m0 + r, a.M - 1) * a.K : a.B + (size_t)min(n0 + r, a.N - 1) * a.K;
+    f.p16[i] = ((lane % kPieces) ^ ((r >> 2) & 3)) * 16;
+    f.dst[i] = (is_a ? 0 : kASlot) + blk * 1024;
   }
   return f;
 }
@@ -99,10 +99,9 @@ __device__ inline FillPlan make_fill_plan(const I8Args& a, int m0, int n0, int w
 template <int S>
 __device__ inline void fill(const FillPlan& f, int kb, int K) {
 #pragma unroll
-  for (int i = 0; i < kFills; ++i) {
+  for (int i = 0; i < kLoads; ++i) {
     const int k = min(kb * BK + f.p16[i], K - 16);
-    load_lds16(f.a[i] + k, slot_a<S>() + f.dst[i]);
-    load_lds16(f.b[i] + k, slot_b<S>() + f.dst[i]);
+    load_lds16(f.src[i] + k, g_lds + S * kSlot + f.dst[i]);
   }
 }
 
@@ -119,22 +118,27 @@ __device__ inline void wait_vm() {
 // that the compiler's conservative tracking of in-flight LDS DMA (it would wait
 // for every outstanding slot fill) stays out of the K loop; the ordering it
 // would enforce is provided explicitly: wait_vm + s_barrier before a slot is
-// read, and lds_wait below before the fragments are used.
-__device__ inline i32x4 lds_read16(const int8_t* p) {
-  typedef __attribute__((address_space(3))) const int8_t* lds_ptr;
-  const uint32_t off = (uint32_t)(uintptr_t)(lds_ptr)p;      // byte offset inside LDS
+// read, and lds_wait + after_wait before the fragments are used.
+__device__ inline i32x4 lds_read16(uint32_t addr) {
   i32x4 v;
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(off) : "memory");
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
 #else
-  v = i32x4{(int)off, 0, 0, 0};   // host pass only (never executed)
+  v = i32x4{(int)addr, 0, 0, 0};   // host pass only (never executed)
 #endif
   return v;
 }
-// waits for this wave's LDS reads and makes the fragments depend on the wait
-__device__ inline void lds_wait(i32x4& a0, i32x4& a1, i32x4& b0, i32x4& b1) {
+// waits until at most N of this wave's LDS reads are in flight
+template <int N>
+__device__ inline void lds_wait() {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1) : : "memory");
+  asm volatile("s_waitcnt lgkmcnt(%0)" : : "n"(N) : "memory");
+#endif
+}
+// makes a fragment depend on the preceding lds_wait
+__device__ inline void after_wait(i32x4& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
 #endif
 }
 
@@ -142,32 +146,44 @@ __device__ inline void lds_wait(i32x4& a0, i32x4& a1, i32x4& b0, i32x4& b1) {
 // block); pieces past it hold whatever the clamped loads fetched and are zeroed
 // here.  Rows past M or N need no masking: they only reach outputs that are
 // never stored.
+//   ard[ks], brd[ks]: LDS addresses (slot 0, tile 0) of the lane's A and B
+//   fragments of k step ks; + 32 * BK per 32-row tile, + kSlot per slot
 template <int S>
-__device__ inline void mma_block(i32x16 (&acc)[2][2], int wm, int wn, int lane, int kvalid) {
-  const int8_t* sa = slot_a<S>();
-  const int8_t* sb = slot_b<S>();
-  const int half = lane >> 5, l32 = lane & 31;
+__device__ inline void mma_block(i32x16 (&acc)[kMT][kNT], const uint32_t (&ard)[2], const uint32_t (&brd)[2],
+                                 int half, int kvalid) {
+  static_assert(BK == 64, "two k steps per block");
+  // operand layout of the 32x32x32 int8 MFMA: lane l supplies row/column l%32,
+  // bytes 16 * (l / 32) .. +16 of the 32-byte k step.  Both k steps'
+  // fragments are read at once; the second step's reads land while the first
+  // multiplies.
+  i32x4 af[2][kMT], bf[2][kNT];
 #pragma unroll
-  for (int ks = 0; ks < BK / 32; ++ks) {
-    // operand layout of the 32x32x32 int8 MFMA: lane l supplies row/column l%32,
-    // bytes 16 * (l / 32) .. +16 of the 32-byte k step
-    const int p = ks * 2 + half;
-    i32x4 af[2], bf[2];
+  for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      af[t] = lds_read16(sa + swz(wm + t * 32 + l32, p));
-      bf[t] = lds_read16(sb + swz(wn + t * 32 + l32, p));
+    for (int t = 0; t < kMT; ++t) af[ks][t] = lds_read16(ard[ks] + S * kSlot + t * 32 * BK);
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) bf[ks][t] = lds_read16(brd[ks] + S * kSlot + t * 32 * BK);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ks == 0)
+      lds_wait<kMT + kNT>();
+    else
+      lds_wait<0>();
+    // pieces past kvalid (a ragged last block): zero the A side
+    const bool live = (ks * 2 + half) * 16 < kvalid;
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      after_wait(af[ks][t]);
+      af[ks][t] = live ? af[ks][t] : i32x4{0, 0, 0, 0};
     }
-    lds_wait(af[0], af[1], bf[0], bf[1]);
-    const bool live = p * 16 < kvalid;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      af[t] = live ? af[t] : i32x4{0, 0, 0, 0};
+    for (int t = 0; t < kNT; ++t) after_wait(bf[ks][t]);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+      for (int nt = 0; nt < kNT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mt], bf[ks][nt], acc[mt][nt], 0, 0, 0);
   }
 }
 
@@ -175,26 +191,38 @@ __device__ inline void mma_block(i32x16 (&acc)[2][2], int wm, int wn, int lane, 
 // block with block kb + kStages - 1 (clamped to the last block near the end, so
 // that every wave always has the same number of loads in flight), multiply slot S
 template <int S>
-__device__ inline void kstep(const I8Args& a, const FillPlan& f, i32x16 (&acc)[2][2], int kb, int nkb, int wm, int wn,
-                             int lane) {
+__device__ inline void kstep(const I8Args& a, const FillPlan& f, i32x16 (&acc)[kMT][kNT], int kb, int nkb,
+                             const uint32_t (&ard)[2], const uint32_t (&brd)[2], int half) {
   // this wave's loads of block kb are done once at most (kStages - 2) blocks
-  // of its loads (2 * kFills each) remain in flight
-  wait_vm<(kStages - 2) * 2 * kFills>();
+  // of its loads remain in flight
+  wait_vm<(kStages - 2) * kLoads>();
   __builtin_amdgcn_s_barrier();                  // every wave's loads of block kb landed,
                                                  // and every wave finished block kb - 1
   constexpr int F = (S + kStages - 1) % kStages;
   fill<F>(f, min(kb + kStages - 1, nkb - 1), a.K);
-  mma_block<S>(acc, wm, wn, lane, a.K - kb * BK);
+  mma_block<S>(acc, ard, brd, half, a.K - kb * BK);
+}
+
+// the last (nkb mod kStages) blocks, slots 0, 1, ... in order
+template <int S>
+__device__ inline void kstep_tail(const I8Args& a, const FillPlan& f, i32x16 (&acc)[kMT][kNT], int kb, int nkb,
+                                  const uint32_t (&ard)[2], const uint32_t (&brd)[2], int half) {
+  if constexpr (S < kStages - 1) {
+    if (kb < nkb) {
+      kstep<S>(a, f, acc, kb, nkb, ard, brd, half);
+      kstep_tail<S + 1>(a, f, acc, kb + 1, nkb, ard, brd, half);
+    }
+  }
 }
 
 // Workgroup -> tile.  Workgroups are dealt round-robin to the 8 XCDs, each
 // with its own L2; when the tile count allows, consecutive tiles of a grouped
-// order (8 tile rows at a time) go to one XCD, so an XCD works on an 8 x 8
-// block of tiles and its L2 serves the A and B rows those tiles share.
+// order (4 tile rows at a time) go to one XCD, so an XCD works on a block of
+// 4 tile rows and its L2 serves the A and B rows those tiles share.
 __device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
   const int T = tm * tn;
   const int t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int gsize = GM * tn;
   const int first = (t / gsize) * GM;
   const int gm = min(tm - first, GM);
@@ -203,65 +231,79 @@ __device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
 }
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void i8_gemm_kernel(I8Args a) {
+__global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int mt, nt;
-  tile_of(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, mt, nt);
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  int mtile, ntile;
+  tile_of(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, mtile, ntile);
+  const int m0 = mtile * BM, n0 = ntile * BN;
+  const int wm = (wave >> 1) * (kMT * 32), wn = (wave & 1) * (kNT * 32);
+  static_assert((kWaves / 2) * kMT * 32 == BM && 2 * kNT * 32 == BN, "waves cover the tile");
   const int nkb = (a.K + BK - 1) / BK;
+  const int half = lane >> 5, l32 = lane & 31;
 
-  i32x16 acc[2][2];
+  i32x16 acc[kMT][kNT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kMT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kNT; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
+  // LDS addresses of the lane's fragments in slot 0, tile 0 ((row + 32 t)
+  // keeps bits 2..3 of the row, so tile t is + 32 * BK * t)
+  typedef __attribute__((address_space(3))) int8_t* lds_ptr;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_ptr)g_lds;
+  uint32_t ard[2], brd[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    ard[ks] = base + swz(wm + l32, ks * 2 + half);
+    brd[ks] = base + kASlot + swz(wn + l32, ks * 2 + half);
+  }
+
   // prologue: blocks 0 .. kStages - 2 in flight (clamped to the last block)
   const FillPlan f = make_fill_plan(a, m0, n0, wave, lane);
+  static_assert(kStages == 6, "the prologue fills kStages - 1 slots");
   fill<0>(f, 0, a.K);
   fill<1>(f, min(1, nkb - 1), a.K);
   fill<2>(f, min(2, nkb - 1), a.K);
+  fill<3>(f, min(3, nkb - 1), a.K);
+  fill<4>(f, min(4, nkb - 1), a.K);
 
   int kb = 0;
   for (; kb + kStages <= nkb; kb += kStages) {
-    kstep<0>(a, f, acc, kb, nkb, wm, wn, lane);
-    kstep<1>(a, f, acc, kb + 1, nkb, wm, wn, lane);
-    kstep<2>(a, f, acc, kb + 2, nkb, wm, wn, lane);
-    kstep<3>(a, f, acc, kb + 3, nkb, wm, wn, lane);
+    kstep<0>(a, f, acc, kb, nkb, ard, brd, half);
+    kstep<1>(a, f, acc, kb + 1, nkb, ard, brd, half);
+    kstep<2>(a, f, acc, kb + 2, nkb, ard, brd, half);
+    kstep<3>(a, f, acc, kb + 3, nkb, ard, brd, half);
+    kstep<4>(a, f, acc, kb + 4, nkb, ard, brd, half);
+    kstep<5>(a, f, acc, kb + 5, nkb, ard, brd, half);
   }
-  if (kb < nkb) {
-    kstep<0>(a, f, acc, kb, nkb, wm, wn, lane);
-    if (kb + 1 < nkb) {
-      kstep<1>(a, f, acc, kb + 1, nkb, wm, wn, lane);
-      if (kb + 2 < nkb) kstep<2>(a, f, acc, kb + 2, nkb, wm, wn, lane);
-    }
-  }
+  kstep_tail<0>(a, f, acc, kb, nkb, ard, brd, half);
   wait_vm<0>();                                  // no load may still target LDS at exit
 
   // ---- fused epilogue: C = Dq - azp*azp_adj (int32), out = s_a * (s_b * C) + bias.
   // Every per-row and per-column parameter is read before the first store
   // (a load after a store the compiler cannot prove disjoint would wait for a
-  // full memory round trip per element): the tile's 128 row scales and zero
-  // points go through LDS (the operand slots are free now), the two columns of
-  // a lane through registers.
+  // full memory round trip per element): the tile's row scales and zero points
+  // go through LDS (the operand slots are free now), a lane's columns through
+  // registers.
   const I8Epi& e = a.e;
-  float* row_s = reinterpret_cast<float*>(st0);
-  int32_t* row_z = reinterpret_cast<int32_t*>(st0 + BM * 4);
+  constexpr int kOutWave = (kMT * 32) * (kNT * 32) * 2;      // a wave's output tile in LDS: 16 KB
+  constexpr int kRowParams = kWaves * kOutWave;              // row scales, then row zero points
+  static_assert(kRowParams + BM * 8 <= kStages * kSlot, "epilogue staging fits in the slots");
+  float* row_s = reinterpret_cast<float*>(g_lds + kRowParams);
+  int32_t* row_z = reinterpret_cast<int32_t*>(g_lds + kRowParams + BM * 4);
   __syncthreads();                               // every wave is done with the slots
-  if (tid < BM) {
-    const int m = min(m0 + tid, a.M - 1);
-    row_s[tid] = e.s_a[e.s_a_vec ? m : 0];
-    row_z[tid] = e.azp ? e.azp[m] : 0;
+  for (int r = tid; r < BM; r += 64 * kWaves) {
+    const int m = min(m0 + r, a.M - 1);
+    row_s[r] = e.s_a[e.s_a_vec ? m : 0];
+    row_z[r] = e.azp ? e.azp[m] : 0;
   }
-  const int half = lane >> 5, l32 = lane & 31;
-  float col_s[2], col_b[2];
-  int32_t col_adj[2];
+  float col_s[kNT], col_b[kNT];
+  int32_t col_adj[kNT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) {
     const int n = min(n0 + wn + nt * 32 + l32, a.N - 1);
     col_s[nt] = e.s_b[e.s_b_vec ? n : 0];
     col_adj[nt] = e.azp_adj ? e.azp_adj[n] : 0;
@@ -274,22 +316,51 @@ __global__ __launch_bounds__(256) void i8_gemm_kernel(I8Args a) {
   }
   __syncthreads();
   const bool per_token_azp = e.azp != nullptr;
+  auto value = [&](int mt, int nt, int el, int r) -> uint16_t {
+    const int32_t c = acc[mt][nt][el] - (per_token_azp ? row_z[r] * col_adj[nt] : col_adj[nt]);
+    const float v = row_s[r] * (col_s[nt] * (float)c) + col_b[nt];
+    return OUT_BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+  };
+  // acc element el of lane l: row 8*(el/4) + 4*(l/32) + el%4, column l%32 of its 32 x 32 tile
+  const bool full = m0 + BM <= a.M && n0 + BN <= a.N && (a.N & 7) == 0 && e.raw == nullptr;
+  if (full) {
+    // whole tile inside Y: stage the wave's 128 x 64 outputs in LDS (16-byte
+    // pieces of a 128-byte row XOR-swizzled by row, conflict-free both ways)
+    // and store them as 16-byte row pieces, 8 full lines per instruction
+    uint8_t* region = reinterpret_cast<uint8_t*>(g_lds) + wave * kOutWave;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int n = n0 + wn + nt * 32 + l32;
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-      for (int el = 0; el < 16; ++el) {
-        // acc element el of lane l: row 8*(el/4) + 4*(l/32) + el%4, column l%32
-        const int r = wm + mt * 32 + 8 * (el >> 2) + 4 * half + (el & 3);
-        const int m = m0 + r;
-        if (m >= a.M || n >= a.N) continue;
-        const int32_t c = acc[mt][nt][el] - (per_token_azp ? row_z[r] * col_adj[nt] : col_adj[nt]);
-        if (e.raw) e.raw[(size_t)m * a.N + n] = c;
-        const float v = row_s[r] * (col_s[nt] * (float)c) + col_b[nt];
-        static_cast<uint16_t*>(e.out)[(size_t)m * a.N + n] =
-            OUT_BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+        for (int el = 0; el < 16; ++el) {
+          const int rl = mt * 32 + 8 * (el >> 2) + 4 * half + (el & 3);   // row inside the wave tile
+          const int cl = nt * 32 + l32;                                   // column inside the wave tile
+          const uint16_t v = value(mt, nt, el, wm + rl);
+          *reinterpret_cast<uint16_t*>(region + rl * 128 + (((cl >> 3) ^ (rl & 7)) << 4) + (cl & 7) * 2) = v;
+        }
+    uint16_t* out = static_cast<uint16_t*>(e.out);
+#pragma unroll
+    for (int i = 0; i < (kMT * 32) / 8; ++i) {
+      const int rl = (lane >> 3) + 8 * i, piece = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(region + rl * 128 + ((piece ^ (rl & 7)) << 4));
+      *reinterpret_cast<uint4*>(out + (size_t)(m0 + wm + rl) * a.N + n0 + wn + piece * 8) = v;
+    }
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int n = n0 + wn + nt * 32 + l32;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+#pragma unroll
+        for (int el = 0; el < 16; ++el) {
+          const int r = wm + mt * 32 + 8 * (el >> 2) + 4 * half + (el & 3);
+          const int m = m0 + r;
+          if (m >= a.M || n >= a.N) continue;
+          if (e.raw)
+            e.raw[(size_t)m * a.N + n] = acc[mt][nt][el] - (per_token_azp ? row_z[r] * col_adj[nt] : col_adj[nt]);
+          static_cast<uint16_t*>(e.out)[(size_t)m * a.N + n] = value(mt, nt, el, r);
+        }
       }
     }
   }
@@ -301,9 +372,9 @@ hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K,
   I8Args a{A, B, M, N, K, e};
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (e.out_bf16)
-    hipLaunchKernelGGL(i8_gemm_kernel<true>, dim3(tiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(i8_gemm_kernel<true>, dim3(tiles), dim3(64 * kWaves), 0, st, a);
   else
-    hipLaunchKernelGGL(i8_gemm_kernel<false>, dim3(tiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(i8_gemm_kernel<false>, dim3(tiles), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError();
 }
 
