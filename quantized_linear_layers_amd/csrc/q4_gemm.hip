@@ -7,10 +7,11 @@
 // spends the vector ALU on nothing but the dequant and amortizes each
 // dequantized weight over as many tokens as the register file allows:
 //
-//   * a workgroup owns a 256 x 256 tile of Y; each of its 4 waves owns all
-//     256 rows x 64 columns (8 x 2 tiles of v_mfma_f32_32x32x16_{bf16,f16},
-//     256 fp32 accumulators per lane), so every weight a wave dequantizes
-//     feeds 8 MFMAs and no weight is dequantized twice in a workgroup;
+//   * a workgroup owns a 256 x 256 tile of Y; each of its 8 waves (two per
+//     SIMD, so one multiplies while the other waits) owns all 256 rows x 32
+//     columns (8 tiles of v_mfma_f32_32x32x16_{bf16,f16}), so every weight a
+//     wave dequantizes feeds 8 MFMAs and no weight is dequantized twice in a
+//     workgroup;
 //   * K advances in blocks of 64 through a ring of 3 LDS stages filled by
 //     global_load_lds (no register staging), two blocks ahead: the X tile
 //     (shared by the 4 waves; 16-byte pieces XOR-swizzled by row so the MFMA
@@ -41,24 +42,23 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-#ifndef QL_GEMM_WM
-#define QL_GEMM_WM 1
+#ifndef QL_GEMM_NTW
+#define QL_GEMM_NTW 1
 #endif
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kWM = QL_GEMM_WM;                 // waves along M
-constexpr int kWN = 4;                          // waves along N: wave (wm, wn) owns rows
-constexpr int kWaves = kWM * kWN;               //   wm * BM / kWM .. +BM / kWM, columns 64 wn .. +64
-constexpr int kMT = BM / 32 / kWM;              // 32-row MFMA tiles per wave
+constexpr int kMT = BM / 32;                    // 32-row MFMA tiles per wave (every wave spans all rows)
+constexpr int kNTW = QL_GEMM_NTW;               // 32-column MFMA tiles per wave
+constexpr int kWaves = BN / (32 * kNTW);        // wave w owns columns 32 kNTW w .. +32 kNTW
 constexpr int kStages = 3;
 constexpr int kATile = BM * BK * 2;             // X tile of one stage: 256 rows x 128 bytes
-constexpr int kBSlice = 2 * 64 * 16;            // packed weights of a 64-column slice: 2 chunks x 64 x 16 B
-constexpr int kSZSlice = 2 * 256;               // scale words, then zero-point words, of a slice
+constexpr int kBWave = 2 * 32 * kNTW * 16;      // packed weights of one wave: 2 chunks x 32 kNTW columns x 16 B
+constexpr int kSZWave = 2 * 32 * kNTW * 4;      // scale words, then zero-point words, of one wave
 constexpr int kBOff = kATile;
-constexpr int kSZOff = kBOff + kWN * kBSlice;
-constexpr int kStage = kSZOff + kWN * kSZSlice;             // 43008 bytes
+constexpr int kSZOff = kBOff + kWaves * kBWave;
+constexpr int kStage = kSZOff + kWaves * kSZWave;           // 43008 bytes
 constexpr int kAFills = kATile / 1024 / kWaves;             // 1 KB X blocks per wave and stage
-constexpr int kSliceLoads = 2 / kWM;                        // chunk copies (and scale/zero copies) per wave
-constexpr int kLoads = kAFills + 2 * kSliceLoads;           // copies per wave and stage
+constexpr int kLoads = kAFills + 2 * kNTW;                  // copies per wave and stage
+constexpr int kXBuf = kWaves >= 8 ? 1 : 2;                  // X fragment buffers per wave
 
 __shared__ __align__(1024) uint8_t g_lds[kStages * kStage];
 
@@ -217,19 +217,20 @@ __device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
 }
 
 // Per-lane sources and LDS destinations of one wave's copies for a stage.
-// The waves of one 64-column slice share its weight chunks and its scale and
-// zero-point words: with kWM waves per slice, wave wm copies chunk c = wm (or
-// both chunks when kWM = 1) and the scale words (wm = 0) or the zero-point
-// words (wm = 1).
-// Sources are kept as 32-bit byte offsets from the (uniform) base pointers,
-// one register each; every operand is far below 4 GiB.
+// Each wave copies its own weight chunks (kNTW copies of 1 KB: flat index
+// f = 64 d + lane -> chunk f / (32 kNTW), column f % (32 kNTW)) and its
+// scale and zero-point words (kNTW copies of 256 B: f < 32 kNTW -> scale word
+// of column f, else the aligned word holding the zero byte of column
+// f - 32 kNTW).  Sources are kept as 32-bit byte offsets from the (uniform)
+// base pointers, one register each; every operand is below 4 GiB.
 struct FillPlan {
   uint32_t x[kAFills];          // X row of each 1 KB block (+ the lane's logical piece)
   int xdst[kAFills];            // byte offset of the block inside the stage
-  uint32_t w;                   // weight chunk column of lane l (chunk row added per block)
-  uint32_t sz[kSliceLoads];     // scale word of lane l / aligned word holding its zero byte
-  int wdst, szdst;              // byte offsets of the slice's weight and scale/zero areas
-  int c0;                       // first chunk (and scale/zero array) this wave copies
+  uint32_t w[kNTW];             // weight column of each chunk copy (chunk row added per block)
+  int wc[kNTW];                 // chunk (0 or 1) of each chunk copy
+  uint32_t sz[kNTW];            // scale word / aligned zero word of each scale copy
+  bool isz[kNTW];               // the copy reads the zero-point array
+  int wdst, szdst;              // byte offsets of the wave's weight and scale/zero areas
 };
 
 template <int S>
@@ -242,47 +243,50 @@ __device__ inline void fill(const GemmArgs& a, const FillPlan& f, int kb) {
   const uint32_t pr = kb >> 2;                              // pair of groups of this k block
   const uint32_t np = a.Np;
 #pragma unroll
-  for (int i = 0; i < kSliceLoads; ++i) {
-    const int c = f.c0 + i;
-    load_lds16(wb + f.w + (uint32_t)(2 * kb + c) * np * 16, st + f.wdst + c * 1024);
+  for (int d = 0; d < kNTW; ++d)
+    load_lds16(wb + f.w[d] + (uint32_t)(2 * kb + f.wc[d]) * np * 16, st + f.wdst + d * 1024);
+#pragma unroll
+  for (int d = 0; d < kNTW; ++d) {
     // scale rows hold one word per column, zero rows one byte per column
-    const char* szb = c == 0 ? reinterpret_cast<const char*>(a.S) : reinterpret_cast<const char*>(a.Z);
-    load_lds4(szb + f.sz[i] + pr * (c == 0 ? np * 4 : np), st + f.szdst + c * 256);
+    const char* szb = f.isz[d] ? reinterpret_cast<const char*>(a.Z) : reinterpret_cast<const char*>(a.S);
+    load_lds4(szb + f.sz[d] + pr * (f.isz[d] ? np : np * 4), st + f.szdst + d * 256);
   }
 }
 
 template <bool BF16>
 struct Frag {
-  f32x16 acc[kMT][2];
+  f32x16 acc[kMT][kNTW];
 };
 
 // Multiplies stage S (k block kb) into the accumulators.
 //   xrd[j]: LDS address (stage 0) of the lane's X piece for k step j of the
 //           block (j = 2c + s); + 4096 per 32-row tile, + kStage per stage
-//   wrd:    LDS address (stage 0) of the lane's 8-byte word pair of chunk 0
-//   szrd:   LDS address (stage 0) of the lane's scale word of column tile 0
+//   wrd:    LDS address (stage 0) of the lane's 8-byte word pair of chunk 0,
+//           column tile 0; + 32 kNTW * 16 per chunk, + 512 per column tile
+//   szrd:   LDS address (stage 0) of the lane's scale word of column tile 0;
+//           + 128 kNTW for its zero word, + 128 per column tile
 template <bool BF16, int S>
 __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd,
                                int zshift) {
   constexpr int SO = S * kStage;
   const uint32_t wst = wrd + SO, szst = szrd + SO;
-  // packed words (2 chunks x 2 column tiles) and this group's scale / zero
-  u32x2 wv[2][2];
-  uint32_t sv[2], zv[2];
+  // packed words (2 chunks x kNTW column tiles) and this group's scale / zero
+  u32x2 wv[2][kNTW];
+  uint32_t sv[kNTW], zv[kNTW];
   static_for<0, 2>([&](auto C) {
-    static_for<0, 2>([&](auto T) { wv[C][T] = lds_read8<C * 1024 + T * 512>(wst); });
+    static_for<0, kNTW>([&](auto T) { wv[C][T] = lds_read8<C * 32 * kNTW * 16 + T * 512>(wst); });
   });
-  static_for<0, 2>([&](auto T) {
+  static_for<0, kNTW>([&](auto T) {
     sv[T] = lds_read4<T * 128>(szst);
-    zv[T] = lds_read4<256 + T * 128>(szst);
+    zv[T] = lds_read4<128 * kNTW + T * 128>(szst);
   });
-  u32x4 xa[2][kMT];
+  u32x4 xa[kXBuf][kMT];
   static_for<0, kMT>([&](auto MT) { xa[0][MT] = lds_read16<MT * 4096>(xrd[0] + SO); });
   wait_lgkm<0>();                                // words, scales, zeros and step 0's X landed
   const int h = (kb >> 1) & 1;                   // group of the block inside its pair
-  float s[2], nzs[2];
+  float s[kNTW], nzs[kNTW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kNTW; ++t) {
     after_wait(wv[0][t]);
     after_wait(wv[1][t]);
     after_wait(sv[t]);
@@ -293,35 +297,45 @@ __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4],
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) after_wait(xa[0][mt]);
   // B operands of step j: chunk j / 2, word j % 2 of the lane's pair
-  u32x4 b[2][2];
+  u32x4 b[2][kNTW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) b[0][t] = dequant8<BF16>(wv[0][t][0], s[t], nzs[t]);
+  for (int t = 0; t < kNTW; ++t) b[0][t] = dequant8<BF16>(wv[0][t][0], s[t], nzs[t]);
   static_for<0, 4>([&](auto J) {
     constexpr int j = J;
-    constexpr int cur = j & 1;
+    constexpr int cur = kXBuf == 2 ? (j & 1) : 0;
+    if constexpr (kXBuf == 1 && j > 0) {
+      // one X buffer (two waves per SIMD hide the read latency)
+      static_for<0, kMT>([&](auto MT) { xa[0][MT] = lds_read16<MT * 4096>(xrd[j] + SO); });
+      wait_lgkm<0>();
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) after_wait(xa[0][mt]);
+    }
     // X of step j + 1 in flight while step j multiplies
-    if constexpr (j < 3)
+    if constexpr (kXBuf == 2 && j < 3)
       static_for<0, kMT>([&](auto MT) { xa[cur ^ 1][MT] = lds_read16<MT * 4096>(xrd[j + 1] + SO); });
-    // one scheduling region: the 16 MFMAs of step j interleaved with the
-    // dequant of step j + 1 (vector ALU work in the shadow of the matrix unit)
+    // one scheduling region: the MFMAs of step j interleaved with the dequant
+    // of step j + 1 (vector ALU work in the shadow of the matrix unit)
     if constexpr (j < 3) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) b[cur ^ 1][t] = dequant8<BF16>(wv[(j + 1) >> 1][t][(j + 1) & 1], s[t], nzs[t]);
+      for (int t = 0; t < kNTW; ++t)
+        b[(j & 1) ^ 1][t] = dequant8<BF16>(wv[(j + 1) >> 1][t][(j + 1) & 1], s[t], nzs[t]);
     }
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) fr.acc[mt][t] = mfma<BF16>(xa[cur][mt], b[cur][t], fr.acc[mt][t]);
+      for (int t = 0; t < kNTW; ++t) fr.acc[mt][t] = mfma<BF16>(xa[cur][mt], b[j & 1][t], fr.acc[mt][t]);
     if constexpr (j < 3) {
 #if defined(__HIP_DEVICE_COMPILE__)
-      static_for<0, 2 * kMT>([&](auto) {
+      static_for<0, kMT * kNTW>([&](auto) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
       });
 #endif
-      wait_lgkm<0>();
+      if constexpr (kXBuf == 2) {
+        wait_lgkm<0>();
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) after_wait(xa[cur ^ 1][mt]);
+        for (int mt = 0; mt < kMT; ++mt) after_wait(xa[cur ^ 1][mt]);
+      }
     }
   });
 }
@@ -344,19 +358,16 @@ __global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
   int mtile, ntile;
   tile_of(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, mtile, ntile);
   const int m0 = mtile * BM, n0 = ntile * BN;
-  const int wm = wave / kWN, wn = wave % kWN;
-  const int nw0 = n0 + 64 * wn;                   // first column of this wave
-  const int mw0 = m0 + wm * (BM / kWM);           // first row of this wave
+  const int nw0 = n0 + 32 * kNTW * wave;         // first column of this wave
   const int nkb = a.K / BK;
-  const size_t np = a.Np;
 
   // ---- copy plan.  X: the stage's 32 blocks of 1 KB (8 rows x 128 bytes),
   // kAFills per wave; lane l writes row 8b + l / 8, stored piece l % 8,
   // which holds logical piece (l % 8) ^ ((row >> 1) & 7): the 16 rows one
   // operand read serves at a time then touch 16 different 16-byte bank groups
-  // (two consecutive 128-byte rows span the 64 banks once).  Rows past M repeat row
-  // M - 1 and columns past Np repeat column Np - 1 (valid loads whose results
-  // only reach outputs that are never stored).
+  // (two consecutive 128-byte rows span the 64 banks once).  Rows past M
+  // repeat row M - 1 and columns past Np repeat column Np - 1 (valid loads
+  // whose results only reach outputs that are never stored).
   FillPlan f;
 #pragma unroll
   for (int i = 0; i < kAFills; ++i) {
@@ -366,13 +377,19 @@ __global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
     f.x[i] = ((uint32_t)m * a.K + ((lane & 7) ^ ((r >> 1) & 7)) * 8) * 2;
     f.xdst[i] = blk * 1024;
   }
-  const int ncol = min(nw0 + lane, a.Np - 1);
-  f.w = (uint32_t)ncol * 16;
-  f.c0 = (kWM == 1) ? 0 : wm;
 #pragma unroll
-  for (int i = 0; i < kSliceLoads; ++i) f.sz[i] = (f.c0 + i) == 0 ? (uint32_t)ncol * 4 : (uint32_t)(ncol & ~3);
-  f.wdst = kBOff + wn * kBSlice;
-  f.szdst = kSZOff + wn * kSZSlice;
+  for (int d = 0; d < kNTW; ++d) {
+    const int fl = 64 * d + lane;
+    const int cw = fl % (32 * kNTW);                          // column of the chunk copy
+    f.w[d] = (uint32_t)min(nw0 + cw, a.Np - 1) * 16;
+    f.wc[d] = fl / (32 * kNTW);
+    const int cs = fl % (32 * kNTW);                          // column of the scale / zero copy
+    const int ncs = min(nw0 + cs, a.Np - 1);
+    f.isz[d] = fl >= 32 * kNTW;
+    f.sz[d] = f.isz[d] ? (uint32_t)(ncs & ~3) : (uint32_t)ncs * 4;
+  }
+  f.wdst = kBOff + wave * kBWave;
+  f.szdst = kSZOff + wave * kSZWave;
 
   // ---- read addresses (stage 0)
   typedef __attribute__((address_space(3))) uint8_t* lds_ptr;
@@ -383,17 +400,17 @@ __global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
   for (int j = 0; j < 4; ++j) {
     // step j = 2c + s takes k 32c + 8 * (2 * half + s) .. +8: logical piece 4c + 2*half + s
     const int p = 4 * (j >> 1) + 2 * half + (j & 1);
-    xrd[j] = base + (wm * (BM / kWM) + l32) * 128 + ((p ^ ((l32 >> 1) & 7)) * 16);
+    xrd[j] = base + l32 * 128 + ((p ^ ((l32 >> 1) & 7)) * 16);
   }
-  const uint32_t wrd = base + f.wdst + l32 * 16 + half * 8;      // + 512 per column tile, + 1024 per chunk
-  const uint32_t szrd = base + f.szdst + l32 * 4;                // + 128 per column tile
+  const uint32_t wrd = base + f.wdst + l32 * 16 + half * 8;      // + 512 per column tile, + 32 kNTW * 16 per chunk
+  const uint32_t szrd = base + f.szdst + l32 * 4;                // + 128 per column tile, + 128 kNTW for zeros
   const int zshift = 8 * (l32 & 3);                              // the column's byte inside its word
 
   Frag<BF16> fr;
 #pragma unroll
   for (int i = 0; i < kMT; ++i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < kNTW; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) fr.acc[i][t][e] = 0.0f;
 
@@ -415,14 +432,14 @@ __global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
 
   // ---- store: acc element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kNTW; ++t) {
     const int n = nw0 + 32 * t + l32;
     if (n >= a.N) continue;
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = mw0 + 32 * mt + 8 * (e >> 2) + 4 * half + (e & 3);
+        const int m = m0 + 32 * mt + 8 * (e >> 2) + 4 * half + (e & 3);
         if (m < a.M) {
           const float v = fr.acc[mt][t][e];
           a.Y[(size_t)m * a.N + n] =
