@@ -205,3 +205,24 @@ def test_exact_fraction_w8a8_epilogue():
             y = Fraction(dq) * Fraction(g["x_absmax"][m]).limit_denominator(100) / 127 \
                 * Fraction(g["w_absmax"][n]).limit_denominator(100) / 127
             assert round(float(y), 4) == g["Y_printed"][m][n]
+
+
+# ---------------------------------------------------------------- FP8 E4M3
+
+def test_lq_fp8_e4m3_examples():
+    from oracle import fp8
+    g = golden("lq_fp8_e4m3.json")
+    c03, c500, c04 = g["cases"]
+    code = int(fp8.e4m3_encode(np.float32(c03["x"])))
+    assert code == int(c03["bits"], 2)
+    v = float(fp8.e4m3_decode(code))
+    assert v == c03["value"]
+    assert round(abs(v - c03["x"]) / c03["x"] * 100, 1) == c03["rel_err_percent"]
+    assert float(fp8.e4m3_decode(fp8.e4m3_encode(c500["x"]))) == c500["value"]
+    assert float(fp8.e4m3_decode(fp8.e4m3_encode(np.float32(c04["x"])))) == c04["value"]
+    # format limits
+    vals = fp8.E4M3_VALUES
+    assert np.nanmax(vals) == g["max_finite"] == 1.75 * 2 ** 8
+    nan_codes = [c for c in range(256) if np.isnan(vals[c])]
+    assert nan_codes == [0x7F, 0xFF]                    # S.1111.111 only, no infinities
+    assert np.nanmin(np.abs(vals[vals != 0])) == 2.0 ** -9

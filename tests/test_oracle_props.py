@@ -265,3 +265,69 @@ def test_w8a8_end_to_end_close_to_float():
 def test_corrected_accumulator_needs_adj():
     with pytest.raises(ValueError):
         w8.corrected_accumulator(np.zeros((1, 1), np.int64), np.zeros(1, np.int32), None)
+
+
+# ---------------------------------------------------------------- FP8 E4M3
+
+def test_fp8_all_codes_round_trip_and_order():
+    from oracle import fp8
+    codes = np.arange(256, dtype=np.uint8)
+    v = fp8.e4m3_decode(codes)
+    ok = ~np.isnan(v)
+    assert np.array_equal(fp8.e4m3_encode(v[ok]), codes[ok])
+    pos = np.sort(v[(codes < 0x80) & ok])
+    assert np.all(np.diff(pos) > 0) and pos[0] == 0.0
+    assert np.isnan(fp8.e4m3_decode(fp8.e4m3_encode(np.nan)))
+
+
+def test_fp8_rounding_ties_even_and_saturation():
+    from oracle import fp8
+    vals = np.sort(fp8.E4M3_VALUES[:0x7F])               # non-negative finite, ascending
+    for lo, hi in zip(vals[:-1], vals[1:]):
+        mid = (lo + hi) / 2
+        c_lo, c_hi = int(fp8.e4m3_encode(lo)), int(fp8.e4m3_encode(hi))
+        c_mid = int(fp8.e4m3_encode(mid))
+        assert c_mid == (c_lo if c_lo % 2 == 0 else c_hi)   # ties go to the even mantissa
+        assert int(fp8.e4m3_encode(np.nextafter(mid, 0))) == c_lo
+        assert int(fp8.e4m3_encode(np.nextafter(mid, 1e9))) == c_hi
+    for x in (448.0, 449.0, 464.0, 1e6, np.float32(3e38)):
+        assert float(fp8.e4m3_decode(fp8.e4m3_encode(x))) == 448.0
+        assert float(fp8.e4m3_decode(fp8.e4m3_encode(-x))) == -448.0
+    assert int(fp8.e4m3_encode(-0.0)) == 0x80 and int(fp8.e4m3_encode(2.0 ** -11)) == 0
+
+
+def test_fp8_per_token_quant_invariants():
+    from oracle import fp8
+    r = np.random.default_rng(5)
+    X = (r.standard_normal((6, 256)) * np.array([1e-3, 0.1, 1, 10, 300, 1e4])[:, None]).astype(np.float32)
+    X[2, :] = 0.0
+    q, s = fp8.quant_per_token_fp8(X)
+    assert q.dtype == np.uint8 and s.dtype == np.float32
+    v = fp8.e4m3_decode(q)
+    assert np.all(np.abs(v) <= 448.0)
+    for m in (0, 1, 3, 4, 5):
+        assert np.max(np.abs(v[m])) == 448.0                 # the row absmax maps to the largest code
+        # relative error of each element within half an E4M3 ulp (2**-4) or the subnormal step
+        err = np.abs(v[m] * np.float64(s[m]) - X[m])
+        bound = np.maximum(np.abs(X[m]) * 2.0 ** -4, 2.0 ** -10 * np.float64(s[m]))
+        assert np.all(err <= bound * (1 + 1e-6))
+    assert np.all(v[2] == 0.0)
+
+
+def test_fp8_gemm_exact_against_fractions():
+    from fractions import Fraction
+    from oracle import fp8
+    r = np.random.default_rng(9)
+    A = r.integers(0, 256, (3, 40), dtype=np.uint8)
+    B = r.integers(0, 256, (4, 40), dtype=np.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x38                             # no NaN codes
+    B[(B & 0x7F) == 0x7F] = 0xB8
+    D = fp8.fp8_gemm(A, B)
+    va, vb = fp8.E4M3_VALUES[A], fp8.E4M3_VALUES[B]
+    for m in range(3):
+        for n in range(4):
+            exact = sum(Fraction(float(x)) * Fraction(float(y)) for x, y in zip(va[m], vb[n]))
+            assert Fraction(float(D[m, n])) == exact
+    out = fp8.fp8_linear(A, B, np.float32([0.5, 2, 4]), np.float32([1, 0.25, 3, 8]), np.float64([1, 2, 3, 4]))
+    assert np.allclose(out, np.float64([0.5, 2, 4])[:, None] * np.float64([1, 0.25, 3, 8])[None] * D + [1, 2, 3, 4],
+                       rtol=0, atol=0)
