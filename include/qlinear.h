@@ -9,7 +9,9 @@
  *          per group of 128 input channels; 16-bit activations; fp32
  *          accumulation; x_fp ≈ s · (x_int − z).
  *   W8A8   int8 × int8 products accumulated in int32, then a fused epilogue
- *          out = s_a · s_b · (Dq − azp · azp_adj) + bias before the single store.
+ *          out = s_a · s_b · (Dq − azp · azp_adj) + bias before the single store;
+ *          or FP8 (E4M3) × FP8 products accumulated in fp32 with the scales
+ *          applied in the same epilogue.
  *
  * Sources (page title, then the page's own section heading):
  *   [QK] "第 9 章 量化 Kernel：INT8 / FP8 / INT4" (Quantization kernels:
@@ -255,6 +257,58 @@ int i8_gemm_scaled(const int8_t* Aq, const int8_t* Bq, int M, int N, int K,
                    const float* s_a, int s_a_len, const float* s_b, int s_b_len,
                    const int32_t* azp, const int32_t* azp_adj, const void* bias,
                    void* out, int out_dtype, int32_t* raw_out, void* stream);
+
+/* =========================================================================
+ * W8A8 with FP8 (E4M3) codes
+ * ========================================================================= */
+
+/*
+ * FP8 E4M3 as in [LQ] "浮点：指数管范围，尾数管精度": the "FN" variant (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits), no infinities, only
+ * S.1111.111 is NaN, largest finite value 1.75 · 2^8 = 448; conversion
+ * rounds to nearest even and saturates (the page converts 500 to 448).
+ * The W8A8 route of [LQ] "W4A4、FP8 与块缩放格式": x / s is converted to
+ * E4M3 instead of being rounded to an int8 code, the FP8 products are
+ * accumulated in fp32 and the epilogue multiplies the two scales; scales are
+ * per token for activations and per channel for weights.  Scale: the absmax
+ * maps to the largest code, s = max(absmax, 1e-5) / 448, in IEEE fp32.
+ */
+
+/*
+ * f8_quant_weight_host — per-output-channel FP8 weights (host).
+ * s_b[n] = max(max_k |W[n][k]|, 1e-5) / 448, Bq[n][k] = e4m3(W[n][k] / s_b[n]).
+ * W [N][K] fp32; Bq [N][K] E4M3 codes out; s_b [N] fp32 out.
+ * Errors: QL_ERR_NULL; QL_ERR_SHAPE unless N > 0, K > 0; QL_ERR_RANGE on NaN/inf.
+ */
+int f8_quant_weight_host(const float* W, int N, int K, uint8_t* Bq, float* s_b);
+
+/*
+ * f8_quant_per_token — dynamic per-token FP8 activation quantization (device).
+ * s_a[m] = max(max_k |X[m][k]|, 1e-5) / 448, Aq[m][k] = e4m3(X[m][k] / s_a[m])
+ * (correctly rounded fp32 division, then one E4M3 rounding: bit-exact with
+ * any IEEE implementation of the same steps).
+ * X [M][K] fp16/bf16; Aq [M][K] E4M3 codes out; s_a [M] fp32 out.
+ * M == 0 is a no-op.
+ * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M >= 0, K > 0 and
+ *         K % 8 == 0; QL_ERR_ALIGN; QL_ERR_HIP.
+ */
+int f8_quant_per_token(const void* X, int x_dtype, int M, int K, uint8_t* Aq, float* s_a, void* stream);
+
+/*
+ * f8_gemm_scaled — FP8 GEMM with fp32 accumulation and the fused epilogue
+ * (device).
+ * out[m][n] = s_a[m] · (s_b[n] · Σ_k e4m3(Aq[m][k]) · e4m3(Bq[n][k])) + bias[n],
+ * one round-to-nearest-even to out_dtype at the single store.
+ * Aq [M][K] and Bq [N][K] E4M3 codes (NaN codes are not allowed); s_a:
+ * s_a_len 1 or M; s_b: s_b_len 1 or N; bias [N] of out_dtype or NULL;
+ * out [M][N] of out_dtype.  M == 0 or N == 0 is a no-op.
+ * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M, N >= 0, K > 0,
+ *         K % 16 == 0, s_a_len in {1, M}, s_b_len in {1, N}; QL_ERR_ALIGN;
+ *         QL_ERR_HIP.
+ */
+int f8_gemm_scaled(const uint8_t* Aq, const uint8_t* Bq, int M, int N, int K,
+                   const float* s_a, int s_a_len, const float* s_b, int s_b_len,
+                   const void* bias, void* out, int out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -47,6 +47,9 @@ def lib():
             "i8_azp_adj": (I, [P, I, I, P]),
             "i8_quant_per_token": (I, [P, I, I, I, P, P, P, P]),
             "i8_gemm_scaled": (I, [P, P, I, I, I, P, I, P, I, P, P, P, P, I, P, P]),
+            "f8_quant_weight_host": (I, [P, I, I, P, P]),
+            "f8_quant_per_token": (I, [P, I, I, I, P, P, P]),
+            "f8_gemm_scaled": (I, [P, P, I, I, I, P, I, P, I, P, P, I, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -228,3 +231,46 @@ def i8_gemm_scaled(Aq, Bq, s_a, s_b, azp=None, azp_adj=None, bias=None, out_dtyp
                                 _ptr(azp), _ptr(azp_adj), _ptr(bias), _ptr(out), _dtype_code(out_dtype),
                                 _ptr(rawt), _stream(Aq, stream)), "i8_gemm_scaled")
     return (out, rawt) if raw else out
+
+
+# ---------------------------------------------------------------- W8A8 with FP8 (E4M3) codes
+
+def f8_quant_weight_host(W):
+    """CPU fp32 [N, K] -> (Bq uint8 E4M3 codes [N, K], s_b fp32 [N])."""
+    W = _host(W, torch.float32)
+    N, K = W.shape
+    Bq = torch.empty((N, K), dtype=torch.uint8)
+    s_b = torch.empty(N, dtype=torch.float32)
+    _check(lib().f8_quant_weight_host(_ptr(W), N, K, _ptr(Bq), _ptr(s_b)), "f8_quant_weight_host")
+    return Bq, s_b
+
+
+def f8_quant_per_token(X, stream=None):
+    """X fp16/bf16 [M, K] on the device -> (Aq uint8 E4M3 codes [M, K], s_a fp32 [M])."""
+    X = _dev(X, name="X")
+    M, K = X.shape
+    Aq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    s_a = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(lib().f8_quant_per_token(_ptr(X), _dtype_code(X.dtype), M, K, _ptr(Aq), _ptr(s_a), _stream(X, stream)),
+           "f8_quant_per_token")
+    return Aq, s_a
+
+
+def f8_gemm_scaled(Aq, Bq, s_a, s_b, bias=None, out_dtype=torch.float16, out=None, stream=None):
+    """out[M, N] = s_a * s_b * (e4m3(Aq)·e4m3(Bq)ᵀ) + bias, on the device."""
+    _dev(Aq, torch.uint8, "Aq")
+    _dev(Bq, torch.uint8, "Bq")
+    _dev(s_a, torch.float32, "s_a")
+    _dev(s_b, torch.float32, "s_b")
+    if bias is not None:
+        _dev(bias, out_dtype, "bias")
+    M, K = Aq.shape
+    N = Bq.shape[0]
+    if Bq.shape[1] != K:
+        raise QLError("Aq and Bq disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=Aq.device)
+    _check(lib().f8_gemm_scaled(_ptr(Aq), _ptr(Bq), M, N, K, _ptr(s_a), s_a.numel(), _ptr(s_b), s_b.numel(),
+                                _ptr(bias), _ptr(out), _dtype_code(out_dtype), _stream(Aq, stream)),
+           "f8_gemm_scaled")
+    return out

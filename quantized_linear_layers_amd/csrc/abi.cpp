@@ -106,4 +106,34 @@ int i8_gemm_scaled(const int8_t* Aq, const int8_t* Bq, int M, int N, int K, cons
   return hip_status("i8_gemm_scaled", ql::launch_i8_gemm(Aq, Bq, M, N, K, e, static_cast<hipStream_t>(stream)));
 }
 
+int f8_quant_per_token(const void* X, int x_dtype, int M, int K, uint8_t* Aq, float* s_a, void* stream) {
+  if (M < 0 || K <= 0 || K % 8)
+    return ql::set_error(QL_ERR_SHAPE, "f8_quant_per_token: need M >= 0, K > 0, K %% 8 == 0 (got %d, %d)", M, K);
+  if (!valid_dtype(x_dtype)) return ql::set_error(QL_ERR_DTYPE, "f8_quant_per_token: x_dtype=%d", x_dtype);
+  if (M == 0) return QL_OK;
+  if (!X || !Aq || !s_a) return ql::set_error(QL_ERR_NULL, "f8_quant_per_token: NULL X, Aq or s_a");
+  if (!aligned16(X) || !aligned16(Aq) || !aligned16(s_a))
+    return ql::set_error(QL_ERR_ALIGN, "f8_quant_per_token: pointers must be 16-byte aligned");
+  return hip_status("f8_quant_per_token",
+                    ql::launch_f8_quant(X, x_dtype == QL_BF16, M, K, Aq, s_a, static_cast<hipStream_t>(stream)));
+}
+
+int f8_gemm_scaled(const uint8_t* Aq, const uint8_t* Bq, int M, int N, int K, const float* s_a, int s_a_len,
+                   const float* s_b, int s_b_len, const void* bias, void* out, int out_dtype, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 16)
+    return ql::set_error(QL_ERR_SHAPE, "f8_gemm_scaled: need M, N >= 0, K > 0, K %% 16 == 0 (got %d, %d, %d)", M, N, K);
+  if (!valid_dtype(out_dtype)) return ql::set_error(QL_ERR_DTYPE, "f8_gemm_scaled: out_dtype=%d", out_dtype);
+  if (M == 0 || N == 0) return QL_OK;
+  if (s_a_len != 1 && s_a_len != M)
+    return ql::set_error(QL_ERR_SHAPE, "f8_gemm_scaled: s_a_len=%d must be 1 or M=%d", s_a_len, M);
+  if (s_b_len != 1 && s_b_len != N)
+    return ql::set_error(QL_ERR_SHAPE, "f8_gemm_scaled: s_b_len=%d must be 1 or N=%d", s_b_len, N);
+  if (!Aq || !Bq || !s_a || !s_b || !out) return ql::set_error(QL_ERR_NULL, "f8_gemm_scaled: NULL operand");
+  const void* ptrs[] = {Aq, Bq, s_a, s_b, bias, out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return ql::set_error(QL_ERR_ALIGN, "f8_gemm_scaled: pointers must be 16-byte aligned");
+  ql::I8Epi e{s_a, s_a_len != 1, s_b, s_b_len != 1, nullptr, nullptr, bias, out, out_dtype == QL_BF16, nullptr};
+  return hip_status("f8_gemm_scaled", ql::launch_f8_gemm(Aq, Bq, M, N, K, e, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

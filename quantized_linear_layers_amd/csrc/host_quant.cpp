@@ -208,6 +208,26 @@ int i8_quant_weight_host(const float* W, int N, int K, int8_t* Bq, float* s_b) {
   return QL_OK;
 }
 
+int f8_quant_weight_host(const float* W, int N, int K, uint8_t* Bq, float* s_b) {
+  if (!W || !Bq || !s_b) return ql::set_error(QL_ERR_NULL, "f8_quant_weight_host: NULL pointer");
+  if (N <= 0 || K <= 0) return ql::set_error(QL_ERR_SHAPE, "f8_quant_weight_host: N=%d K=%d must be > 0", N, K);
+  for (int n = 0; n < N; ++n) {
+    const float* w = W + (size_t)n * K;
+    float amax = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const float v = w[k];
+      if (!(v == v) || isinf(v))
+        return ql::set_error(QL_ERR_RANGE, "f8_quant_weight_host: W[%d][%d] is not finite", n, k);
+      amax = std::max(amax, fabsf(v));
+    }
+    if (amax < 1e-5f) amax = 1e-5f;
+    const float s = amax / 448.0f;
+    s_b[n] = s;
+    for (int k = 0; k < K; ++k) Bq[(size_t)n * K + k] = (uint8_t)ql::e4m3_code(w[k] / s);
+  }
+  return QL_OK;
+}
+
 int i8_azp_adj(const int8_t* Bq, int N, int K, int32_t* azp_adj) {
   if (!Bq || !azp_adj) return ql::set_error(QL_ERR_NULL, "i8_azp_adj: NULL pointer");
   if (N <= 0 || K <= 0) return ql::set_error(QL_ERR_SHAPE, "i8_azp_adj: N=%d K=%d must be > 0", N, K);

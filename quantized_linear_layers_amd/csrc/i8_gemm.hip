@@ -21,13 +21,21 @@
 // fall on 16 different 16-byte bank groups.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ql_internal.h"
 
 namespace ql {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// accumulators: int32 for int8 operands, fp32 for FP8 (E4M3) operands
+template <bool FP8>
+using Acc = std::conditional_t<FP8, f32x16, i32x16>;
 
 #ifndef QL_I8_WAVES
 #define QL_I8_WAVES 8
@@ -148,10 +156,53 @@ __device__ inline void after_wait(i32x4& v) {
 // never stored.
 //   ard[ks], brd[ks]: LDS addresses (slot 0, tile 0) of the lane's A and B
 //   fragments of k step ks; + 32 * BK per 32-row tile, + kSlot per slot
-template <int S>
-__device__ inline void mma_block(i32x16 (&acc)[kMT][kNT], const uint32_t (&ard)[2], const uint32_t (&brd)[2],
+// The byte of K a lane's fragment register holds is the same for A and B
+// (both are read with the same piece pattern), so the products pair up
+// whatever order the matrix unit sums them in.
+//   int8: two 32-byte k steps; lane l supplies bytes 16 * (l / 32) .. +16 of
+//         each (piece 2 ks + l / 32)
+//   FP8:  one 64-byte k step of v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3,
+//         fp32 accumulation); lane l supplies bytes 32 * (l / 32) .. +32
+//         (pieces 2 (l / 32) + j, j = 0, 1)
+__device__ inline int frag_piece(bool fp8, int j, int half) { return fp8 ? 2 * half + j : 2 * j + half; }
+
+template <int S, bool FP8>
+__device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard)[2], const uint32_t (&brd)[2],
                                  int half, int kvalid) {
-  static_assert(BK == 64, "two k steps per block");
+  static_assert(BK == 64, "two 16-byte pieces per lane and block");
+  if constexpr (FP8) {
+    i32x4 af[2][kMT], bf[2][kNT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int t = 0; t < kMT; ++t) af[j][t] = lds_read16(ard[j] + S * kSlot + t * 32 * BK);
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) bf[j][t] = lds_read16(brd[j] + S * kSlot + t * 32 * BK);
+    }
+    lds_wait<0>();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      // pieces past kvalid (a ragged last block): zero the A side
+      const bool live = frag_piece(true, j, half) * 16 < kvalid;
+#pragma unroll
+      for (int t = 0; t < kMT; ++t) {
+        after_wait(af[j][t]);
+        af[j][t] = live ? af[j][t] : i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) after_wait(bf[j][t]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const i32x8 a8 = __builtin_shufflevector(af[0][mt], af[1][mt], 0, 1, 2, 3, 4, 5, 6, 7);
+        const i32x8 b8 = __builtin_shufflevector(bf[0][nt], bf[1][nt], 0, 1, 2, 3, 4, 5, 6, 7);
+        // format codes 0, 0: both operands FP8 E4M3; no block scales
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[mt][nt], 0, 0, 0, 0, 0, 0);
+      }
+    return;
+  } else {
   // operand layout of the 32x32x32 int8 MFMA: lane l supplies row/column l%32,
   // bytes 16 * (l / 32) .. +16 of the 32-byte k step.  Both k steps'
   // fragments are read at once; the second step's reads land while the first
@@ -185,13 +236,14 @@ __device__ inline void mma_block(i32x16 (&acc)[kMT][kNT], const uint32_t (&ard)[
       for (int nt = 0; nt < kNT; ++nt)
         acc[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mt], bf[ks][nt], acc[mt][nt], 0, 0, 0);
   }
+  }
 }
 
 // one k-block: wait for slot S, barrier, refill the slot freed by the previous
 // block with block kb + kStages - 1 (clamped to the last block near the end, so
 // that every wave always has the same number of loads in flight), multiply slot S
-template <int S>
-__device__ inline void kstep(const I8Args& a, const FillPlan& f, i32x16 (&acc)[kMT][kNT], int kb, int nkb,
+template <int S, bool FP8>
+__device__ inline void kstep(const I8Args& a, const FillPlan& f, Acc<FP8> (&acc)[kMT][kNT], int kb, int nkb,
                              const uint32_t (&ard)[2], const uint32_t (&brd)[2], int half) {
   // this wave's loads of block kb are done once at most (kStages - 2) blocks
   // of its loads remain in flight
@@ -200,17 +252,17 @@ __device__ inline void kstep(const I8Args& a, const FillPlan& f, i32x16 (&acc)[k
                                                  // and every wave finished block kb - 1
   constexpr int F = (S + kStages - 1) % kStages;
   fill<F>(f, min(kb + kStages - 1, nkb - 1), a.K);
-  mma_block<S>(acc, ard, brd, half, a.K - kb * BK);
+  mma_block<S, FP8>(acc, ard, brd, half, a.K - kb * BK);
 }
 
 // the last (nkb mod kStages) blocks, slots 0, 1, ... in order
-template <int S>
-__device__ inline void kstep_tail(const I8Args& a, const FillPlan& f, i32x16 (&acc)[kMT][kNT], int kb, int nkb,
+template <int S, bool FP8>
+__device__ inline void kstep_tail(const I8Args& a, const FillPlan& f, Acc<FP8> (&acc)[kMT][kNT], int kb, int nkb,
                                   const uint32_t (&ard)[2], const uint32_t (&brd)[2], int half) {
   if constexpr (S < kStages - 1) {
     if (kb < nkb) {
-      kstep<S>(a, f, acc, kb, nkb, ard, brd, half);
-      kstep_tail<S + 1>(a, f, acc, kb + 1, nkb, ard, brd, half);
+      kstep<S, FP8>(a, f, acc, kb, nkb, ard, brd, half);
+      kstep_tail<S + 1, FP8>(a, f, acc, kb + 1, nkb, ard, brd, half);
     }
   }
 }
@@ -230,7 +282,7 @@ __device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
   nt = (t % gsize) / gm;
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool FP8>
 __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -242,7 +294,7 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
   const int nkb = (a.K + BK - 1) / BK;
   const int half = lane >> 5, l32 = lane & 31;
 
-  i32x16 acc[kMT][kNT];
+  Acc<FP8> acc[kMT][kNT];
 #pragma unroll
   for (int i = 0; i < kMT; ++i)
 #pragma unroll
@@ -257,8 +309,8 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
   uint32_t ard[2], brd[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    ard[ks] = base + swz(wm + l32, ks * 2 + half);
-    brd[ks] = base + kASlot + swz(wn + l32, ks * 2 + half);
+    ard[ks] = base + swz(wm + l32, frag_piece(FP8, ks, half));
+    brd[ks] = base + kASlot + swz(wn + l32, frag_piece(FP8, ks, half));
   }
 
   // prologue: blocks 0 .. kStages - 2 in flight (clamped to the last block)
@@ -272,14 +324,14 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
 
   int kb = 0;
   for (; kb + kStages <= nkb; kb += kStages) {
-    kstep<0>(a, f, acc, kb, nkb, ard, brd, half);
-    kstep<1>(a, f, acc, kb + 1, nkb, ard, brd, half);
-    kstep<2>(a, f, acc, kb + 2, nkb, ard, brd, half);
-    kstep<3>(a, f, acc, kb + 3, nkb, ard, brd, half);
-    kstep<4>(a, f, acc, kb + 4, nkb, ard, brd, half);
-    kstep<5>(a, f, acc, kb + 5, nkb, ard, brd, half);
+    kstep<0, FP8>(a, f, acc, kb, nkb, ard, brd, half);
+    kstep<1, FP8>(a, f, acc, kb + 1, nkb, ard, brd, half);
+    kstep<2, FP8>(a, f, acc, kb + 2, nkb, ard, brd, half);
+    kstep<3, FP8>(a, f, acc, kb + 3, nkb, ard, brd, half);
+    kstep<4, FP8>(a, f, acc, kb + 4, nkb, ard, brd, half);
+    kstep<5, FP8>(a, f, acc, kb + 5, nkb, ard, brd, half);
   }
-  kstep_tail<0>(a, f, acc, kb, nkb, ard, brd, half);
+  kstep_tail<0, FP8>(a, f, acc, kb, nkb, ard, brd, half);
   wait_vm<0>();                                  // no load may still target LDS at exit
 
   // ---- fused epilogue: C = Dq - azp*azp_adj (int32), out = s_a * (s_b * C) + bias.
@@ -317,8 +369,12 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
   __syncthreads();
   const bool per_token_azp = e.azp != nullptr;
   auto value = [&](int mt, int nt, int el, int r) -> uint16_t {
-    const int32_t c = acc[mt][nt][el] - (per_token_azp ? row_z[r] * col_adj[nt] : col_adj[nt]);
-    const float v = row_s[r] * (col_s[nt] * (float)c) + col_b[nt];
+    float c;
+    if constexpr (FP8)
+      c = acc[mt][nt][el];
+    else
+      c = (float)(acc[mt][nt][el] - (per_token_azp ? row_z[r] * col_adj[nt] : col_adj[nt]));
+    const float v = row_s[r] * (col_s[nt] * c) + col_b[nt];
     return OUT_BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
   };
   // acc element el of lane l: row 8*(el/4) + 4*(l/32) + el%4, column l%32 of its 32 x 32 tile
@@ -357,8 +413,9 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
           const int r = wm + mt * 32 + 8 * (el >> 2) + 4 * half + (el & 3);
           const int m = m0 + r;
           if (m >= a.M || n >= a.N) continue;
-          if (e.raw)
-            e.raw[(size_t)m * a.N + n] = acc[mt][nt][el] - (per_token_azp ? row_z[r] * col_adj[nt] : col_adj[nt]);
+          if constexpr (!FP8)
+            if (e.raw)
+              e.raw[(size_t)m * a.N + n] = acc[mt][nt][el] - (per_token_azp ? row_z[r] * col_adj[nt] : col_adj[nt]);
           static_cast<uint16_t*>(e.out)[(size_t)m * a.N + n] = value(mt, nt, el, r);
         }
       }
@@ -372,9 +429,22 @@ hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K,
   I8Args a{A, B, M, N, K, e};
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (e.out_bf16)
-    hipLaunchKernelGGL(i8_gemm_kernel<true>, dim3(tiles), dim3(64 * kWaves), 0, st, a);
+    hipLaunchKernelGGL((i8_gemm_kernel<true, false>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
   else
-    hipLaunchKernelGGL(i8_gemm_kernel<false>, dim3(tiles), dim3(64 * kWaves), 0, st, a);
+    hipLaunchKernelGGL((i8_gemm_kernel<false, false>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_f8_gemm(const uint8_t* A, const uint8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
+  I8Args a{reinterpret_cast<const int8_t*>(A), reinterpret_cast<const int8_t*>(B), M, N, K, e};
+  a.e.azp = nullptr;
+  a.e.azp_adj = nullptr;
+  a.e.raw = nullptr;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (e.out_bf16)
+    hipLaunchKernelGGL((i8_gemm_kernel<true, true>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((i8_gemm_kernel<false, true>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-// Dynamic per-token int8 activation quantization: one workgroup per row.
+// Dynamic per-token int8 (and FP8 E4M3) activation quantization: one
+// workgroup per row.
 //
 // The row's range is found with one reduction ([LQ] "校准：静态与动态":
 // per-token absmax/range at run time costs one extra reduction), then the
@@ -24,7 +25,9 @@ __device__ inline float half_hi(uint32_t v, bool bf16) {
   return bf16 ? __builtin_bit_cast(float, v & 0xFFFF0000u) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
-template <bool BF16, bool ASYM>
+// FP8: symmetric, s = max(absmax, 1e-5) / 448 and the code is the E4M3
+// rounding of x / s (the largest code maps to the row absmax)
+template <bool BF16, bool ASYM, bool FP8 = false>
 __global__ __launch_bounds__(kThreads) void i8_quant_kernel(const uint16_t* __restrict__ X, int K,
                                                              int8_t* __restrict__ Aq, float* __restrict__ s_a,
                                                              int32_t* __restrict__ azp) {
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void i8_quant_kernel(const uint16_t* __re
     s = fmaxf(mx - mn, 1e-5f) / 255.0f;
     z = -128.0f - rintf(mn / s);
   } else {
-    s = fmaxf(mx, 1e-5f) / 127.0f;
+    s = fmaxf(mx, 1e-5f) / (FP8 ? 448.0f : 127.0f);
     z = 0.0f;
   }
   if (tid == 0) {
@@ -89,6 +92,11 @@ __global__ __launch_bounds__(kThreads) void i8_quant_kernel(const uint16_t* __re
     uint32_t out[2] = {0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if constexpr (FP8) {
+        const uint32_t qa = e4m3_code(half_lo(w[i], BF16) / s), qb = e4m3_code(half_hi(w[i], BF16) / s);
+        out[i >> 1] |= (qa | (qb << 8)) << (16 * (i & 1));
+        continue;
+      }
       const float a = fminf(fmaxf(rintf(half_lo(w[i], BF16) / s) + z, lo), 127.0f);
       const float b = fminf(fmaxf(rintf(half_hi(w[i], BF16) / s) + z, lo), 127.0f);
       const uint32_t qa = (uint32_t)(int32_t)a & 0xFFu, qb = (uint32_t)(int32_t)b & 0xFFu;
@@ -117,6 +125,16 @@ hipError_t launch_i8_quant(const void* X, bool bf16, int M, int K, int8_t* Aq, f
     if (azp) hipLaunchKernelGGL((i8_quant_kernel<false, true>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
     else hipLaunchKernelGGL((i8_quant_kernel<false, false>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_f8_quant(const void* X, bool bf16, int M, int K, uint8_t* Aq, float* s_a, hipStream_t st) {
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  int8_t* q = reinterpret_cast<int8_t*>(Aq);
+  if (bf16)
+    hipLaunchKernelGGL((i8_quant_kernel<true, false, true>), dim3(M), dim3(kThreads), 0, st, x, K, q, s_a, nullptr);
+  else
+    hipLaunchKernelGGL((i8_quant_kernel<false, false, true>), dim3(M), dim3(kThreads), 0, st, x, K, q, s_a, nullptr);
   return hipGetLastError();
 }
 

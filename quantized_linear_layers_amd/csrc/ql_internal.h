@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace ql {
 
 // Records a printf-style message for ql_last_error() and returns `code`.
@@ -51,6 +53,24 @@ inline Q4Layout q4_layout(int N, int K) {
 // (k = 2p, k = 2p + 1) as two 16-bit lanes.
 inline int nib_pos(int i) { return (i & 1) * 4 + (i >> 1); }
 
+// ---------------------------------------------------------------- FP8 E4M3
+// fp32 -> OCP FP8 E4M3 code ("FN": sign, 4 exponent bits with bias 7, 3
+// mantissa bits, no infinities, S.1111.111 = NaN, largest finite 1.75 * 2^8 =
+// 448): round to nearest, ties to even, saturating at +-448.  Normal results
+// round the fp32 significand at its bit 20 (the carry moves into the
+// exponent); below 2^-6 the grid is 2^-9 and v * 512 is rounded exactly.
+__host__ __device__ inline uint32_t e4m3_code(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;                 // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;                 // |v| >= 448: saturate
+  if (a < 0x3C800000u)                                       // |v| < 2^-6
+    return sign | (uint32_t)rintf(__builtin_bit_cast(float, a) * 512.0f);
+  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+  return sign | ((r >> 20) - (120u << 3));
+}
+
 // ---------------------------------------------------------------- launch plans
 struct GemvPlan {
   int nt;          // 16-column slices per workgroup (1, 2 or 4)
@@ -69,6 +89,8 @@ hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N,
 hipError_t launch_i8_quant(const void* X, bool bf16, int M, int K, int8_t* Aq, float* s_a,
                            int32_t* azp, hipStream_t st);
 
+hipError_t launch_f8_quant(const void* X, bool bf16, int M, int K, uint8_t* Aq, float* s_a, hipStream_t st);
+
 struct I8Epi {
   const float* s_a; int s_a_vec;
   const float* s_b; int s_b_vec;
@@ -80,6 +102,10 @@ struct I8Epi {
 };
 
 hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K,
+                          const I8Epi& e, hipStream_t st);
+
+// FP8 (E4M3) operands with the same tiling; e.azp, e.azp_adj and e.raw must be null
+hipError_t launch_f8_gemm(const uint8_t* A, const uint8_t* B, int M, int N, int K,
                           const I8Epi& e, hipStream_t st);
 
 }  // namespace ql

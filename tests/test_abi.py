@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -164,3 +164,56 @@ def test_i8_weight_prep_vs_oracle():
     assert np.array_equal(s_b.numpy().view(np.uint32), s_b_o.view(np.uint32))
     adj = ql.i8_azp_adj(Bq)
     assert np.array_equal(adj.numpy(), ow8.azp_adj(Bq_o))
+
+
+def test_f8_validation():
+    L = ql.lib()
+    P = FAKE
+    assert L.f8_quant_per_token(P, 0, 4, 12, P, P, None) == QL_ERR_SHAPE         # K % 8
+    assert L.f8_quant_per_token(P, 5, 4, 16, P, P, None) == QL_ERR_DTYPE
+    assert L.f8_quant_per_token(None, 0, 4, 16, P, P, None) == QL_ERR_NULL
+    assert L.f8_quant_per_token(FAKE_MIS, 0, 4, 16, P, P, None) == QL_ERR_ALIGN
+    assert L.f8_quant_per_token(None, 0, 0, 16, None, None, None) == QL_OK
+    args = dict(Aq=P, Bq=P, M=4, N=8, K=32, s_a=P, sal=4, s_b=P, sbl=8, bias=P, out=P, od=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.f8_gemm_scaled(a["Aq"], a["Bq"], a["M"], a["N"], a["K"], a["s_a"], a["sal"], a["s_b"], a["sbl"],
+                                a["bias"], a["out"], a["od"], None)
+    assert call(K=24) == QL_ERR_SHAPE
+    assert call(sal=3) == QL_ERR_SHAPE
+    assert call(sbl=2) == QL_ERR_SHAPE
+    assert call(od=4) == QL_ERR_DTYPE
+    assert call(Bq=None) == QL_ERR_NULL
+    assert call(out=FAKE_MIS) == QL_ERR_ALIGN
+    assert call(N=0, Bq=None) == QL_OK
+
+
+def test_f8_weight_prep_vs_oracle():
+    from oracle import fp8 as of8
+    w = wl.WORKLOADS["w8a8_prefill"]
+    W = wl.weight(w, 4096, 1024)
+    W[3, :] = 0.0                                   # a degenerate row: the 1e-5 floor
+    W[5, 7] = 1000.0                                # one large outlier
+    Bq, s_b = ql.f8_quant_weight_host(torch.from_numpy(W))
+    Bq_o, s_b_o = of8.quant_weight_per_channel_fp8(W)
+    assert np.array_equal(s_b.numpy().view(np.uint32), s_b_o.view(np.uint32))
+    assert np.array_equal(Bq.numpy(), Bq_o)
+    with pytest.raises(ql.QLError, match="-8"):
+        W[0, 0] = float("inf")
+        ql.f8_quant_weight_host(torch.from_numpy(W))
+
+
+def test_e4m3_encoder_every_code_boundary():
+    # the host encoder on every E4M3 value, every midpoint and its neighbours
+    from oracle import fp8 as of8
+    vals = np.sort(of8.E4M3_VALUES[:0x7F]).astype(np.float32)
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)     # exact in fp32
+    f32 = np.float32
+    xs = np.concatenate([vals, mids, np.nextafter(mids, f32(0)), np.nextafter(mids, f32(1e9))])
+    xs = np.concatenate([xs, -xs]).astype(np.float32)
+    W = torch.from_numpy(np.concatenate([xs, np.zeros((-len(xs)) % 16, np.float32)]).reshape(1, -1).copy())
+    W[0, -1] = 448.0                               # row absmax 448: the scale is exactly 1
+    Bq, s_b = ql.f8_quant_weight_host(W)
+    assert float(s_b[0]) == 1.0
+    assert np.array_equal(Bq.numpy()[0], of8.e4m3_encode(W.numpy()[0]))
