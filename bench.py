@@ -19,8 +19,8 @@ launches).  The step contains only the decode kernel, so the roofline
 object's mean launch duration is the timed region's elapsed time (HIP events
 on the launch stream) over its launches.  `per_case_eager` adds a second pass of eager launches,
 each bracketed by HIP events (which adds the event overhead to each figure).
-The `also` object holds the other workloads (70B decode, W8A8 prefill GEMM,
-W4A16 prefill GEMM).
+The `also` object holds the other workloads (70B decode, W8A8 prefill GEMM
+with int8 and with FP8 codes, W4A16 prefill GEMM).
 """
 
 import argparse
@@ -35,7 +35,7 @@ import torch
 import workloads as wl
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-MFMA_PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "i8": 5.0e15}   # dense, published
+MFMA_PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "i8": 5.0e15, "fp8": 5.0e15}   # dense, published
 METRIC = "W4A16 GEMV effective GB/s (% HBM peak); W8A8/W4A16 GEMM TOPS (% MFMA peak)"
 MALL_DEFEAT_BYTES = 1 << 30
 
@@ -224,6 +224,30 @@ def bench_w8a8(ql, reps):
             "end_to_end_us": round((tq + tg) * 1e3, 2)}
 
 
+def bench_f8(ql, reps):
+    """The W8A8 prefill workload with FP8 (E4M3) codes instead of int8."""
+    w = wl.WORKLOADS["w8a8_prefill"]
+    M, (K, N) = w.Ms[0], w.shapes[0]
+    X = wl.activations(w, M, K, N).cuda()
+    Bq, s_b = ql.f8_quant_weight_host(torch.from_numpy(wl.weight(w, K, N)))
+    Bq, s_b = Bq.cuda(), s_b.cuda()
+    bias = wl.bias(w, N).cuda()
+    Aq, s_a = ql.f8_quant_per_token(X)
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    fq = lambda r: ql.f8_quant_per_token(X)
+    fg = lambda r: ql.f8_gemm_scaled(Aq, Bq, s_a, s_b, bias, out=out)
+    for _ in range(3):
+        fq(0)
+        fg(0)
+    torch.cuda.synchronize()
+    tq, tg = time_launches([fq, fg], reps, torch.cuda.current_stream())
+    ops = 2.0 * M * N * K
+    return {"workload": w.name + ", FP8 E4M3 codes", "M": M, "K": K, "N": N,
+            "gemm_us": round(tg * 1e3, 2), "gemm_TFLOPS": round(ops / (tg * 1e-3) / 1e12, 1),
+            "gemm_frac_mfma_fp8": round(ops / (tg * 1e-3) / MFMA_PEAK["fp8"], 4),
+            "quant_us": round(tq * 1e3, 2), "end_to_end_us": round((tq + tg) * 1e3, 2)}
+
+
 def bench_w4_prefill(ql, reps):
     w = wl.WORKLOADS["w4a16_prefill"]
     M, (K, N) = w.Ms[0], w.shapes[0]
@@ -307,6 +331,8 @@ def main():
         print(f"# decode_70b: kernels {r70['kernel_gbs']:.1f} GB/s", flush=True)
         also["w8a8_prefill"] = bench_w8a8(ql, 20)
         print(f"# w8a8: {also['w8a8_prefill']}", flush=True)
+        also["w8a8_fp8_prefill"] = bench_f8(ql, 20)
+        print(f"# w8a8 fp8: {also['w8a8_fp8_prefill']}", flush=True)
         also["w4a16_prefill"] = bench_w4_prefill(ql, 10)
         print(f"# w4a16 prefill: {also['w4a16_prefill']}", flush=True)
 
