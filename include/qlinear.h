@@ -102,6 +102,21 @@ int q4_quantize_host(const float* W, int N, int K, int group,
                      uint32_t* wq, uint16_t* scales, uint8_t* zeros);
 
 /*
+ * q4_quantize_sym_host — per-group symmetric round-to-nearest to 4 bits with
+ * the zero point fixed at 8 (unsigned codes 1..15 standing for −7..7).
+ *
+ * [LQ] "对称与非对称": z = 0, s = max|w| / q_max with q_max = 7, signed codes
+ * −7..7 (−8 unused); stored as the unsigned code + 8, which is exactly the
+ * asymmetric code of a zero point 8 ([QK] §9.5's plain decode subtracts 8).
+ * For each output channel n and group g, in IEEE fp32 with round-half-to-even:
+ *     s = fp16(max(max |w|, 1e-5) / 7),  q = clamp(round(w / s), −7, 7) + 8
+ * No zero-point array: pass zeros = NULL to q4_pack.
+ * W [N][K] fp32; wq [K/8][N] canonical words out; scales [K/group][N] fp16 out.
+ * Errors: as q4_quantize_host.
+ */
+int q4_quantize_sym_host(const float* W, int N, int K, int group, uint32_t* wq, uint16_t* scales);
+
+/*
  * q4_packed_bytes — size of the device weight blob for an N x K layer.
  * Returns 0 for invalid sizes (see q4_pack).
  */
@@ -129,10 +144,12 @@ size_t q4_packed_bytes(int N, int K, int group);
  * (each region starts on a 256-byte boundary).  The rows are chunk-major so
  * that all output channels at one K position are contiguous in memory.
  *
+ * zeros == NULL stores the zero point 8 for every group (the symmetric codes
+ * of q4_quantize_sym_host).
  * packed: host buffer of packed_bytes >= q4_packed_bytes(N, K, group).
  * Copy it to device memory (any 16-byte-aligned address) for q4_gemm.
- * Errors: QL_ERR_NULL; QL_ERR_SHAPE as q4_quantize_host; QL_ERR_UNSUPPORTED
- *         unless group == 128; QL_ERR_SIZE if packed_bytes is too small;
+ * Errors: QL_ERR_NULL (wq, scales or packed); QL_ERR_SHAPE as q4_quantize_host;
+ *         QL_ERR_UNSUPPORTED unless group == 128; QL_ERR_SIZE if packed_bytes is too small;
  *         QL_ERR_RANGE if a code or zero exceeds 15.
  */
 int q4_pack(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros,

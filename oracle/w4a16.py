@@ -64,6 +64,39 @@ def quantize_w4(W, group=GROUP):
             np.ascontiguousarray(z.T.astype(np.uint8)))
 
 
+def quantize_w4_sym(W, group=GROUP):
+    """Per-group symmetric round-to-nearest quantization to 4 bits, stored as
+    unsigned codes with the zero point fixed at 8.
+
+    [LQ] "对称与非对称" (symmetric vs asymmetric): z = 0, s = max|x| / q_max with
+    q_max = 2**(b-1) - 1 = 7, signed codes -7..7 (the code -8 stays unused);
+    [LQ] "整数" and [QK] §9.5's plain decode (code - 8): the signed code is
+    stored as the unsigned nibble code + 8, which dequantizes exactly like an
+    asymmetric code with z = 8.  Same readings as quantize_w4: fp32
+    arithmetic, the codes use the fp16-rounded scale, the range is floored at
+    1e-5.
+
+        s16 = fp16(max(max_k |w|, 1e-5) / 7)
+        q = clamp(round(w / s16), -7, 7) + 8
+
+    Returns q uint8 [N, K] (1..15), s16 float16 [K/group, N], z uint8
+    [K/group, N] (all 8).
+    """
+    W = np.asarray(W, np.float32)
+    N, K = W.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    G = K // group
+    Wg = W.reshape(N, G, group)
+    amax = np.maximum(np.abs(Wg).max(axis=2), np.float32(1e-5))
+    s16 = to_f16(amax / np.float32(7))
+    sf = s16.astype(np.float32)
+    q = np.clip(rne(Wg / sf[:, :, None]), -7, 7) + 8
+    return (q.reshape(N, K).astype(np.uint8),
+            np.ascontiguousarray(s16.T),
+            np.full((G, N), 8, np.uint8))
+
+
 def pack_canonical(q):
     """Canonical int32 packing: 8 codes along K per 32-bit word, code i of a
     word at bits 4i..4i+3, words indexed [k // 8, n] ([LQ] W4A16 section: the

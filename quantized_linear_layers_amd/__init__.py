@@ -39,6 +39,7 @@ def lib():
             "ql_last_error": (C.c_char_p, []),
             "ql_abi_version": (I, []),
             "q4_quantize_host": (I, [P, I, I, I, P, P, P]),
+            "q4_quantize_sym_host": (I, [P, I, I, I, P, P]),
             "q4_packed_bytes": (Z, [I, I, I]),
             "q4_pack": (I, [P, P, P, I, I, I, P, Z]),
             "q4_unpack": (I, [P, Z, I, I, I, P, P, P]),
@@ -110,15 +111,28 @@ def q4_quantize_host(W, group=GROUP):
     return wq, scales, zeros
 
 
+def q4_quantize_sym_host(W, group=GROUP):
+    """W: CPU fp32 [N, K] -> (wq uint32 [K/8, N] as int32, scales fp16 [K/g, N]); symmetric codes with
+    the zero point fixed at 8 (pack with zeros=None)."""
+    W = _host(W, torch.float32)
+    N, K = W.shape
+    wq = torch.empty((K // 8, N), dtype=torch.int32)
+    scales = torch.empty((K // group, N), dtype=torch.float16)
+    _check(lib().q4_quantize_sym_host(_ptr(W), N, K, group, _ptr(wq), _ptr(scales)), "q4_quantize_sym_host")
+    return wq, scales
+
+
 def q4_packed_bytes(N, K, group=GROUP):
     return int(lib().q4_packed_bytes(N, K, group))
 
 
 def q4_pack(wq, scales, zeros, N, K, group=GROUP, device=None):
-    """Canonical host triple -> device blob (uint8 tensor on `device`, CPU if None)."""
+    """Canonical host triple -> device blob (uint8 tensor on `device`, CPU if None).
+    zeros=None stores the zero point 8 for every group (symmetric codes)."""
     wq = _host(wq, torch.int32)
     scales = _host(scales, torch.float16)
-    zeros = _host(zeros, torch.uint8)
+    if zeros is not None:
+        zeros = _host(zeros, torch.uint8)
     nb = q4_packed_bytes(N, K, group)
     if nb == 0:
         raise QLError(f"q4_pack: invalid shape N={N} K={K} group={group}")

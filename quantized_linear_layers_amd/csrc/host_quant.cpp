@@ -113,6 +113,37 @@ int q4_quantize_host(const float* W, int N, int K, int group, uint32_t* wq, uint
   return QL_OK;
 }
 
+int q4_quantize_sym_host(const float* W, int N, int K, int group, uint32_t* wq, uint16_t* scales) {
+  if (!W || !wq || !scales) return ql::set_error(QL_ERR_NULL, "q4_quantize_sym_host: NULL pointer");
+  if (int e = check_q4_shape("q4_quantize_sym_host", N, K, group)) return e;
+  const int G = K / group;
+  memset(wq, 0, sizeof(uint32_t) * (size_t)(K / 8) * N);
+  for (int n = 0; n < N; ++n) {
+    for (int g = 0; g < G; ++g) {
+      const float* w = W + (size_t)n * K + (size_t)g * group;
+      float amax = 0.0f;
+      for (int i = 0; i < group; ++i) {
+        const float v = w[i];
+        if (!(v == v) || isinf(v))
+          return ql::set_error(QL_ERR_RANGE, "q4_quantize_sym_host: W[%d][%d] is not finite", n, g * group + i);
+        amax = std::max(amax, fabsf(v));
+      }
+      if (amax < 1e-5f) amax = 1e-5f;
+      const uint16_t sb = f32_to_f16_bits(amax / 7.0f);
+      if ((sb & 0x7C00u) == 0x7C00u)
+        return ql::set_error(QL_ERR_RANGE, "q4_quantize_sym_host: group (%d,%d) overflows the fp16 scale", n, g);
+      const float s = f16_bits_to_f32(sb);
+      scales[(size_t)g * N + n] = sb;
+      for (int i = 0; i < group; ++i) {
+        const float q = std::min(std::max(rintf(w[i] / s), -7.0f), 7.0f) + 8.0f;
+        const int k = g * group + i;
+        wq[(size_t)(k / 8) * N + n] |= (uint32_t)q << (4 * (k % 8));
+      }
+    }
+  }
+  return QL_OK;
+}
+
 size_t q4_packed_bytes(int N, int K, int group) {
   if (N <= 0 || K <= 0 || group != ql::kGroup || K % group) return 0;
   return ql::q4_layout(N, K).bytes;
@@ -120,15 +151,16 @@ size_t q4_packed_bytes(int N, int K, int group) {
 
 int q4_pack(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros, int N, int K, int group,
             void* packed, size_t packed_bytes) {
-  if (!wq || !scales || !zeros || !packed) return ql::set_error(QL_ERR_NULL, "q4_pack: NULL pointer");
+  if (!wq || !scales || !packed) return ql::set_error(QL_ERR_NULL, "q4_pack: NULL pointer");
   if (int e = check_q4_shape("q4_pack", N, K, group)) return e;
   const ql::Q4Layout L = ql::q4_layout(N, K);
   if (packed_bytes < L.bytes)
     return ql::set_error(QL_ERR_SIZE, "q4_pack: packed_bytes=%zu < %zu", packed_bytes, L.bytes);
   const int G = K / group;
+  auto zero = [&](int g, int n) -> uint8_t { return zeros ? zeros[(size_t)g * N + n] : (uint8_t)8; };
   for (int g = 0; g < G; ++g)
     for (int n = 0; n < N; ++n)
-      if (zeros[(size_t)g * N + n] > 15)
+      if (zero(g, n) > 15)
         return ql::set_error(QL_ERR_RANGE, "q4_pack: zeros[%d][%d]=%d exceeds 15", g, n, zeros[(size_t)g * N + n]);
   uint8_t* out = static_cast<uint8_t*>(packed);
   memset(out, 0, L.bytes);
@@ -147,7 +179,7 @@ int q4_pack(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros, in
   for (int g = 0; g < G; ++g) {
     for (int n = 0; n < N; ++n) {
       memcpy(out + s_byte(L, n, g), &scales[(size_t)g * N + n], 2);
-      out[z_byte(L, n, g)] |= (uint8_t)(zeros[(size_t)g * N + n] << (4 * (g % 2)));
+      out[z_byte(L, n, g)] |= (uint8_t)(zero(g, n) << (4 * (g % 2)));
     }
   }
   return QL_OK;

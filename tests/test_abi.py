@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -217,3 +217,19 @@ def test_e4m3_encoder_every_code_boundary():
     Bq, s_b = ql.f8_quant_weight_host(W)
     assert float(s_b[0]) == 1.0
     assert np.array_equal(Bq.numpy()[0], of8.e4m3_encode(W.numpy()[0]))
+
+
+def test_q4_symmetric_quantize_and_pack_vs_oracle():
+    w = wl.WORKLOADS["decode_7b"]
+    W = wl.weight(w, 4096, 512)
+    W[3, :128] = 0.0                                   # a degenerate group: the 1e-5 floor
+    wq, s = ql.q4_quantize_sym_host(torch.from_numpy(W))
+    q_o, s_o, z_o = ow4.quantize_w4_sym(W)
+    assert np.array_equal(wq.numpy().view(np.uint32), ow4.pack_canonical(q_o))
+    assert np.array_equal(s.numpy().view(np.uint16), s_o.view(np.uint16))
+    N, K = W.shape
+    blob = ql.q4_pack(wq, s, None, N, K)
+    wq2, s2, z2 = ql.q4_unpack(blob, N, K)
+    assert torch.equal(wq2, wq) and torch.equal(s2.view(torch.int16), s.view(torch.int16))
+    assert np.array_equal(z2.numpy(), z_o)             # every zero point is 8
+    assert ql.lib().q4_quantize_sym_host(None, 4, 128, 128, FAKE, FAKE) == QL_ERR_NULL

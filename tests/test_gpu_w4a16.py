@@ -139,3 +139,24 @@ def test_alternating_shapes_are_deterministic():
                 first.append(e)
             else:
                 assert e == first[i]
+
+
+# ---------------------------------------------------------------- symmetric codes (zero point 8)
+
+@pytest.mark.parametrize("M,K,N,dtype", [(1, 4096, 4096, torch.float16), (16, 11008, 4096, torch.float16),
+                                         (8, 8192, 1024, torch.bfloat16), (300, 1024, 520, torch.bfloat16)])
+def test_symmetric_codes(M, K, N, dtype):
+    """Blobs from q4_quantize_sym_host + q4_pack(zeros=None) through both
+    kernels (decode for M <= 16, GEMM above) against the oracle's symmetric
+    quantizer and explicit-dequant product."""
+    w = wl.WORKLOADS["decode_7b"]
+    W = wl.weight(w, K, N)
+    wq, s = ql.q4_quantize_sym_host(torch.from_numpy(W))
+    blob = ql.q4_pack(wq, s, None, N, K, device="cuda")
+    r = np.random.default_rng(M + K)
+    X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
+    Y = ql.q4_gemm(X.cuda(), blob, N)
+    torch.cuda.synchronize()
+    q, s_o, z = ow4.quantize_w4_sym(W)
+    Y64 = ow4.w4a16_linear(wl.as_f64(X), q, s_o, z)
+    assert rel_err(wl.as_f64(Y.cpu()), Y64) <= TOL

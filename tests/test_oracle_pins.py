@@ -226,3 +226,20 @@ def test_lq_fp8_e4m3_examples():
     nan_codes = [c for c in range(256) if np.isnan(vals[c])]
     assert nan_codes == [0x7F, 0xFF]                    # S.1111.111 only, no infinities
     assert np.nanmin(np.abs(vals[vals != 0])) == 2.0 ** -9
+
+
+def test_lq_symmetric_int4_as_zero8_codes():
+    """The symmetric W4 quantizer (codes + 8, z = 8) reproduces the page's
+    symmetric INT4 codes on its vector and its GELU row (one group of 8); the
+    MSE printed for the GELU row (with the exact scale 3.1/7) holds within the
+    fp16 rounding of the stored scale."""
+    g = golden("lq_asym_vs_sym.json")
+    for key in ("x", "gelu_row"):
+        x = np.array(g[key])
+        q, s16, z = w4.quantize_w4_sym(x[None, :], group=8)
+        s4, qmax = qu.symmetric_params(x, 4)
+        assert np.array_equal(q[0].astype(int) - 8, qu.quantize_symmetric(x, s4, qmax).astype(int))
+        assert np.all(z == 8) and q.min() >= 1
+        deq = w4.dequantize_w4(q, s16, z, group=8)[0]
+        assert np.array_equal(deq, float(s16[0, 0]) * (q[0].astype(np.float64) - 8))
+    assert abs(qu.mse(deq, x) - g["gelu_sym_int4_mse"]) / g["gelu_sym_int4_mse"] < 0.01
