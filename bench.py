@@ -264,6 +264,31 @@ def bench_w4_prefill(ql, reps):
             "TFLOPS": round(ops / (t * 1e-3) / 1e12, 1), "frac_mfma_bf16": round(ops / (t * 1e-3) / MFMA_PEAK["bf16"], 4)}
 
 
+def bench_mid_m(ql, reps):
+    """W4A16 with 32 .. 256 tokens (the large-M kernel's small tiles), each
+    (M, K, N) case timed on its own, weights rotated over copies larger than
+    the last-level cache."""
+    w = wl.WORKLOADS["mid_m_7b"]
+    per_case = {}
+    for (K, N) in w.shapes:
+        R = _copies_for(ql.q4_packed_bytes(N, K))
+        _, blobs = _prepare_w4(ql, w, K, N, R)
+        for M in w.Ms:
+            X = wl.activations(w, M, K, N).cuda()
+            Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
+            launchers = [ql.q4_gemm_launcher(X, blobs[r], N, Y) for r in range(R)]
+            fns = [lambda r, f=f: f() for f in launchers]
+            for f in launchers:
+                f()
+            torch.cuda.synchronize()
+            t = float(np.mean(time_launches(fns, reps, torch.cuda.current_stream())))
+            per_case[f"{M}x{K}x{N}"] = {"us": round(t * 1e3, 2),
+                                        "TFLOPS": round(2.0 * M * N * K / (t * 1e-3) / 1e12, 1),
+                                        "GBps": round(w4a16_bytes(M, K, N) / (t * 1e-3) / 1e9, 1)}
+        del blobs
+    return {"workload": w.name, "per_case": per_case}
+
+
 def cpu_baseline(budget_s=20.0):
     """The oracle (explicit dequant + fp64 product), untuned, on the host cores,
     over whole steps of the 7B decode workload until about budget_s seconds."""
@@ -335,6 +360,8 @@ def main():
         print(f"# w8a8 fp8: {also['w8a8_fp8_prefill']}", flush=True)
         also["w4a16_prefill"] = bench_w4_prefill(ql, 10)
         print(f"# w4a16 prefill: {also['w4a16_prefill']}", flush=True)
+        also["w4a16_mid_m"] = bench_mid_m(ql, 10)
+        print(f"# w4a16 mid-M: {also['w4a16_mid_m']}", flush=True)
 
     cpu = None if args.no_cpu else cpu_baseline()
     # the step is nothing but the decode kernel's launches: its mean launch

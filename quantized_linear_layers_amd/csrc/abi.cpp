@@ -61,7 +61,7 @@ int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed,
     return ql::set_error(QL_ERR_SIZE, "q4_gemm: packed_bytes=%zu < %zu for N=%d K=%d", packed_bytes, L.bytes, N, K);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = x_dtype == QL_BF16;
-  if (M <= 16) {
+  if (M <= ql::kGemvMaxM) {
     const ql::GemvPlan P = ql::plan_q4_gemv(M, N, K);
     return hip_status("q4_gemm", ql::launch_q4_gemv(X, bf16, M, K, N, static_cast<const uint8_t*>(packed),
                                                      L, P, Y, st));

@@ -33,34 +33,55 @@
 
 #include "ql_internal.h"
 
+#ifdef QL_GEMM_TILE
+#include <cstdlib>
+#endif
+
 namespace ql {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-#ifndef QL_GEMM_NTW
-#define QL_GEMM_NTW 1
-#endif
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kMT = BM / 32;                    // 32-row MFMA tiles per wave (every wave spans all rows)
-constexpr int kNTW = QL_GEMM_NTW;               // 32-column MFMA tiles per wave
-constexpr int kWaves = BN / (32 * kNTW);        // wave w owns columns 32 kNTW w .. +32 kNTW
-constexpr int kStages = 3;
-constexpr int kATile = BM * BK * 2;             // X tile of one stage: 256 rows x 128 bytes
-constexpr int kBWave = 2 * 32 * kNTW * 16;      // packed weights of one wave: 2 chunks x 32 kNTW columns x 16 B
-constexpr int kSZWave = 2 * 32 * kNTW * 4;      // scale words, then zero-point words, of one wave
-constexpr int kBOff = kATile;
-constexpr int kSZOff = kBOff + kWaves * kBWave;
-constexpr int kStage = kSZOff + kWaves * kSZWave;           // 43008 bytes
-constexpr int kAFills = kATile / 1024 / kWaves;             // 1 KB X blocks per wave and stage
-constexpr int kLoads = kAFills + 2 * kNTW;                  // copies per wave and stage
-constexpr int kXBuf = kWaves >= 8 ? 1 : 2;                  // X fragment buffers per wave
+constexpr int BK = 64;
+constexpr int kNTW = 1;                         // 32-column MFMA tiles per wave
 
-__shared__ __align__(1024) uint8_t g_lds[kStages * kStage];
+// Tile configuration.  A workgroup owns BM = 32 MT rows x BN = 32 WN columns
+// of Y.  Its WN * WK waves form WK K-groups of WN waves: the K-groups take
+// consecutive, equal runs of the K blocks (the workgroup's split of K), each
+// with its own X tile in every LDS stage; the WN waves of a K-group share
+// that X tile and own 32 columns each.  With WK > 1 the K-groups add their
+// partial tiles in LDS at the end.  Prefill uses <8, 8, 1>: one K-group, all
+// 256 rows per wave; fewer tokens use smaller square tiles with the K range
+// split among the waves, so that a layer still yields hundreds of workgroups.
+template <int MT_, int WN_, int WK_, int ST_>
+struct Cfg {
+  static constexpr int kMT = MT_;               // 32-row MFMA tiles per wave (every wave spans all BM rows)
+  static constexpr int WN = WN_, WK = WK_;
+  static constexpr int kStages = ST_;
+  static constexpr int BM = 32 * kMT, BN = 32 * WN * kNTW;
+  static constexpr int kWaves = WN * WK;
+  static constexpr int kATile = BM * BK * 2;             // X tile of one K-group and stage: BM rows x 128 bytes
+  static constexpr int kBWave = 2 * 32 * kNTW * 16;      // packed weights of one wave: 2 chunks x 32 columns x 16 B
+  static constexpr int kSZWave = 2 * 32 * kNTW * 4;      // scale words, then zero-point words, of one wave
+  static constexpr int kBOff = kATile;
+  static constexpr int kSZOff = kBOff + WN * kBWave;
+  static constexpr int kKGroup = kSZOff + WN * kSZWave;  // one K-group's part of a stage
+  static constexpr int kStage = WK * kKGroup;
+  static constexpr int kLds = kStages * kStage;
+  static constexpr int kAFills = kATile / 1024 / WN;     // 1 KB X blocks per wave and stage
+  static constexpr int kLoads = kAFills + 2 * kNTW;      // copies per wave and stage
+  static constexpr int kXBuf = kWaves >= 8 ? 1 : 2;      // X fragment buffers per wave
+  static constexpr int kRed = (WK - 1) * WN * kMT * 4096;  // partial tiles of K-groups 1 .. WK-1
+  static_assert(kAFills >= 1 && kATile % (1024 * WN) == 0, "X blocks per wave");
+  static_assert(kRed <= kLds, "the K-group reduction reuses the stages");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+};
+using PrefillCfg = Cfg<8, 8, 1, 3>;
 
 struct GemmArgs {
   const uint16_t* X;
@@ -223,9 +244,10 @@ __device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
 // of column f, else the aligned word holding the zero byte of column
 // f - 32 kNTW).  Sources are kept as 32-bit byte offsets from the (uniform)
 // base pointers, one register each; every operand is below 4 GiB.
+template <class C>
 struct FillPlan {
-  uint32_t x[kAFills];          // X row of each 1 KB block (+ the lane's logical piece)
-  int xdst[kAFills];            // byte offset of the block inside the stage
+  uint32_t x[C::kAFills];       // X row of each 1 KB block (+ the lane's logical piece)
+  int xdst[C::kAFills];         // byte offset of the block inside the stage
   uint32_t w[kNTW];             // weight column of each chunk copy (chunk row added per block)
   int wc[kNTW];                 // chunk (0 or 1) of each chunk copy
   uint32_t sz[kNTW];            // scale word / aligned zero word of each scale copy
@@ -233,13 +255,13 @@ struct FillPlan {
   int wdst, szdst;              // byte offsets of the wave's weight and scale/zero areas
 };
 
-template <int S>
-__device__ inline void fill(const GemmArgs& a, const FillPlan& f, int kb) {
-  uint8_t* st = g_lds + S * kStage;
+template <class C, int S>
+__device__ inline void fill(uint8_t* lds, const GemmArgs& a, const FillPlan<C>& f, int kb) {
+  uint8_t* st = lds + S * C::kStage;
   const char* xb = reinterpret_cast<const char*>(a.X);
   const char* wb = reinterpret_cast<const char*>(a.W);
 #pragma unroll
-  for (int i = 0; i < kAFills; ++i) load_lds16(xb + f.x[i] + (uint32_t)kb * (BK * 2), st + f.xdst[i]);
+  for (int i = 0; i < C::kAFills; ++i) load_lds16(xb + f.x[i] + (uint32_t)kb * (BK * 2), st + f.xdst[i]);
   const uint32_t pr = kb >> 2;                              // pair of groups of this k block
   const uint32_t np = a.Np;
 #pragma unroll
@@ -253,9 +275,9 @@ __device__ inline void fill(const GemmArgs& a, const FillPlan& f, int kb) {
   }
 }
 
-template <bool BF16>
+template <class C>
 struct Frag {
-  f32x16 acc[kMT][kNTW];
+  f32x16 acc[C::kMT][kNTW];
 };
 
 // Multiplies stage S (k block kb) into the accumulators.
@@ -265,16 +287,17 @@ struct Frag {
 //           column tile 0; + 32 kNTW * 16 per chunk, + 512 per column tile
 //   szrd:   LDS address (stage 0) of the lane's scale word of column tile 0;
 //           + 128 kNTW for its zero word, + 128 per column tile
-template <bool BF16, int S>
-__device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd,
+template <class C, bool BF16, int S>
+__device__ inline void compute(Frag<C>& fr, int kb, const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd,
                                int zshift) {
-  constexpr int SO = S * kStage;
+  constexpr int kMT = C::kMT, kXBuf = C::kXBuf;
+  constexpr int SO = S * C::kStage;
   const uint32_t wst = wrd + SO, szst = szrd + SO;
   // packed words (2 chunks x kNTW column tiles) and this group's scale / zero
   u32x2 wv[2][kNTW];
   uint32_t sv[kNTW], zv[kNTW];
-  static_for<0, 2>([&](auto C) {
-    static_for<0, kNTW>([&](auto T) { wv[C][T] = lds_read8<C * 32 * kNTW * 16 + T * 512>(wst); });
+  static_for<0, 2>([&](auto CH) {
+    static_for<0, kNTW>([&](auto T) { wv[CH][T] = lds_read8<CH * 32 * kNTW * 16 + T * 512>(wst); });
   });
   static_for<0, kNTW>([&](auto T) {
     sv[T] = lds_read4<T * 128>(szst);
@@ -340,26 +363,38 @@ __device__ inline void compute(Frag<BF16>& fr, int kb, const uint32_t (&xrd)[4],
   });
 }
 
-template <bool BF16, int S>
-__device__ inline void kstep(Frag<BF16>& fr, const GemmArgs& a, const FillPlan& f, int kb, int nkb,
-                             const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd, int zshift) {
-  // this wave's copies of block kb have landed once only the next block's remain
-  wait_vm<(kStages - 2) * kLoads>();
-  __builtin_amdgcn_s_barrier();   // every wave's copies of block kb landed; block kb - 1 fully read
-  constexpr int F = (S + kStages - 1) % kStages;
-  fill<F>(a, f, min(kb + kStages - 1, nkb - 1));
-  compute<BF16, S>(fr, kb, xrd, wrd, szrd, zshift);
+// Step i of a K-group's run (the run's block kb0 + i, present if i < cnt):
+// wait for its copies, refill the stage read one step earlier with the block
+// kStages - 1 steps ahead (clamped to the layer's last block: a valid copy
+// that is never multiplied), then multiply.  Every wave of the workgroup
+// takes the same number of steps, so the barriers match.
+template <class C, bool BF16, int S>
+__device__ inline void kstep(uint8_t* lds, Frag<C>& fr, const GemmArgs& a, const FillPlan<C>& f, int i, int kb0,
+                             int cnt, int nkb, const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd, int zshift) {
+  // this wave's copies of step i have landed once only the later steps' remain
+  wait_vm<(C::kStages - 2) * C::kLoads>();
+  __builtin_amdgcn_s_barrier();   // every wave's copies of step i landed; step i - 1 fully read
+  constexpr int F = (S + C::kStages - 1) % C::kStages;
+  fill<C, F>(lds, a, f, min(kb0 + i + C::kStages - 1, nkb - 1));
+  if (i < cnt) compute<C, BF16, S>(fr, kb0 + i, xrd, wrd, szrd, zshift);
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
+template <class C, bool BF16>
+__global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(GemmArgs a) {
+  constexpr int kMT = C::kMT, kAFills = C::kAFills, kStages = C::kStages;
+  __shared__ __align__(1024) uint8_t lds[C::kLds];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % C::WN, wk = wave / C::WN;          // column slot and K-group of this wave
   int mtile, ntile;
-  tile_of(blockIdx.x, (a.M + BM - 1) / BM, (a.N + BN - 1) / BN, mtile, ntile);
-  const int m0 = mtile * BM, n0 = ntile * BN;
-  const int nw0 = n0 + 32 * kNTW * wave;         // first column of this wave
+  tile_of(blockIdx.x, (a.M + C::BM - 1) / C::BM, (a.N + C::BN - 1) / C::BN, mtile, ntile);
+  const int m0 = mtile * C::BM, n0 = ntile * C::BN;
+  const int nw0 = n0 + 32 * kNTW * wn;           // first column of this wave
   const int nkb = a.K / BK;
+  // this K-group's run of blocks: kb0 .. kb0 + cnt - 1 (every run takes `steps` steps)
+  const int steps = (nkb + C::WK - 1) / C::WK;
+  const int kb0 = min(nkb, wk * steps), cnt = min(nkb, kb0 + steps) - kb0;
+  const int kgoff = wk * C::kKGroup;             // this K-group's part of every stage
 
   // ---- copy plan.  X: the stage's 32 blocks of 1 KB (8 rows x 128 bytes),
   // kAFills per wave; lane l writes row 8b + l / 8, stored piece l % 8,
@@ -368,14 +403,14 @@ __global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
   // (two consecutive 128-byte rows span the 64 banks once).  Rows past M
   // repeat row M - 1 and columns past Np repeat column Np - 1 (valid loads
   // whose results only reach outputs that are never stored).
-  FillPlan f;
+  FillPlan<C> f;
 #pragma unroll
   for (int i = 0; i < kAFills; ++i) {
-    const int blk = wave * kAFills + i;
+    const int blk = wn * kAFills + i;
     const int r = blk * 8 + (lane >> 3);
     const int m = min(m0 + r, a.M - 1);
     f.x[i] = ((uint32_t)m * a.K + ((lane & 7) ^ ((r >> 1) & 7)) * 8) * 2;
-    f.xdst[i] = blk * 1024;
+    f.xdst[i] = kgoff + blk * 1024;
   }
 #pragma unroll
   for (int d = 0; d < kNTW; ++d) {
@@ -388,25 +423,25 @@ __global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
     f.isz[d] = fl >= 32 * kNTW;
     f.sz[d] = f.isz[d] ? (uint32_t)(ncs & ~3) : (uint32_t)ncs * 4;
   }
-  f.wdst = kBOff + wave * kBWave;
-  f.szdst = kSZOff + wave * kSZWave;
+  f.wdst = kgoff + C::kBOff + wn * C::kBWave;
+  f.szdst = kgoff + C::kSZOff + wn * C::kSZWave;
 
   // ---- read addresses (stage 0)
   typedef __attribute__((address_space(3))) uint8_t* lds_ptr;
-  const uint32_t base = (uint32_t)(uintptr_t)(lds_ptr)g_lds;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_ptr)lds;
   const int half = lane >> 5, l32 = lane & 31;
   uint32_t xrd[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     // step j = 2c + s takes k 32c + 8 * (2 * half + s) .. +8: logical piece 4c + 2*half + s
     const int p = 4 * (j >> 1) + 2 * half + (j & 1);
-    xrd[j] = base + l32 * 128 + ((p ^ ((l32 >> 1) & 7)) * 16);
+    xrd[j] = base + kgoff + l32 * 128 + ((p ^ ((l32 >> 1) & 7)) * 16);
   }
   const uint32_t wrd = base + f.wdst + l32 * 16 + half * 8;      // + 512 per column tile, + 32 kNTW * 16 per chunk
   const uint32_t szrd = base + f.szdst + l32 * 4;                // + 128 per column tile, + 128 kNTW for zeros
   const int zshift = 8 * (l32 & 3);                              // the column's byte inside its word
 
-  Frag<BF16> fr;
+  Frag<C> fr;
 #pragma unroll
   for (int i = 0; i < kMT; ++i)
 #pragma unroll
@@ -414,21 +449,45 @@ __global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) fr.acc[i][t][e] = 0.0f;
 
-  // prologue: blocks 0 .. kStages - 2 in flight (clamped to the last block)
-  fill<0>(a, f, 0);
-  fill<1>(a, f, min(1, nkb - 1));
+  // prologue: steps 0 .. kStages - 2 in flight (clamped to the last block)
+  static_for<0, kStages - 1>([&](auto J) { fill<C, J>(lds, a, f, min(kb0 + (int)J, nkb - 1)); });
 
-  int kb = 0;
-  for (; kb + kStages <= nkb; kb += kStages) {
-    kstep<BF16, 0>(fr, a, f, kb, nkb, xrd, wrd, szrd, zshift);
-    kstep<BF16, 1>(fr, a, f, kb + 1, nkb, xrd, wrd, szrd, zshift);
-    kstep<BF16, 2>(fr, a, f, kb + 2, nkb, xrd, wrd, szrd, zshift);
-  }
-  if (kb < nkb) {
-    kstep<BF16, 0>(fr, a, f, kb, nkb, xrd, wrd, szrd, zshift);
-    if (kb + 1 < nkb) kstep<BF16, 1>(fr, a, f, kb + 1, nkb, xrd, wrd, szrd, zshift);
-  }
+  int i = 0;
+  for (; i + kStages <= steps; i += kStages)
+    static_for<0, kStages>(
+        [&](auto S) { kstep<C, BF16, S>(lds, fr, a, f, i + S, kb0, cnt, nkb, xrd, wrd, szrd, zshift); });
+  static_for<0, kStages - 1>([&](auto S) {
+    if (i + S < steps) kstep<C, BF16, S>(lds, fr, a, f, i + S, kb0, cnt, nkb, xrd, wrd, szrd, zshift);
+  });
   wait_vm<0>();                                  // no copy may still target LDS at exit
+
+  if constexpr (C::WK > 1) {
+    // K-groups 1 .. WK-1 leave their partial tiles in LDS (16 bytes per lane
+    // and 4 accumulators); K-group 0 adds them and stores
+    __syncthreads();                             // every stage fully read
+    if (wk > 0) {
+      uint8_t* red = lds + ((wk - 1) * C::WN + wn) * (kMT * 4096);
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(red + mt * 4096 + q * 1024 + lane * 16) =
+              f32x4{fr.acc[mt][0][4 * q], fr.acc[mt][0][4 * q + 1], fr.acc[mt][0][4 * q + 2], fr.acc[mt][0][4 * q + 3]};
+    }
+    __syncthreads();
+    if (wk > 0) return;
+    for (int w = 1; w < C::WK; ++w) {
+      const uint8_t* red = lds + ((w - 1) * C::WN + wn) * (kMT * 4096);
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(red + mt * 4096 + q * 1024 + lane * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fr.acc[mt][0][4 * q + e] += v[e];
+        }
+    }
+  }
 
   // ---- store: acc element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
 #pragma unroll
@@ -449,7 +508,45 @@ __global__ __launch_bounds__(64 * kWaves) void q4_gemm_kernel(GemmArgs a) {
   }
 }
 
+template <class C>
+hipError_t launch_cfg(const GemmArgs& a, bool bf16, hipStream_t st) {
+  const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
+  if (bf16)
+    hipLaunchKernelGGL((q4_gemm_kernel<C, true>), dim3(tiles), dim3(64 * C::kWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((q4_gemm_kernel<C, false>), dim3(tiles), dim3(64 * C::kWaves), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// Square tile edge for an M x N x K product.  Every tile size has 8 waves and
+// the same LDS stages, so one workgroup fills a compute unit, and with few
+// tokens its K loop runs at a near-constant time per stage (two stages in
+// flight: memory round trips, not arithmetic, set the pace).  The estimate is
+// rounds x (ramp + K steps of a K-group x step time), with 256 workgroups a
+// round and the step times measured on the Llama-2 7B / 70B layers (0.72,
+// 0.76, 0.92 and 1.38 us for tiles 32 .. 256, ramp 2.5 us); the smallest
+// estimate wins, ties going to the larger tile.
+int gemm_tile(int M, int N, int K) {
+#ifdef QL_GEMM_TILE
+  if (const char* e = getenv("QL_GEMM_TILE")) return atoi(e);
+#endif
+  const long nkb = K / BK;
+  int best = 256;
+  double best_cost = 0.0;
+  for (int t = 256; t >= 32; t /= 2) {
+    const long wk = 256 / t;                             // K-groups of the tile's configuration
+    const long wgs = (long)((M + t - 1) / t) * ((N + t - 1) / t);
+    const double step = t == 256 ? 1.38 : t == 128 ? 0.92 : t == 64 ? 0.76 : 0.72;
+    const double cost = (double)((wgs + 255) / 256) * (2.5 + (double)((nkb + wk - 1) / wk) * step);
+    if (t == 256 || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const uint8_t* blob, const Q4Layout& L,
                           void* Y, hipStream_t st) {
@@ -463,12 +560,12 @@ hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const u
   a.S = reinterpret_cast<const uint32_t*>(blob + L.s_off);
   a.Z = blob + L.z_off;
   a.Y = static_cast<uint16_t*>(Y);
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (bf16)
-    hipLaunchKernelGGL(q4_gemm_kernel<true>, dim3(tiles), dim3(64 * kWaves), 0, st, a);
-  else
-    hipLaunchKernelGGL(q4_gemm_kernel<false>, dim3(tiles), dim3(64 * kWaves), 0, st, a);
-  return hipGetLastError();
+  switch (gemm_tile(M, N, K)) {
+    case 32: return launch_cfg<Cfg<1, 1, 8, 3>>(a, bf16, st);
+    case 64: return launch_cfg<Cfg<2, 2, 4, 3>>(a, bf16, st);
+    case 128: return launch_cfg<Cfg<4, 4, 2, 3>>(a, bf16, st);
+    default: return launch_cfg<PrefillCfg>(a, bf16, st);
+  }
 }
 
 }  // namespace ql

@@ -79,6 +79,10 @@ struct GemvPlan {
 
 GemvPlan plan_q4_gemv(int M, int N, int K);
 
+// square tile edge the large-M kernel uses for an M x N x K product (32 .. 256)
+int gemm_tile(int M, int N, int K);
+// token counts served by the decode-family kernel; larger M takes the GEMM
+constexpr int kGemvMaxM = 16;
 hipError_t launch_q4_gemv(const void* X, bool bf16, int M, int K, int N,
                           const uint8_t* blob, const Q4Layout& L, const GemvPlan& P,
                           void* Y, hipStream_t st);

@@ -79,6 +79,27 @@ def test_decode_70b_sampled(M, K, N):
     check(W, wl.activations(w, M, K, N), cols=cols)
 
 
+@pytest.mark.parametrize("K,N", wl.WORKLOADS["mid_m_7b"].shapes)
+@pytest.mark.parametrize("M", wl.WORKLOADS["mid_m_7b"].Ms)
+def test_mid_m_7b(M, K, N):
+    w = wl.WORKLOADS["mid_m_7b"]
+    check(wl.weight(w, K, N), wl.activations(w, M, K, N))
+
+
+# shapes whose token and channel counts select each square tile of the large-M
+# kernel (32, 64, 128: the K range split among 8, 4, 2 K-groups of waves,
+# with uneven and empty runs for K = 1152 and 384); 256 is the prefill test
+@pytest.mark.parametrize("M,K,N,dtype", [(200, 1152, 1000, torch.float16), (77, 384, 4160, torch.bfloat16),
+                                         (256, 1152, 4096, torch.float16), (300, 2560, 4000, torch.bfloat16),
+                                         (512, 1152, 8192, torch.bfloat16), (400, 384, 8000, torch.float16)])
+def test_gemm_tiles(M, K, N, dtype):
+    r = np.random.default_rng(M + K + N)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
+    cols = np.sort(r.choice(N, min(N, 512), replace=False))
+    check(W, X, cols=cols)
+
+
 def test_prefill_sampled():
     w = wl.WORKLOADS["w4a16_prefill"]
     M, (K, N) = w.Ms[0], w.shapes[0]
@@ -92,7 +113,7 @@ def test_prefill_sampled():
 # ---------------------------------------------------------------- ragged shapes and edges
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16, 17, 40, 130])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 16, 17, 24, 32, 33, 40, 48, 49, 64, 65, 130])
 @pytest.mark.parametrize("K,N", [(128, 72), (384, 200), (1152, 1000), (2560, 64)])
 def test_ragged(M, K, N, dtype):
     r = np.random.default_rng(M * 1000 + K + N)

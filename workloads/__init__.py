@@ -1,7 +1,7 @@
 """Seeded synthetic workloads shared by the oracle side and the device side.
 
 This module holds NO arithmetic of the method (no quantization, packing,
-dequantization or products): only the five workload descriptions and the
+dequantization or products): only the workload descriptions and the
 seeded random draws of their fp32 weights, 16-bit activations and biases.
 Both the tests/bench (device side) and the oracle consume these draws.
 
@@ -55,6 +55,9 @@ WORKLOADS = {
                              bias_std=0.1),
     "w4a16_prefill": Workload(4, "W4A16 prefill GEMM (M=4096, K=4096, N=14336)", "w4a16",
                               (4096,), ((4096, 14336),), "bf16", 0.02),
+    "mid_m_7b": Workload(5, "W4A16 mid-M (batched decode), Llama-2-7B-shaped layers", "w4a16",
+                         (32, 64, 128, 256), ((4096, 4096), (4096, 11008), (11008, 4096)),
+                         "f16", 0.02, outliers=True),
 }
 
 
