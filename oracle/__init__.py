@@ -30,4 +30,4 @@ Every function is pinned by a ``-m "not gpu"`` test against values the pages
 print, closed forms, invariants or brute force (tests/test_oracle_*.py).
 """
 
-from . import fp8, numerics, quant, w4a16, w8a8  # noqa: F401
+from . import fp8, numerics, quant, rmsnorm, w4a16, w8a8  # noqa: F401

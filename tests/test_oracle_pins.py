@@ -243,3 +243,28 @@ def test_lq_symmetric_int4_as_zero8_codes():
         deq = w4.dequantize_w4(q, s16, z, group=8)[0]
         assert np.array_equal(deq, float(s16[0, 0]) * (q[0].astype(np.float64) - 8))
     assert abs(qu.mse(deq, x) - g["gelu_sym_int4_mse"]) / g["gelu_sym_int4_mse"] < 0.01
+
+
+# ---------------------------------------------------------------- RMSNorm + per-token quant
+
+def test_lq_rmsnorm_is_x_over_norm_times_sqrt_d():
+    from oracle import rmsnorm as rn
+    assert golden("lq_rmsnorm_fold.json")["quarot_norm_of_output"] == "sqrt(d)"
+    r = np.random.default_rng(5)
+    for d in (4, 37, 4096):
+        x = r.standard_normal((3, d))
+        y = rn.rms_norm64(x, np.ones(d), 0.0)
+        np.testing.assert_allclose(y, x / np.linalg.norm(x, axis=1, keepdims=True) * np.sqrt(d), rtol=1e-13)
+        np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.sqrt(d), rtol=1e-13)
+
+
+def test_lq_awq_gamma_over_s_emits_x_over_s():
+    # an RMSNorm whose output is the page's x (gamma = rms(row), eps = 0, row = x);
+    # dividing gamma by the AWQ scale s must emit the page's x / s
+    from oracle import rmsnorm as rn
+    g = golden("lq_rmsnorm_fold.json")
+    x = np.array(g["awq_x"], np.float64)
+    s = np.array(g["awq_s"], np.float64)
+    rms = np.sqrt(np.mean(x * x))
+    np.testing.assert_allclose(rn.rms_norm64(x[None], np.full(4, rms), 0.0)[0], x, rtol=1e-14)
+    np.testing.assert_allclose(rn.rms_norm64(x[None], rms / s, 0.0)[0], g["awq_x_over_s"], rtol=1e-14)

@@ -331,3 +331,86 @@ def test_fp8_gemm_exact_against_fractions():
     out = fp8.fp8_linear(A, B, np.float32([0.5, 2, 4]), np.float32([1, 0.25, 3, 8]), np.float64([1, 2, 3, 4]))
     assert np.allclose(out, np.float64([0.5, 2, 4])[:, None] * np.float64([1, 0.25, 3, 8])[None] * D + [1, 2, 3, 4],
                        rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- RMSNorm + per-token quant
+
+def _f16_rows(r, M, K, scale=1.0):
+    return (r.standard_normal((M, K)) * scale).astype(np.float16).astype(np.float64)
+
+
+def test_rmsnorm_constant_rows_closed_form():
+    # row m = c_m everywhere: y[m, k] = gamma[k] * c_m / sqrt(c_m^2 + eps)
+    from oracle import rmsnorm as rn
+    c = np.array([0.5, -3.0, 7.25, 1e-3])
+    gamma = np.linspace(-2.0, 3.0, 9)
+    for eps in (0.0, 1e-6, 0.25):
+        X = np.repeat(c[:, None], 9, axis=1)
+        want = gamma[None, :] * (c / np.sqrt(c * c + eps))[:, None]
+        np.testing.assert_allclose(rn.rms_norm64(X, gamma, eps), want, rtol=1e-14)
+        y32, _ = rn.rms_norm_f32(X, gamma, eps)
+        np.testing.assert_allclose(y32, want, rtol=4 * 2.0 ** -24, atol=1e-30)
+
+
+def test_rmsnorm_f32_steps_against_exact_arithmetic():
+    # mean square within one fp32 ulp of the exact rational value; y within a
+    # few fp32 ulps of the exact real result
+    from oracle import rmsnorm as rn
+    r = np.random.default_rng(11)
+    for K in (1, 3, 8, 33):
+        X = _f16_rows(r, 4, K, 3.0)
+        gamma = _f16_rows(r, 1, K)[0]
+        eps = 1e-5
+        ms = rn.mean_square_f32(X)
+        y32, inv = rn.rms_norm_f32(X, gamma, eps)
+        for m in range(4):
+            ex = sum(Fraction(float(v)) ** 2 for v in X[m]) / K
+            assert abs(Fraction(float(ms[m])) - ex) <= Fraction(float(np.spacing(np.float32(ms[m]))))
+            exact_inv = 1.0 / np.sqrt(float(ex) + float(np.float32(eps)))
+            assert abs(float(inv[m]) - exact_inv) <= 3 * 2.0 ** -24 * exact_inv
+            want = X[m] * exact_inv * gamma
+            assert np.all(np.abs(y32[m] - want) <= 5 * 2.0 ** -24 * np.abs(want) + 1e-40)
+
+
+def test_rmsnorm_power_of_two_scale_invariance_is_exact():
+    # with eps = 0, scaling a row by 2**j changes nothing, bit for bit
+    from oracle import rmsnorm as rn
+    r = np.random.default_rng(12)
+    X = _f16_rows(r, 3, 64)
+    gamma = _f16_rows(r, 1, 64)[0]
+    y0, _ = rn.rms_norm_f32(X, gamma, 0.0)
+    for j in (-6, 3):
+        yj, _ = rn.rms_norm_f32(X * 2.0 ** j, gamma, 0.0)
+        assert np.array_equal(y0, yj)
+
+
+def test_rmsnorm_rows_are_independent_and_gamma_is_per_channel():
+    from oracle import rmsnorm as rn
+    r = np.random.default_rng(13)
+    X = _f16_rows(r, 5, 16)
+    gamma = _f16_rows(r, 1, 16)[0]
+    y, _ = rn.rms_norm_f32(X, gamma, 1e-6)
+    for m in range(5):
+        ym, _ = rn.rms_norm_f32(X[m:m + 1], gamma, 1e-6)
+        assert np.array_equal(ym[0], y[m])
+    # permuting channels of x and gamma together permutes y
+    p = r.permutation(16)
+    yp, _ = rn.rms_norm_f32(X[:, p], gamma[p], 1e-6)
+    assert np.array_equal(yp, y[:, p])
+
+
+def test_rmsnorm_quant_is_the_per_token_quant_of_y():
+    from oracle import rmsnorm as rn
+    from oracle import w8a8 as w8
+    r = np.random.default_rng(14)
+    X = _f16_rows(r, 6, 128, 2.0)
+    gamma = _f16_rows(r, 1, 128)[0]
+    Aq, s_a, azp = rn.rmsnorm_quant_per_token(X, gamma, 1e-6)
+    y, _ = rn.rms_norm_f32(X, gamma, 1e-6)
+    Aq2, s2, z2 = w8.quant_per_token_asym(y)
+    assert np.array_equal(Aq, Aq2) and np.array_equal(s_a, s2) and np.array_equal(azp, z2)
+    # dequantized codes sit within half a step of y
+    deq = s_a[:, None].astype(np.float64) * (Aq.astype(np.float64) - azp[:, None])
+    assert np.all(np.abs(deq - y) <= 0.5 * s_a[:, None] * (1 + 1e-6))
+    Aqs, ss = rn.rmsnorm_quant_per_token(X, gamma, 1e-6, asym=False)
+    assert np.all(np.abs(Aqs.astype(np.int32)).max(axis=1) == 127)
