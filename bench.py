@@ -208,19 +208,23 @@ def bench_w8a8(ql, reps):
     Aq, s_a, azp = ql.i8_quant_per_token(X)
     out = torch.empty((M, N), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
+    gamma = wl.norm_weight(w, K).cuda()
     fq = lambda r: ql.i8_quant_per_token(X)
     fg = lambda r: ql.i8_gemm_scaled(Aq, Bq, s_a, s_b, azp, adj, bias, out=out)
+    fn = lambda r: ql.i8_rmsnorm_quant_per_token(X, gamma, 1e-5)
     for _ in range(3):
         fq(0)
         fg(0)
+        fn(0)
     torch.cuda.synchronize()
-    tq, tg = time_launches([fq, fg], reps, stream)
+    tq, tg, tn = time_launches([fq, fg, fn], reps, stream)
     ops = 2.0 * M * N * K
     qbytes = M * K * 2 + M * K + M * 4 + M * 4
     return {"workload": w.name, "M": M, "K": K, "N": N,
             "gemm_us": round(tg * 1e3, 2), "gemm_TOPS": round(ops / (tg * 1e-3) / 1e12, 1),
             "gemm_frac_mfma_i8": round(ops / (tg * 1e-3) / MFMA_PEAK["i8"], 4),
             "quant_us": round(tq * 1e3, 2), "quant_GBps": round(qbytes / (tq * 1e-3) / 1e9, 1),
+            "rmsnorm_quant_us": round(tn * 1e3, 2), "rmsnorm_quant_GBps": round((qbytes + K * 2) / (tn * 1e-3) / 1e9, 1),
             "end_to_end_us": round((tq + tg) * 1e3, 2)}
 
 

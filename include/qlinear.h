@@ -244,6 +244,33 @@ int i8_quant_per_token(const void* X, int x_dtype, int M, int K,
                        int8_t* Aq, float* s_a, int32_t* azp, void* stream);
 
 /*
+ * i8_rmsnorm_quant_per_token — RMSNorm fused with the dynamic per-token int8
+ * quantization of its output (device).  The normalized activations are never
+ * written: the kernel that normalizes a row also takes its range and emits
+ * its codes ([QK] §9.9: fuse the per-row reduction of the activation
+ * quantization into the producing operator; [LQ] "校准：静态与动态": the
+ * per-token reduction is folded into RMSNorm; RMSNorm as x / rms(x) · γ from
+ * [LQ] "QuaRot：把整个残差流旋转掉" and "缩放融合到哪里").
+ *
+ * Per row m, in this order (IEEE, round-half-to-even):
+ *     ms  = fp32( (Σ_k x² in fp64) / K in fp64 )      (the squares are exact)
+ *     inv = 1 / sqrt(ms + eps)                          (fp32, correctly rounded)
+ *     y   = (x · inv) · gamma[k]                        (fp32; not rounded to 16 bits)
+ * then y is quantized exactly as i8_quant_per_token quantizes x: asymmetric
+ * with azp != NULL, symmetric with azp == NULL.
+ *
+ * X [M][K] fp16/bf16; gamma [K] of the same dtype; eps > 0 and finite; Aq
+ * [M][K] int8 out; s_a [M] fp32 out; azp [M] int32 out or NULL.  M == 0 is a
+ * no-op.  Inputs are read once; nothing is allocated.
+ * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M >= 0, K > 0 and
+ *         K % 8 == 0; QL_ERR_RANGE unless eps > 0 and finite; QL_ERR_ALIGN;
+ *         QL_ERR_HIP.
+ */
+int i8_rmsnorm_quant_per_token(const void* X, int x_dtype, int M, int K,
+                               const void* gamma, float eps,
+                               int8_t* Aq, float* s_a, int32_t* azp, void* stream);
+
+/*
  * i8_gemm_scaled — int8 GEMM with int32 accumulation and the fused epilogue
  * (device).
  *

@@ -48,7 +48,8 @@ def mean_square_f32(X):
     rounded fp64 value of the exact sum."""
     X = np.asarray(X, np.float64)
     K = X.shape[1]
-    return np.array([math.fsum(r * r) / K for r in X], np.float64).astype(np.float32)
+    with np.errstate(over="ignore"):         # a mean square beyond the fp32 range becomes inf
+        return np.array([math.fsum(r * r) / K for r in X], np.float64).astype(np.float32)
 
 
 def rms_norm_f32(X, gamma, eps):

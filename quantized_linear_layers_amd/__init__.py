@@ -47,6 +47,7 @@ def lib():
             "i8_quant_weight_host": (I, [P, I, I, P, P]),
             "i8_azp_adj": (I, [P, I, I, P]),
             "i8_quant_per_token": (I, [P, I, I, I, P, P, P, P]),
+            "i8_rmsnorm_quant_per_token": (I, [P, I, I, I, P, C.c_float, P, P, P, P]),
             "i8_gemm_scaled": (I, [P, P, I, I, I, P, I, P, I, P, P, P, P, I, P, P]),
             "f8_quant_weight_host": (I, [P, I, I, P, P]),
             "f8_quant_per_token": (I, [P, I, I, I, P, P, P]),
@@ -218,6 +219,23 @@ def i8_quant_per_token(X, symmetric=False, stream=None):
     azp = None if symmetric else torch.empty(M, dtype=torch.int32, device=X.device)
     _check(lib().i8_quant_per_token(_ptr(X), _dtype_code(X.dtype), M, K, _ptr(Aq), _ptr(s_a), _ptr(azp),
                                     _stream(X, stream)), "i8_quant_per_token")
+    return Aq, s_a, azp
+
+
+def i8_rmsnorm_quant_per_token(X, gamma, eps, symmetric=False, stream=None):
+    """RMSNorm(X) · gamma quantized per token, in one kernel.  X fp16/bf16
+    [M, K] and gamma [K] of the same dtype on the device; eps > 0.
+    Returns (Aq int8 [M, K], s_a fp32 [M], azp int32 [M] or None)."""
+    X = _dev(X, name="X")
+    _dev(gamma, X.dtype, "gamma")
+    M, K = X.shape
+    if tuple(gamma.shape) != (K,):
+        raise QLError(f"i8_rmsnorm_quant_per_token: gamma has shape {tuple(gamma.shape)}, expected ({K},)")
+    Aq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    s_a = torch.empty(M, dtype=torch.float32, device=X.device)
+    azp = None if symmetric else torch.empty(M, dtype=torch.int32, device=X.device)
+    _check(lib().i8_rmsnorm_quant_per_token(_ptr(X), _dtype_code(X.dtype), M, K, _ptr(gamma), float(eps), _ptr(Aq),
+                                            _ptr(s_a), _ptr(azp), _stream(X, stream)), "i8_rmsnorm_quant_per_token")
     return Aq, s_a, azp
 
 

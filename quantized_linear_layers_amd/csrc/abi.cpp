@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <cmath>
 #include <string>
 
 #include "../../include/qlinear.h"
@@ -84,6 +85,23 @@ int i8_quant_per_token(const void* X, int x_dtype, int M, int K, int8_t* Aq, flo
     return ql::set_error(QL_ERR_ALIGN, "i8_quant_per_token: pointers must be 16-byte aligned");
   return hip_status("i8_quant_per_token",
                     ql::launch_i8_quant(X, x_dtype == QL_BF16, M, K, Aq, s_a, azp, static_cast<hipStream_t>(stream)));
+}
+
+int i8_rmsnorm_quant_per_token(const void* X, int x_dtype, int M, int K, const void* gamma, float eps, int8_t* Aq,
+                               float* s_a, int32_t* azp, void* stream) {
+  if (M < 0 || K <= 0 || K % 8)
+    return ql::set_error(QL_ERR_SHAPE, "i8_rmsnorm_quant_per_token: need M >= 0, K > 0, K %% 8 == 0 (got %d, %d)", M,
+                         K);
+  if (!valid_dtype(x_dtype)) return ql::set_error(QL_ERR_DTYPE, "i8_rmsnorm_quant_per_token: x_dtype=%d", x_dtype);
+  if (!(eps > 0.0f) || !std::isfinite(eps))
+    return ql::set_error(QL_ERR_RANGE, "i8_rmsnorm_quant_per_token: eps=%g must be > 0 and finite", (double)eps);
+  if (M == 0) return QL_OK;
+  if (!X || !gamma || !Aq || !s_a) return ql::set_error(QL_ERR_NULL, "i8_rmsnorm_quant_per_token: NULL X, gamma, Aq or s_a");
+  if (!aligned16(X) || !aligned16(gamma) || !aligned16(Aq) || !aligned16(s_a) || (azp && !aligned16(azp)))
+    return ql::set_error(QL_ERR_ALIGN, "i8_rmsnorm_quant_per_token: pointers must be 16-byte aligned");
+  return hip_status("i8_rmsnorm_quant_per_token",
+                    ql::launch_rmsnorm_quant(X, x_dtype == QL_BF16, M, K, gamma, eps, Aq, s_a, azp,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int i8_gemm_scaled(const int8_t* Aq, const int8_t* Bq, int M, int N, int K, const float* s_a, int s_a_len,

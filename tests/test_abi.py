@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -73,6 +73,19 @@ def test_i8_validation():
     assert L.i8_quant_per_token(P, 3, 4, 16, P, P, P, None) == QL_ERR_DTYPE
     assert L.i8_quant_per_token(None, 0, 4, 16, P, P, P, None) == QL_ERR_NULL
     assert L.i8_quant_per_token(P, 0, 0, 16, None, None, None, None) == QL_OK
+    # fused RMSNorm + quant: eps must be > 0 and finite
+    F = C.c_float
+    rq = L.i8_rmsnorm_quant_per_token
+    assert rq(P, 0, 4, 12, P, F(1e-6), P, P, P, None) == QL_ERR_SHAPE
+    assert rq(P, 5, 4, 16, P, F(1e-6), P, P, P, None) == QL_ERR_DTYPE
+    assert rq(P, 0, 4, 16, P, F(0.0), P, P, P, None) == QL_ERR_RANGE
+    assert rq(P, 0, 4, 16, P, F(-1.0), P, P, P, None) == QL_ERR_RANGE
+    assert rq(P, 0, 4, 16, P, F(float("nan")), P, P, P, None) == QL_ERR_RANGE
+    assert rq(P, 0, 4, 16, P, F(float("inf")), P, P, P, None) == QL_ERR_RANGE
+    assert rq(P, 0, 4, 16, None, F(1e-6), P, P, P, None) == QL_ERR_NULL
+    assert rq(None, 0, 4, 16, P, F(1e-6), P, P, P, None) == QL_ERR_NULL
+    assert rq(P, 0, 4, 16, FAKE_MIS, F(1e-6), P, P, P, None) == QL_ERR_ALIGN
+    assert rq(None, 0, 0, 16, None, F(1e-6), None, None, None, None) == QL_OK
     args = dict(Aq=P, Bq=P, M=4, N=8, K=32, s_a=P, sal=4, s_b=P, sbl=8, azp=P, adj=P, bias=P, out=P, od=0, raw=None)
 
     def call(**kw):

@@ -7,7 +7,7 @@ Both the tests/bench (device side) and the oracle consume these draws.
 
 Recipe (the same for every workload): one NumPy ``default_rng`` per tensor,
 seeded with ``SeedSequence([seed, workload_id, M, K, N, tensor_id])`` where
-tensor_id is 0 = W, 1 = X, 2 = outlier channel set, 3 = bias.  W is drawn
+tensor_id is 0 = W, 1 = X, 2 = outlier channel set, 3 = bias, 4 = RMSNorm gain.  W is drawn
 with M = 0 so that every M of a (K, N) layer shares one weight.  W =
 standard_normal((N, K)) * w_std (fp32); X = standard_normal((M, K)) + x_mean
 (fp32); if the workload has outliers, round(0.01 * K) input channels, chosen
@@ -97,6 +97,16 @@ def bias(wl, N):
     r = _rng(wl, 0, 0, N, 3)
     b = r.standard_normal(N, dtype=np.float32) * np.float32(wl.bias_std)
     return torch.from_numpy(b).to(torch.float16)
+
+
+def norm_weight(wl, K):
+    """RMSNorm gain [K] in the activation dtype, as a CPU torch tensor:
+    1 + 0.2 * N(0, 1) (tensor id 4)."""
+    import torch
+    r = _rng(wl, 0, K, 0, 4)
+    g = r.standard_normal(K, dtype=np.float32) * np.float32(0.2) + np.float32(1.0)
+    dt = torch.float16 if wl.x_dtype == "f16" else torch.bfloat16
+    return torch.from_numpy(g).to(dt)
 
 
 def as_f64(t):
