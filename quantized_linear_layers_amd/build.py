@@ -30,7 +30,7 @@ SOURCES = {
     "host_quant.cpp": ["-ffp-contract=off"],
     "q4_gemv.hip": [],
     "q4_gemm.hip": [],
-    "i8_quant.hip": [],
+    "i8_quant.hip": ["-ffp-contract=off"],
     "i8_gemm.hip": [],
 }
 

@@ -1,13 +1,28 @@
-// Dynamic per-token int8 (and FP8 E4M3) activation quantization: one
-// workgroup per row.
+// Dynamic per-token activation quantization (int8 asymmetric / symmetric and
+// FP8 E4M3), optionally fused with the RMSNorm that produces the row: one
+// wave per row.
 //
 // The row's range is found with one reduction ([LQ] "校准：静态与动态":
 // per-token absmax/range at run time costs one extra reduction), then the
 // scale, the int32 zero point and the codes follow the formulas in qlinear.h
-// with IEEE fp32 division and round-half-to-even, so every code is decided
-// exactly as a scalar CPU implementation of the same steps decides it.
-// The row is read from HBM once: up to 8 pieces of 8 values per thread stay
-// in registers between the reduction and the quantization.
+// in IEEE fp32 with round-half-to-even, so every code is decided exactly as a
+// scalar CPU implementation of the same steps decides it.
+//
+// A wave owns a row: its lanes read 16-byte pieces of it (lane l: pieces
+// l, l + 64, ...; 64 lanes x 16 bytes = one contiguous kilobyte per load), up
+// to kLanePieces of them stay in registers between the reduction and the
+// quantization (so the row is read from HBM once for K <= 4096; the rest of a
+// longer row is read again, mostly from the L2), and the
+// reductions are wave shuffles: no LDS, no barriers, and four rows per
+// workgroup that never wait for each other.
+//
+// x / s with a cheap exact rounding.  The codes are functions of the
+// correctly rounded fp32 quotient x / s.  With r = 1 / s and t = x * r (both
+// rounded), |t - x/s| <= (2^-23 + 2^-48) |x/s| and the rounded quotient is
+// within 2^-24 |x/s| of x/s: t decides the code unless it lies next to a
+// rounding boundary of the code (about one value in 10^5 does), and those
+// values are recomputed with the IEEE division in a loop outside the
+// unrolled fast path.
 #include <hip/hip_runtime.h>
 
 #include "ql_internal.h"
@@ -15,8 +30,8 @@
 namespace ql {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRegPieces = 8;     // 8 x 8 values per thread kept in registers (K <= 16384)
+constexpr int kRowWaves = 4;       // rows (one per wave) per workgroup
+constexpr int kLanePieces = 8;     // 8-value pieces per lane held in registers (K <= 4096)
 
 __device__ inline float half_lo(uint32_t v, bool bf16) {
   return bf16 ? __builtin_bit_cast(float, v << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
@@ -25,261 +40,244 @@ __device__ inline float half_hi(uint32_t v, bool bf16) {
   return bf16 ? __builtin_bit_cast(float, v & 0xFFFF0000u) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
-// FP8: symmetric, s = max(absmax, 1e-5) / 448 and the code is the E4M3
-// rounding of x / s (the largest code maps to the row absmax)
-template <bool BF16, bool ASYM, bool FP8 = false>
-__global__ __launch_bounds__(kThreads) void i8_quant_kernel(const uint16_t* __restrict__ X, int K,
-                                                             int8_t* __restrict__ Aq, float* __restrict__ s_a,
-                                                             int32_t* __restrict__ azp) {
-  __shared__ float red[2][kThreads / 64];
-  const int m = blockIdx.x, tid = threadIdx.x;
-  const uint16_t* x = X + (size_t)m * K;
-  const int pieces = K / 8;
-
-  uint4 v[kRegPieces];
-  float mn = 0.0f, mx = 0.0f;       // the range always contains 0
-  auto fold = [&](uint4 p) {
-    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = half_lo(w[i], BF16), b = half_hi(w[i], BF16);
-      if (ASYM) {
-        mn = fminf(mn, fminf(a, b));
-        mx = fmaxf(mx, fmaxf(a, b));
-      } else {
-        mx = fmaxf(mx, fmaxf(fabsf(a), fabsf(b)));
-      }
-    }
-  };
-#pragma unroll
-  for (int r = 0; r < kRegPieces; ++r) {
-    const int p = tid + r * kThreads;
-    v[r] = p < pieces ? reinterpret_cast<const uint4*>(x)[p] : make_uint4(0, 0, 0, 0);
-    if (p < pieces) fold(v[r]);
-  }
-  for (int p = tid + kRegPieces * kThreads; p < pieces; p += kThreads) fold(reinterpret_cast<const uint4*>(x)[p]);
-
-  // ---- row reduction: wave shuffles, then across the four waves
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = mn;
-    red[1][tid >> 6] = mx;
-  }
-  __syncthreads();
-  mn = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
-  mx = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-
-  float s, z;
-  if (ASYM) {
-    s = fmaxf(mx - mn, 1e-5f) / 255.0f;
-    z = -128.0f - rintf(mn / s);
+// Fast code of y / s from t = y * r (r = 1 / s).  Sets `near` when t lies
+// so close to a rounding boundary that the rounded quotient might fall on the
+// other side; such values are redone with the IEEE division (code_exact).
+// t is within 3 fp32 ulps (relative 1.5 * 2^-23) of the rounded quotient.
+//   int8: |y / s| <= 256; both round alike unless t is within 2^-21 |t| of
+//         a half-integer;
+//   E4M3: both round alike unless t is within 8 ulps of an E4M3 midpoint (low
+//         20 significand bits near 0x80000); t below 2^-6 (the subnormal
+//         codes, a few values in 10^4) always takes the exact path.  On the
+//         fast path 2^-6 <= |t| <= 448 (1 + 2^-21), where the code is the
+//         fp32 significand rounded at bit 20 (ties to even), which stays at
+//         or below the largest code 0x7E.
+template <int MODE>
+__device__ inline uint32_t code_fast(float t, float z, float lo, bool& near) {
+  if constexpr (MODE == 1) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, t);
+    const uint32_t a = b & 0x7FFFFFFFu;
+    const int d = (int)(a & 0xFFFFFu) - 0x80000;
+    near = a < 0x3C800000u || (d <= 8 && d >= -8);
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return ((b >> 24) & 0x80u) | (((r >> 20) - (120u << 3)) & 0x7Fu);   // garbage below 2^-6 stays in its byte
   } else {
-    s = fmaxf(mx, 1e-5f) / (FP8 ? 448.0f : 127.0f);
-    z = 0.0f;
+    const float c = rintf(t);
+    near = fabsf(t - c) >= 0.5f - fabsf(t) * 0x1p-21f;
+    return (uint32_t)(int32_t)__builtin_amdgcn_fmed3f(c + z, lo, 127.0f) & 0xFFu;
   }
-  if (tid == 0) {
-    s_a[m] = s;
-    if (ASYM) azp[m] = (int32_t)z;
-  }
-  const float lo = ASYM ? -128.0f : -127.0f;
-
-  auto quant = [&](uint4 p) -> uint2 {
-    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
-    uint32_t out[2] = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (FP8) {
-        const uint32_t qa = e4m3_code(half_lo(w[i], BF16) / s), qb = e4m3_code(half_hi(w[i], BF16) / s);
-        out[i >> 1] |= (qa | (qb << 8)) << (16 * (i & 1));
-        continue;
-      }
-      const float a = fminf(fmaxf(rintf(half_lo(w[i], BF16) / s) + z, lo), 127.0f);
-      const float b = fminf(fmaxf(rintf(half_hi(w[i], BF16) / s) + z, lo), 127.0f);
-      const uint32_t qa = (uint32_t)(int32_t)a & 0xFFu, qb = (uint32_t)(int32_t)b & 0xFFu;
-      out[i >> 1] |= (qa | (qb << 8)) << (16 * (i & 1));
-    }
-    return make_uint2(out[0], out[1]);
-  };
-  uint2* q = reinterpret_cast<uint2*>(Aq + (size_t)m * K);
-#pragma unroll
-  for (int r = 0; r < kRegPieces; ++r) {
-    const int p = tid + r * kThreads;
-    if (p < pieces) q[p] = quant(v[r]);
-  }
-  for (int p = tid + kRegPieces * kThreads; p < pieces; p += kThreads) q[p] = quant(reinterpret_cast<const uint4*>(x)[p]);
 }
 
-// RMSNorm fused with the per-token quantization (one workgroup per row):
-// the row is normalized and quantized in the same pass over it, so the
-// normalized activations never leave the compute unit ([QK] §9.9: fuse the
-// per-row reduction of the activation quantization with the operator that
-// produces the activations; [LQ] "校准：静态与动态": the dynamic per-token
-// reduction is folded into RMSNorm's kernel).  Per row, in this order:
-//   ms  = fp32( (sum of x^2 in fp64) / K in fp64 )   (the squares are exact)
-//   inv = 1 / sqrt(ms + eps)                          (two correctly rounded fp32 steps)
-//   y   = (x * inv) * gamma                           (fp32, never rounded to 16 bits)
-// then the range of y, its scale / zero point and codes exactly as above.
-template <bool BF16, bool ASYM>
-__global__ __launch_bounds__(kThreads) void rmsnorm_quant_kernel(const uint16_t* __restrict__ X,
-                                                                  const uint16_t* __restrict__ gamma, float eps, int K,
-                                                                  int8_t* __restrict__ Aq, float* __restrict__ s_a,
-                                                                  int32_t* __restrict__ azp) {
-  __shared__ double dred[kThreads / 64];
-  __shared__ float red[2][kThreads / 64];
-  const int m = blockIdx.x, tid = threadIdx.x;
-  const uint16_t* x = X + (size_t)m * K;
-  const uint4* xv = reinterpret_cast<const uint4*>(x);
+template <int MODE>
+__device__ inline uint32_t code_exact(float y, float s, float z, float lo) {
+  if constexpr (MODE == 1)
+    return e4m3_code(y / s);
+  else
+    return (uint32_t)(int32_t)fminf(fmaxf(rintf(y / s) + z, lo), 127.0f) & 0xFFu;
+}
+
+// the 8 values of a piece as fp32, optionally normalized: (x * inv) * gamma
+template <bool BF16, bool NORM>
+__device__ inline void piece_values(uint4 p, uint4 g, float inv, float (&y)[8]) {
+  const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+  const uint32_t u[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[2 * i] = half_lo(w[i], BF16);
+    y[2 * i + 1] = half_hi(w[i], BF16);
+    if constexpr (NORM) {
+      y[2 * i] = (y[2 * i] * inv) * half_lo(u[i], BF16);
+      y[2 * i + 1] = (y[2 * i + 1] * inv) * half_hi(u[i], BF16);
+    }
+  }
+}
+
+// MODE 0: int8 (ASYM selects the zero point); MODE 1: FP8 E4M3 (symmetric,
+// s = max(absmax, 1e-5) / 448, code = E4M3 rounding of x / s).  NORM: the
+// row is first normalized as y = (x * inv) * gamma with
+// inv = 1 / sqrt(fp32(sum of x^2 in fp64 / K) + eps)  ([QK] §9.9: the per-row
+// reduction of the activation quantization fused into the operator that
+// produces the activations; [LQ] "QuaRot：把整个残差流旋转掉" for the form
+// of RMSNorm).
+template <bool BF16, bool ASYM, int MODE, bool NORM>
+__global__ __launch_bounds__(64 * kRowWaves) void quant_rows_kernel(const uint16_t* __restrict__ X,
+                                                                     const uint16_t* __restrict__ gamma, float eps,
+                                                                     int M, int K, int8_t* __restrict__ Aq,
+                                                                     float* __restrict__ s_a,
+                                                                     int32_t* __restrict__ azp) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * kRowWaves + (int)(threadIdx.x >> 6);
+  if (m >= M) return;                            // a whole wave; nothing here synchronizes waves
+  const uint4* xv = reinterpret_cast<const uint4*>(X + (size_t)m * K);
   const uint4* gv = reinterpret_cast<const uint4*>(gamma);
   const int pieces = K / 8;
 
-  // ---- mean square: fp64 sum of the exact squares
-  uint4 v[kRegPieces], g[kRegPieces];
-  double ss = 0.0;
-  auto sq = [&](uint4 p) {
-    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+  // the lane's register-resident pieces, converted to fp32 once (zero past the row)
+  float y[kLanePieces][8];
+  uint4 g[kLanePieces];
+  // every load is issued before the first wait: indices past the row re-read
+  // its last piece (a valid address) and the value is then replaced by zeros
+  uint4 xp[kLanePieces];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double a = half_lo(w[i], BF16), b = half_hi(w[i], BF16);
-      ss += a * a;
-      ss += b * b;
-    }
-  };
-#pragma unroll
-  for (int r = 0; r < kRegPieces; ++r) {
-    const int p = tid + r * kThreads;
-    v[r] = p < pieces ? xv[p] : make_uint4(0, 0, 0, 0);
-    g[r] = p < pieces ? gv[p] : make_uint4(0, 0, 0, 0);
-    if (p < pieces) sq(v[r]);
+  for (int r = 0; r < kLanePieces; ++r) {
+    const int pc = min(lane + 64 * r, pieces - 1);
+    xp[r] = xv[pc];
+    if constexpr (NORM) g[r] = gv[pc];
   }
-  for (int p = tid + kRegPieces * kThreads; p < pieces; p += kThreads) sq(xv[p]);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((tid & 63) == 0) dred[tid >> 6] = ss;
-  __syncthreads();
-  ss = (dred[0] + dred[1]) + (dred[2] + dred[3]);
-  const float ms = (float)(ss / (double)K);
-  const float inv = 1.0f / sqrtf(ms + eps);
+  for (int r = 0; r < kLanePieces; ++r) {
+    const uint32_t keep = lane + 64 * r < pieces ? 0xFFFFFFFFu : 0u;
+    xp[r] = make_uint4(xp[r].x & keep, xp[r].y & keep, xp[r].z & keep, xp[r].w & keep);
+    if constexpr (NORM) g[r] = make_uint4(g[r].x & keep, g[r].y & keep, g[r].z & keep, g[r].w & keep);
+    else g[r] = make_uint4(0, 0, 0, 0);
+    piece_values<BF16, false>(xp[r], xp[r], 1.0f, y[r]);
+  }
 
-  // ---- y and its range
-  auto norm = [&](uint32_t xw, uint32_t gw, float& a, float& b) {
-    a = (half_lo(xw, BF16) * inv) * half_lo(gw, BF16);
-    b = (half_hi(xw, BF16) * inv) * half_hi(gw, BF16);
-  };
-  float mn = 0.0f, mx = 0.0f;       // the range always contains 0
-  auto fold = [&](uint4 p, uint4 q) {
-    const uint32_t w[4] = {p.x, p.y, p.z, p.w}, u[4] = {q.x, q.y, q.z, q.w};
+  // ---- RMSNorm: mean square from the fp64 sum of the exact squares
+  float inv = 1.0f;
+  if constexpr (NORM) {
+    double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a, b;
-      norm(w[i], u[i], a, b);
-      if (ASYM) {
-        mn = fminf(mn, fminf(a, b));
-        mx = fmaxf(mx, fmaxf(a, b));
+    for (int r = 0; r < kLanePieces; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += (double)y[r][i] * (double)y[r][i];
+    for (int p = lane + 64 * kLanePieces; p < pieces; p += 64) {
+      float t[8];
+      piece_values<BF16, false>(xv[p], xv[p], 1.0f, t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += (double)t[i] * (double)t[i];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    ss = __shfl(ss, 0);                          // one value for the whole row
+    const float ms = (float)(ss / (double)K);
+    inv = 1.0f / sqrtf(ms + eps);
+#pragma unroll
+    for (int r = 0; r < kLanePieces; ++r) {
+      const uint32_t u[4] = {g[r].x, g[r].y, g[r].z, g[r].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[r][2 * i] = (y[r][2 * i] * inv) * half_lo(u[i], BF16);
+        y[r][2 * i + 1] = (y[r][2 * i + 1] * inv) * half_hi(u[i], BF16);
+      }
+    }
+  }
+
+  // ---- range of the (normalized) row
+  float mn = 0.0f, mx = 0.0f;                    // the range always contains 0
+  auto fold8 = [&](const float (&t)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (ASYM) {
+        mn = fminf(mn, t[i]);
+        mx = fmaxf(mx, t[i]);
       } else {
-        mx = fmaxf(mx, fmaxf(fabsf(a), fabsf(b)));
+        mx = fmaxf(mx, fabsf(t[i]));
       }
     }
   };
 #pragma unroll
-  for (int r = 0; r < kRegPieces; ++r)
-    if (tid + r * kThreads < pieces) fold(v[r], g[r]);
-  for (int p = tid + kRegPieces * kThreads; p < pieces; p += kThreads) fold(xv[p], gv[p]);
+  for (int r = 0; r < kLanePieces; ++r) fold8(y[r]);         // zero pieces are inside the range
+  for (int p = lane + 64 * kLanePieces; p < pieces; p += 64) {
+    float t[8];
+    piece_values<BF16, NORM>(xv[p], NORM ? gv[p] : make_uint4(0, 0, 0, 0), inv, t);
+    fold8(t);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
+    if constexpr (ASYM) mn = fminf(mn, __shfl_xor(mn, o));
     mx = fmaxf(mx, __shfl_xor(mx, o));
   }
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = mn;
-    red[1][tid >> 6] = mx;
-  }
-  __syncthreads();
-  mn = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
-  mx = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
 
   float s, z;
-  if (ASYM) {
+  if constexpr (ASYM) {
     s = fmaxf(mx - mn, 1e-5f) / 255.0f;
     z = -128.0f - rintf(mn / s);
   } else {
-    s = fmaxf(mx, 1e-5f) / 127.0f;
+    s = fmaxf(mx, 1e-5f) / (MODE == 1 ? 448.0f : 127.0f);
     z = 0.0f;
   }
-  if (tid == 0) {
+  if (lane == 0) {
     s_a[m] = s;
-    if (ASYM) azp[m] = (int32_t)z;
+    if constexpr (ASYM) azp[m] = (int32_t)z;
   }
+  const float rs = 1.0f / s;
   const float lo = ASYM ? -128.0f : -127.0f;
 
-  auto quant = [&](uint4 p, uint4 q) -> uint2 {
-    const uint32_t w[4] = {p.x, p.y, p.z, p.w}, u[4] = {q.x, q.y, q.z, q.w};
-    uint32_t out[2] = {0, 0};
+  auto quant = [&](const float (&t)[8]) -> uint2 {
+    uint32_t out[2] = {0, 0}, fix = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float ya, yb;
-      norm(w[i], u[i], ya, yb);
-      const float a = fminf(fmaxf(rintf(ya / s) + z, lo), 127.0f);
-      const float b = fminf(fmaxf(rintf(yb / s) + z, lo), 127.0f);
-      const uint32_t qa = (uint32_t)(int32_t)a & 0xFFu, qb = (uint32_t)(int32_t)b & 0xFFu;
-      out[i >> 1] |= (qa | (qb << 8)) << (16 * (i & 1));
+    for (int i = 0; i < 8; ++i) {
+      bool near;
+      out[i >> 2] |= code_fast<MODE>(t[i] * rs, z, lo, near) << (8 * (i & 3));
+      fix |= (uint32_t)near << i;
+    }
+    // the rare values next to a rounding boundary: exact division, one at a
+    // time, outside the unrolled fast path
+#pragma nounroll
+    for (; __builtin_expect(fix != 0, 0); fix &= fix - 1) {
+      const int i = __builtin_ctz(fix);
+      float yi = t[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) yi = i == j ? t[j] : yi;
+      const uint32_t sh = 8 * (i & 3), c = code_exact<MODE>(yi, s, z, lo) << sh, keep = ~(0xFFu << sh);
+      if (i < 4)
+        out[0] = (out[0] & keep) | c;
+      else
+        out[1] = (out[1] & keep) | c;
     }
     return make_uint2(out[0], out[1]);
   };
-  uint2* q = reinterpret_cast<uint2*>(Aq + (size_t)m * K);
+  uint2* qo = reinterpret_cast<uint2*>(Aq + (size_t)m * K);
 #pragma unroll
-  for (int r = 0; r < kRegPieces; ++r) {
-    const int p = tid + r * kThreads;
-    if (p < pieces) q[p] = quant(v[r], g[r]);
+  for (int r = 0; r < kLanePieces; ++r) {
+    const int p = lane + 64 * r;
+    if (p < pieces) qo[p] = quant(y[r]);
   }
-  for (int p = tid + kRegPieces * kThreads; p < pieces; p += kThreads) q[p] = quant(xv[p], gv[p]);
+  for (int p = lane + 64 * kLanePieces; p < pieces; p += 64) {
+    float t[8];
+    piece_values<BF16, NORM>(xv[p], NORM ? gv[p] : make_uint4(0, 0, 0, 0), inv, t);
+    qo[p] = quant(t);
+  }
 }
 
-}  // namespace
-
-hipError_t launch_rmsnorm_quant(const void* X, bool bf16, int M, int K, const void* gamma, float eps, int8_t* Aq,
-                                float* s_a, int32_t* azp, hipStream_t st) {
+template <int MODE, bool NORM>
+hipError_t launch_rows(const void* X, bool bf16, int M, int K, const void* gamma, float eps, int8_t* Aq, float* s_a,
+                       int32_t* azp, hipStream_t st) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* g = static_cast<const uint16_t*>(gamma);
+  const dim3 grid((M + kRowWaves - 1) / kRowWaves), block(64 * kRowWaves);
   if (bf16) {
     if (azp)
-      hipLaunchKernelGGL((rmsnorm_quant_kernel<true, true>), dim3(M), dim3(kThreads), 0, st, x, g, eps, K, Aq, s_a, azp);
+      hipLaunchKernelGGL((quant_rows_kernel<true, true, MODE, NORM>), grid, block, 0, st, x, g, eps, M, K, Aq, s_a, azp);
     else
-      hipLaunchKernelGGL((rmsnorm_quant_kernel<true, false>), dim3(M), dim3(kThreads), 0, st, x, g, eps, K, Aq, s_a, azp);
+      hipLaunchKernelGGL((quant_rows_kernel<true, false, MODE, NORM>), grid, block, 0, st, x, g, eps, M, K, Aq, s_a,
+                         azp);
   } else {
     if (azp)
-      hipLaunchKernelGGL((rmsnorm_quant_kernel<false, true>), dim3(M), dim3(kThreads), 0, st, x, g, eps, K, Aq, s_a, azp);
+      hipLaunchKernelGGL((quant_rows_kernel<false, true, MODE, NORM>), grid, block, 0, st, x, g, eps, M, K, Aq, s_a,
+                         azp);
     else
-      hipLaunchKernelGGL((rmsnorm_quant_kernel<false, false>), dim3(M), dim3(kThreads), 0, st, x, g, eps, K, Aq, s_a,
+      hipLaunchKernelGGL((quant_rows_kernel<false, false, MODE, NORM>), grid, block, 0, st, x, g, eps, M, K, Aq, s_a,
                          azp);
   }
   return hipGetLastError();
 }
 
+}  // namespace
+
 hipError_t launch_i8_quant(const void* X, bool bf16, int M, int K, int8_t* Aq, float* s_a, int32_t* azp,
                            hipStream_t st) {
-  const uint16_t* x = static_cast<const uint16_t*>(X);
-  if (bf16) {
-    if (azp) hipLaunchKernelGGL((i8_quant_kernel<true, true>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
-    else hipLaunchKernelGGL((i8_quant_kernel<true, false>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
-  } else {
-    if (azp) hipLaunchKernelGGL((i8_quant_kernel<false, true>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
-    else hipLaunchKernelGGL((i8_quant_kernel<false, false>), dim3(M), dim3(kThreads), 0, st, x, K, Aq, s_a, azp);
-  }
-  return hipGetLastError();
+  return launch_rows<0, false>(X, bf16, M, K, nullptr, 0.0f, Aq, s_a, azp, st);
+}
+
+hipError_t launch_rmsnorm_quant(const void* X, bool bf16, int M, int K, const void* gamma, float eps, int8_t* Aq,
+                                float* s_a, int32_t* azp, hipStream_t st) {
+  return launch_rows<0, true>(X, bf16, M, K, gamma, eps, Aq, s_a, azp, st);
 }
 
 hipError_t launch_f8_quant(const void* X, bool bf16, int M, int K, uint8_t* Aq, float* s_a, hipStream_t st) {
-  const uint16_t* x = static_cast<const uint16_t*>(X);
-  int8_t* q = reinterpret_cast<int8_t*>(Aq);
-  if (bf16)
-    hipLaunchKernelGGL((i8_quant_kernel<true, false, true>), dim3(M), dim3(kThreads), 0, st, x, K, q, s_a, nullptr);
-  else
-    hipLaunchKernelGGL((i8_quant_kernel<false, false, true>), dim3(M), dim3(kThreads), 0, st, x, K, q, s_a, nullptr);
-  return hipGetLastError();
+  return launch_rows<1, false>(X, bf16, M, K, nullptr, 0.0f, reinterpret_cast<int8_t*>(Aq), s_a, nullptr, st);
 }
 
 }  // namespace ql

@@ -59,16 +59,19 @@ inline int nib_pos(int i) { return (i & 1) * 4 + (i >> 1); }
 // 448): round to nearest, ties to even, saturating at +-448.  Normal results
 // round the fp32 significand at its bit 20 (the carry moves into the
 // exponent); below 2^-6 the grid is 2^-9 and v * 512 is rounded exactly.
+// Written with selects only (both roundings are computed, the range picks
+// one), so an unrolled loop of codes stays straight-line code.
 __host__ __device__ inline uint32_t e4m3_code(float v) {
   const uint32_t b = __builtin_bit_cast(uint32_t, v);
   const uint32_t sign = (b >> 24) & 0x80u;
   const uint32_t a = b & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;                 // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;                 // |v| >= 448: saturate
-  if (a < 0x3C800000u)                                       // |v| < 2^-6
-    return sign | (uint32_t)rintf(__builtin_bit_cast(float, a) * 512.0f);
   const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-  return sign | ((r >> 20) - (120u << 3));
+  const uint32_t normal = (r >> 20) - (120u << 3);
+  const float sub = rintf(__builtin_bit_cast(float, a < 0x3C800000u ? a : 0u) * 512.0f);   // |v| < 2^-6
+  uint32_t c = a < 0x3C800000u ? (uint32_t)sub : normal;
+  c = a >= 0x43E00000u ? 0x7Eu : c;                          // |v| >= 448: saturate
+  c = a > 0x7F800000u ? 0x7Fu : c;                           // NaN
+  return sign | c;
 }
 
 // ---------------------------------------------------------------- launch plans
