@@ -142,3 +142,58 @@ def w4a16_linear(X, q, s16, z, group=GROUP):
     """
     Wd = dequantize_w4(q, s16, z, group)
     return np.asarray(X, np.float64) @ Wd.T
+
+
+# ---------------------------------------------------------------- act-order (g_idx)
+
+def g_idx_from_order(order, group=GROUP):
+    """Group index of every input channel when channels are quantized in the
+    given order ([LQ] GPTQ section, "工程细节" (engineering details), its
+    act-order item: channels are processed in decreasing activation energy,
+    groups are formed along that processing order, and g_idx records the group
+    of each input channel).  order: a permutation of range(K); channel
+    order[j] lands in group j // group.  Returns int64 [K]."""
+    order = np.asarray(order, np.int64)
+    K = order.size
+    if sorted(order.tolist()) != list(range(K)):
+        raise ValueError("order must be a permutation of range(K)")
+    g = np.empty(K, np.int64)
+    g[order] = np.arange(K) // group
+    return g
+
+
+def quantize_w4_act_order(W, g_idx, group=GROUP):
+    """quantize_w4 with the groups given by g_idx instead of consecutive runs
+    of K: group j holds the input channels k with g_idx[k] == j, and its
+    (s16, z) come from those channels' weights by the same fp32 formulas.
+
+    W: [N, K]; g_idx: int [K] with values 0..K/group-1.  Returns q uint8
+    [N, K] (original channel order), s16 float16 [K/group, N], z uint8
+    [K/group, N]."""
+    W = np.asarray(W, np.float32)
+    N, K = W.shape
+    g_idx = np.asarray(g_idx, np.int64)
+    G = K // group
+    q = np.zeros((N, K), np.uint8)
+    s16 = np.zeros((G, N), np.float16)
+    z = np.zeros((G, N), np.uint8)
+    for j in range(G):
+        ch = np.nonzero(g_idx == j)[0]
+        qj, sj, zj = quantize_w4(W[:, ch], group=len(ch))
+        q[:, ch] = qj
+        s16[j], z[j] = sj[0], zj[0]
+    return q, s16, z
+
+
+def dequantize_w4_gidx(q, s16, z, g_idx):
+    """x_hat[n, k] = s[g_idx[k], n] * (q[n, k] - z[g_idx[k], n]) in fp64 (the
+    non-contiguous scale reads the act-order item describes)."""
+    g_idx = np.asarray(g_idx, np.int64)
+    s = np.asarray(s16, np.float64)[g_idx, :].T
+    zz = np.asarray(z, np.float64)[g_idx, :].T
+    return s * (np.asarray(q, np.float64) - zz)
+
+
+def w4a16_linear_gidx(X, q, s16, z, g_idx):
+    """Y64 = X · dequant_gidx(W)ᵀ in fp64."""
+    return np.asarray(X, np.float64) @ dequantize_w4_gidx(q, s16, z, g_idx).T

@@ -414,3 +414,57 @@ def test_rmsnorm_quant_is_the_per_token_quant_of_y():
     assert np.all(np.abs(deq - y) <= 0.5 * s_a[:, None] * (1 + 1e-6))
     Aqs, ss = rn.rmsnorm_quant_per_token(X, gamma, 1e-6, asym=False)
     assert np.all(np.abs(Aqs.astype(np.int32)).max(axis=1) == 127)
+
+
+# ---------------------------------------------------------------- act-order (g_idx)
+
+def test_act_order_identity_order_is_the_plain_path():
+    from oracle import w4a16 as w4
+    r = np.random.default_rng(21)
+    W = (r.standard_normal((24, 384)) * 0.02).astype(np.float32)
+    X = r.standard_normal((3, 384))
+    g = w4.g_idx_from_order(np.arange(384))
+    assert np.array_equal(g, np.arange(384) // 128)
+    qa, sa, za = w4.quantize_w4_act_order(W, g)
+    q, s, z = w4.quantize_w4(W)
+    assert np.array_equal(qa, q) and np.array_equal(sa.view(np.uint16), s.view(np.uint16)) and np.array_equal(za, z)
+    np.testing.assert_array_equal(w4.w4a16_linear_gidx(X, qa, sa, za, g), w4.w4a16_linear(X, q, s, z))
+
+
+def test_act_order_equals_plain_path_on_permuted_channels():
+    # quantizing in order P == plain grouping of W[:, P]; the product is the
+    # same with X[:, P]
+    from oracle import w4a16 as w4
+    r = np.random.default_rng(22)
+    K = 512
+    W = (r.standard_normal((16, K)) * 0.02).astype(np.float32)
+    X = r.standard_normal((4, K))
+    P = r.permutation(K)
+    g = w4.g_idx_from_order(P)
+    qa, sa, za = w4.quantize_w4_act_order(W, g)
+    q, s, z = w4.quantize_w4(W[:, P])
+    assert np.array_equal(qa[:, P], q) and np.array_equal(sa.view(np.uint16), s.view(np.uint16))
+    assert np.array_equal(za, z)
+    np.testing.assert_allclose(w4.w4a16_linear_gidx(X, qa, sa, za, g), w4.w4a16_linear(X[:, P], q, s, z),
+                               rtol=1e-12, atol=1e-12)
+    # every group holds exactly `group` channels and g_idx inverts the order
+    assert np.all(np.bincount(g) == 128)
+    assert np.all(g[P] == np.arange(K) // 128)
+
+
+def test_act_order_brute_force_tiny():
+    # one output channel, K = 256: the product written out channel by channel
+    from oracle import w4a16 as w4
+    r = np.random.default_rng(23)
+    K = 256
+    W = (r.standard_normal((1, K)) * 0.05).astype(np.float32)
+    x = r.standard_normal(K)
+    P = r.permutation(K)
+    g = w4.g_idx_from_order(P)
+    q, s, z = w4.quantize_w4_act_order(W, g)
+    want = sum(x[k] * float(s[g[k], 0]) * (int(q[0, k]) - int(z[g[k], 0])) for k in range(K))
+    got = w4.w4a16_linear_gidx(x[None], q, s, z, g)[0, 0]
+    assert abs(got - want) <= 1e-12 * max(1.0, abs(want))
+    # a wrong channel-to-group map changes the result
+    g_bad = np.roll(g, 1)
+    assert abs(w4.w4a16_linear_gidx(x[None], q, s, z, g_bad)[0, 0] - want) > 1e-6
