@@ -45,7 +45,7 @@ MALL_DEFEAT_BYTES = 1 << 30
 # same run.  It belongs to one version of the kernel source: when the source
 # hash differs, the figure is stale and `traffic` is reported as null.
 TRAFFIC = {"source_sha256": "da8e171ba218a270af66a1ee6ed615db6461c57465ef06b5e42e2166d3111fa2",
-           "bytes_per_launch": 19395555}
+           "bytes_per_launch": 19395521}
 
 
 def w4a16_bytes(M, K, N, group=128, e=2):

@@ -193,6 +193,54 @@ int q4_unpack(const void* packed, size_t packed_bytes, int N, int K, int group,
 int q4_gemm(const void* X, int x_dtype, int M, int K, int N,
             const void* packed, size_t packed_bytes, int group, void* Y, void* stream);
 
+/* -------------------------------------------------------------------------
+ * Act-order (g_idx).  [LQ] GPTQ section, "工程细节", its act-order item:
+ * input channels are quantized in decreasing activation energy, groups are
+ * formed along that processing order, and g_idx[k] records the group of
+ * input channel k, so the scale of a channel is no longer found at k / group.
+ * Here the blob is stored in processing order (every group is again a run of
+ * `group` channels) together with the permutation perm (perm[j] = the
+ * original channel at position j), and the activations are permuted once per
+ * call: Y = X · Wᵀ = Xp · Wpᵀ with Xp[m][j] = X[m][perm[j]].  Forward:
+ * q4_permute_columns(X → Xp), then q4_gemm(Xp, blob).
+ * ------------------------------------------------------------------------- */
+
+/*
+ * q4_quantize_act_order_host — q4_quantize_host with the groups given by
+ * g_idx (host): group g holds the channels k with g_idx[k] == g, and its
+ * (scale, zero) come from those channels' weights by the same formulas.
+ * g_idx [K] int32: every value in [0, K/group) and every group holding
+ * exactly `group` channels.  wq / scales / zeros as q4_quantize_host (codes in
+ * the original channel order, scales and zeros indexed by group).
+ * Errors: as q4_quantize_host; QL_ERR_RANGE for an invalid g_idx.
+ */
+int q4_quantize_act_order_host(const float* W, int N, int K, int group, const int32_t* g_idx,
+                               uint32_t* wq, uint16_t* scales, uint8_t* zeros);
+
+/*
+ * q4_pack_act_order — q4_pack of the codes reordered into processing order
+ * (host).  perm [K] int32 out: perm[j] = the channel whose code sits at
+ * position j (the channels of group g, ascending, at positions g·group ..
+ * g·group + group − 1).  Copy perm to the device for q4_permute_columns.
+ * Errors: as q4_pack; QL_ERR_NULL also for g_idx or perm; QL_ERR_RANGE for an
+ *         invalid g_idx.
+ */
+int q4_pack_act_order(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros,
+                      const int32_t* g_idx, int N, int K, int group,
+                      void* packed, size_t packed_bytes, int32_t* perm);
+
+/*
+ * q4_permute_columns — Xp[m][j] = X[m][perm[j]] (device), the activations in
+ * the blob's channel order.  X and Xp [M][K] fp16/bf16 (distinct buffers);
+ * perm [K] int32 on the device (values outside [0, K) are clamped: wrong
+ * output, never an out-of-bounds read).  M == 0 is a no-op.
+ * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M >= 0, K > 0 and
+ *         K % 8 == 0; QL_ERR_UNSUPPORTED if M > 65535 or X == Xp;
+ *         QL_ERR_ALIGN; QL_ERR_HIP.
+ */
+int q4_permute_columns(const void* X, int x_dtype, int M, int K, const int32_t* perm,
+                       void* Xp, void* stream);
+
 /* =========================================================================
  * W8A8
  * ========================================================================= */

@@ -44,6 +44,9 @@ def lib():
             "q4_pack": (I, [P, P, P, I, I, I, P, Z]),
             "q4_unpack": (I, [P, Z, I, I, I, P, P, P]),
             "q4_gemm": (I, [P, I, I, I, I, P, Z, I, P, P]),
+            "q4_quantize_act_order_host": (I, [P, I, I, I, P, P, P, P]),
+            "q4_pack_act_order": (I, [P, P, P, P, I, I, I, P, Z, P]),
+            "q4_permute_columns": (I, [P, I, I, I, P, P, P]),
             "i8_quant_weight_host": (I, [P, I, I, P, P]),
             "i8_azp_adj": (I, [P, I, I, P]),
             "i8_quant_per_token": (I, [P, I, I, I, P, P, P, P]),
@@ -165,6 +168,60 @@ def q4_gemm(X, packed, N, group=GROUP, Y=None, stream=None):
     _check(lib().q4_gemm(_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group, _ptr(Y),
                          _stream(X, stream)), "q4_gemm")
     return Y
+
+
+# ---------------------------------------------------------------- act-order (g_idx)
+
+def q4_quantize_act_order_host(W, g_idx, group=GROUP):
+    """W: CPU fp32 [N, K], g_idx: CPU int32 [K] -> (wq, scales, zeros) as q4_quantize_host, with the
+    groups given by g_idx."""
+    W = _host(W, torch.float32)
+    g_idx = _host(g_idx, torch.int32)
+    N, K = W.shape
+    wq = torch.empty((K // 8, N), dtype=torch.int32)
+    scales = torch.empty((K // group, N), dtype=torch.float16)
+    zeros = torch.empty((K // group, N), dtype=torch.uint8)
+    _check(lib().q4_quantize_act_order_host(_ptr(W), N, K, group, _ptr(g_idx), _ptr(wq), _ptr(scales), _ptr(zeros)),
+           "q4_quantize_act_order_host")
+    return wq, scales, zeros
+
+
+def q4_pack_act_order(wq, scales, zeros, g_idx, N, K, group=GROUP, device=None):
+    """Canonical triple + g_idx -> (blob in processing order, perm int32 [K]), both on `device`."""
+    wq = _host(wq, torch.int32)
+    scales = _host(scales, torch.float16)
+    if zeros is not None:
+        zeros = _host(zeros, torch.uint8)
+    g_idx = _host(g_idx, torch.int32)
+    nb = q4_packed_bytes(N, K, group)
+    if nb == 0:
+        raise QLError(f"q4_pack_act_order: invalid shape N={N} K={K} group={group}")
+    blob = torch.empty(nb, dtype=torch.uint8)
+    perm = torch.empty(K, dtype=torch.int32)
+    _check(lib().q4_pack_act_order(_ptr(wq), _ptr(scales), _ptr(zeros), _ptr(g_idx), N, K, group, _ptr(blob), nb,
+                                   _ptr(perm)), "q4_pack_act_order")
+    return (blob, perm) if device is None else (blob.to(device), perm.to(device))
+
+
+def q4_permute_columns(X, perm, Xp=None, stream=None):
+    """Xp[m, j] = X[m, perm[j]] on the device (the activations in the blob's channel order)."""
+    X = _dev(X, name="X")
+    _dev(perm, torch.int32, "perm")
+    M, K = X.shape
+    if perm.numel() != K:
+        raise QLError(f"q4_permute_columns: perm has {perm.numel()} entries, expected {K}")
+    if Xp is None:
+        Xp = torch.empty_like(X)
+    else:
+        _dev(Xp, X.dtype, "Xp")
+    _check(lib().q4_permute_columns(_ptr(X), _dtype_code(X.dtype), M, K, _ptr(perm), _ptr(Xp), _stream(X, stream)),
+           "q4_permute_columns")
+    return Xp
+
+
+def q4_gemm_act_order(X, packed, perm, N, group=GROUP, Y=None, stream=None):
+    """Y = X · dequant(W)ᵀ for an act-order blob: q4_permute_columns, then q4_gemm."""
+    return q4_gemm(q4_permute_columns(X, perm, stream=stream), packed, N, group, Y, stream)
 
 
 def q4_gemm_launcher(X, packed, N, Y, group=GROUP, stream=None):

@@ -32,6 +32,7 @@ SOURCES = {
     "q4_gemm.hip": [],
     "i8_quant.hip": ["-ffp-contract=off"],
     "i8_gemm.hip": [],
+    "act_order.hip": [],
 }
 
 

@@ -74,6 +74,20 @@ int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed,
   return hip_status("q4_gemm", ql::launch_q4_gemm(X, bf16, M, K, N, static_cast<const uint8_t*>(packed), L, Y, st));
 }
 
+int q4_permute_columns(const void* X, int x_dtype, int M, int K, const int32_t* perm, void* Xp, void* stream) {
+  if (M < 0 || K <= 0 || K % 8)
+    return ql::set_error(QL_ERR_SHAPE, "q4_permute_columns: need M >= 0, K > 0, K %% 8 == 0 (got %d, %d)", M, K);
+  if (!valid_dtype(x_dtype)) return ql::set_error(QL_ERR_DTYPE, "q4_permute_columns: x_dtype=%d", x_dtype);
+  if (M == 0) return QL_OK;
+  if (M > 65535) return ql::set_error(QL_ERR_UNSUPPORTED, "q4_permute_columns: M=%d exceeds 65535 rows per call", M);
+  if (!X || !perm || !Xp) return ql::set_error(QL_ERR_NULL, "q4_permute_columns: NULL X, perm or Xp");
+  if (!aligned16(X) || !aligned16(perm) || !aligned16(Xp))
+    return ql::set_error(QL_ERR_ALIGN, "q4_permute_columns: pointers must be 16-byte aligned");
+  if (X == Xp) return ql::set_error(QL_ERR_UNSUPPORTED, "q4_permute_columns: X and Xp must not be the same buffer");
+  return hip_status("q4_permute_columns",
+                    ql::launch_permute_cols(X, M, K, perm, Xp, static_cast<hipStream_t>(stream)));
+}
+
 int i8_quant_per_token(const void* X, int x_dtype, int M, int K, int8_t* Aq, float* s_a, int32_t* azp,
                        void* stream) {
   if (M < 0 || K <= 0 || K % 8)

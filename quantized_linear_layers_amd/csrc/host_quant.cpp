@@ -73,6 +73,25 @@ inline size_t s_byte(const ql::Q4Layout& L, int n, int g) {
 }
 inline size_t z_byte(const ql::Q4Layout& L, int n, int g) { return L.z_off + (size_t)(g / 2) * L.Np + n; }
 
+// Channels of every group in ascending order, from a group index per input
+// channel; every group must hold exactly `group` channels (the act-order
+// layout: groups are runs of `group` channels of the processing order).
+int order_from_g_idx(const char* fn, const int32_t* g_idx, int K, int group, int32_t* order) {
+  const int G = K / group;
+  int* fill = new int[G]();
+  for (int k = 0; k < K; ++k) {
+    const int g = g_idx[k];
+    if (g < 0 || g >= G || fill[g] >= group) {
+      delete[] fill;
+      return ql::set_error(QL_ERR_RANGE, "%s: g_idx[%d]=%d is out of range or its group holds more than %d channels",
+                           fn, k, g, group);
+    }
+    order[(size_t)g * group + fill[g]++] = k;
+  }
+  delete[] fill;
+  return QL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,6 +163,56 @@ int q4_quantize_sym_host(const float* W, int N, int K, int group, uint32_t* wq, 
   return QL_OK;
 }
 
+int q4_quantize_act_order_host(const float* W, int N, int K, int group, const int32_t* g_idx, uint32_t* wq,
+                               uint16_t* scales, uint8_t* zeros) {
+  if (!W || !g_idx || !wq || !scales || !zeros)
+    return ql::set_error(QL_ERR_NULL, "q4_quantize_act_order_host: NULL pointer");
+  if (int e = check_q4_shape("q4_quantize_act_order_host", N, K, group)) return e;
+  int32_t* order = new int32_t[K];
+  if (int e = order_from_g_idx("q4_quantize_act_order_host", g_idx, K, group, order)) {
+    delete[] order;
+    return e;
+  }
+  const int G = K / group;
+  memset(wq, 0, sizeof(uint32_t) * (size_t)(K / 8) * N);
+  int rc = QL_OK;
+  for (int n = 0; n < N && rc == QL_OK; ++n) {
+    const float* w = W + (size_t)n * K;
+    for (int g = 0; g < G && rc == QL_OK; ++g) {
+      const int32_t* ch = order + (size_t)g * group;
+      float mn = 0.0f, mx = 0.0f;
+      for (int i = 0; i < group; ++i) {
+        const float v = w[ch[i]];
+        if (!(v == v) || isinf(v)) {
+          rc = ql::set_error(QL_ERR_RANGE, "q4_quantize_act_order_host: W[%d][%d] is not finite", n, ch[i]);
+          break;
+        }
+        mn = std::min(mn, v);
+        mx = std::max(mx, v);
+      }
+      if (rc != QL_OK) break;
+      float range = mx - mn;
+      if (range < 1e-5f) range = 1e-5f;
+      const uint16_t sb = f32_to_f16_bits(range / 15.0f);
+      if ((sb & 0x7C00u) == 0x7C00u) {
+        rc = ql::set_error(QL_ERR_RANGE, "q4_quantize_act_order_host: group (%d,%d) overflows the fp16 scale", n, g);
+        break;
+      }
+      const float sc = f16_bits_to_f32(sb);
+      const float z = std::min(std::max(rintf(-mn / sc), 0.0f), 15.0f);
+      scales[(size_t)g * N + n] = sb;
+      zeros[(size_t)g * N + n] = (uint8_t)z;
+      for (int i = 0; i < group; ++i) {
+        const int k = ch[i];
+        const float q = std::min(std::max(rintf(w[k] / sc) + z, 0.0f), 15.0f);
+        wq[(size_t)(k / 8) * N + n] |= (uint32_t)q << (4 * (k % 8));
+      }
+    }
+  }
+  delete[] order;
+  return rc;
+}
+
 size_t q4_packed_bytes(int N, int K, int group) {
   if (N <= 0 || K <= 0 || group != ql::kGroup || K % group) return 0;
   return ql::q4_layout(N, K).bytes;
@@ -183,6 +252,24 @@ int q4_pack(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros, in
     }
   }
   return QL_OK;
+}
+
+int q4_pack_act_order(const uint32_t* wq, const uint16_t* scales, const uint8_t* zeros, const int32_t* g_idx, int N,
+                      int K, int group, void* packed, size_t packed_bytes, int32_t* perm) {
+  if (!wq || !scales || !g_idx || !packed || !perm) return ql::set_error(QL_ERR_NULL, "q4_pack_act_order: NULL pointer");
+  if (int e = check_q4_shape("q4_pack_act_order", N, K, group)) return e;
+  if (int e = order_from_g_idx("q4_pack_act_order", g_idx, K, group, perm)) return e;
+  // the codes in processing order: position j holds channel perm[j]
+  uint32_t* wp = new uint32_t[(size_t)(K / 8) * N]();
+  for (int j = 0; j < K; ++j) {
+    const int k = perm[j];
+    const uint32_t* src = wq + (size_t)(k / 8) * N;
+    uint32_t* dst = wp + (size_t)(j / 8) * N;
+    for (int n = 0; n < N; ++n) dst[n] |= ((src[n] >> (4 * (k % 8))) & 0xFu) << (4 * (j % 8));
+  }
+  const int rc = q4_pack(wp, scales, zeros, N, K, group, packed, packed_bytes);
+  delete[] wp;
+  return rc;
 }
 
 int q4_unpack(const void* packed, size_t packed_bytes, int N, int K, int group, uint32_t* wq,

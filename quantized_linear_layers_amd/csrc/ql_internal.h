@@ -93,6 +93,7 @@ hipError_t launch_q4_gemv(const void* X, bool bf16, int M, int K, int N,
 hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N,
                           const uint8_t* blob, const Q4Layout& L, void* Y, hipStream_t st);
 
+hipError_t launch_permute_cols(const void* X, int M, int K, const int32_t* perm, void* Xp, hipStream_t st);
 hipError_t launch_rmsnorm_quant(const void* X, bool bf16, int M, int K, const void* gamma, float eps, int8_t* Aq,
                                 float* s_a, int32_t* azp, hipStream_t st);
 hipError_t launch_i8_quant(const void* X, bool bf16, int M, int K, int8_t* Aq, float* s_a,

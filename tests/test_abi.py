@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -246,3 +246,61 @@ def test_q4_symmetric_quantize_and_pack_vs_oracle():
     assert torch.equal(wq2, wq) and torch.equal(s2.view(torch.int16), s.view(torch.int16))
     assert np.array_equal(z2.numpy(), z_o)             # every zero point is 8
     assert ql.lib().q4_quantize_sym_host(None, 4, 128, 128, FAKE, FAKE) == QL_ERR_NULL
+
+
+def _act_order_case(K=1024, N=96, seed=31):
+    r = np.random.default_rng(seed)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    energy = r.standard_normal(K) ** 2                 # a stand-in for the activation energy diag(H)
+    order = np.argsort(-energy, kind="stable")
+    return W, ow4.g_idx_from_order(order).astype(np.int32)
+
+
+def test_q4_act_order_quantize_and_pack_vs_oracle():
+    W, g = _act_order_case()
+    N, K = W.shape
+    wq, s, z = ql.q4_quantize_act_order_host(torch.from_numpy(W), torch.from_numpy(g))
+    q_o, s_o, z_o = ow4.quantize_w4_act_order(W, g)
+    assert np.array_equal(wq.numpy().view(np.uint32), ow4.pack_canonical(q_o))
+    assert np.array_equal(s.numpy().view(np.uint16), s_o.view(np.uint16))
+    assert np.array_equal(z.numpy(), z_o)
+    blob, perm = ql.q4_pack_act_order(wq, s, z, torch.from_numpy(g), N, K)
+    perm = perm.numpy()
+    # perm lists each group's channels, ascending, group after group
+    assert np.array_equal(np.sort(perm), np.arange(K))
+    assert np.all(g[perm] == np.arange(K) // 128)
+    for j in range(K // 128):
+        assert np.all(np.diff(perm[128 * j:128 * (j + 1)]) > 0)
+    # the blob holds the codes in processing order with the groups' own scales and zeros
+    wq2, s2, z2 = ql.q4_unpack(blob, N, K)
+    assert np.array_equal(wq2.numpy().view(np.uint32), ow4.pack_canonical(q_o[:, perm]))
+    assert torch.equal(s2.view(torch.int16), s.view(torch.int16)) and torch.equal(z2, z)
+
+
+def test_q4_act_order_validation():
+    L = ql.lib()
+    W, g = _act_order_case(K=256, N=8)
+    wq = np.zeros((32, 8), np.int32)
+    sc = np.zeros((2, 8), np.float16)
+    z = np.zeros((2, 8), np.uint8)
+    perm = np.zeros(256, np.int32)
+    blob = np.zeros(L.q4_packed_bytes(8, 256, 128), np.uint8)
+    ptr = lambda a: a.ctypes.data_as(C.c_void_p)
+    bad = g.copy()
+    bad[0] = 2                                          # group index out of range
+    assert L.q4_pack_act_order(ptr(wq), ptr(sc), ptr(z), ptr(bad), 8, 256, 128, ptr(blob), blob.size,
+                               ptr(perm)) == QL_ERR_RANGE
+    bad = g.copy()
+    bad[np.nonzero(g == 0)[0][0]] = 1                  # group 1 would hold 129 channels
+    assert L.q4_pack_act_order(ptr(wq), ptr(sc), ptr(z), ptr(bad), 8, 256, 128, ptr(blob), blob.size,
+                               ptr(perm)) == QL_ERR_RANGE
+    assert L.q4_quantize_act_order_host(ptr(W), 8, 256, 128, ptr(bad), ptr(wq), ptr(sc), ptr(z)) == QL_ERR_RANGE
+    assert L.q4_pack_act_order(ptr(wq), ptr(sc), ptr(z), None, 8, 256, 128, ptr(blob), blob.size,
+                               ptr(perm)) == QL_ERR_NULL
+    P = FAKE
+    assert L.q4_permute_columns(P, 0, 4, 12, P, P, None) == QL_ERR_SHAPE
+    assert L.q4_permute_columns(P, 4, 4, 16, P, P, None) == QL_ERR_DTYPE
+    assert L.q4_permute_columns(None, 0, 4, 16, P, P, None) == QL_ERR_NULL
+    assert L.q4_permute_columns(P, 0, 4, 16, P, FAKE_MIS, None) == QL_ERR_ALIGN
+    assert L.q4_permute_columns(P, 0, 4, 16, P, P, None) == QL_ERR_UNSUPPORTED      # X == Xp
+    assert L.q4_permute_columns(None, 0, 0, 16, None, None, None) == QL_OK

@@ -181,3 +181,32 @@ def test_symmetric_codes(M, K, N, dtype):
     q, s_o, z = ow4.quantize_w4_sym(W)
     Y64 = ow4.w4a16_linear(wl.as_f64(X), q, s_o, z)
     assert rel_err(wl.as_f64(Y.cpu()), Y64) <= TOL
+
+
+# ---------------------------------------------------------------- act-order (g_idx)
+
+def _act_order_layer(K, N, seed):
+    r = np.random.default_rng(seed)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    order = np.argsort(-(r.standard_normal(K) ** 2), kind="stable")   # decreasing stand-in energy
+    return W, ow4.g_idx_from_order(order).astype(np.int32)
+
+
+@pytest.mark.parametrize("M,K,N,dtype", [(1, 4096, 4096, torch.float16), (5, 1152, 1000, torch.bfloat16),
+                                         (16, 4096, 11008, torch.float16), (64, 2560, 640, torch.bfloat16),
+                                         (300, 1024, 768, torch.float16)])
+def test_act_order(M, K, N, dtype):
+    W, g = _act_order_layer(K, N, M + K + N)
+    wq, s, z = ql.q4_quantize_act_order_host(torch.from_numpy(W), torch.from_numpy(g))
+    blob, perm = ql.q4_pack_act_order(wq, s, z, torch.from_numpy(g), N, K, device="cuda")
+    X = torch.from_numpy(np.random.default_rng(M).standard_normal((M, K)).astype(np.float32)).to(dtype)
+    Xd = X.cuda()
+    Xp = ql.q4_permute_columns(Xd, perm)
+    Y = ql.q4_gemm_act_order(Xd, blob, perm, N)
+    torch.cuda.synchronize()
+    # the permutation is a pure gather: bit-exact
+    assert torch.equal(Xp.cpu(), X[:, torch.from_numpy(perm.cpu().numpy().astype(np.int64))])
+    q, s_o, z_o = ow4.quantize_w4_act_order(W, g)
+    Y64 = ow4.w4a16_linear_gidx(wl.as_f64(X), q, s_o, z_o, g)
+    e = rel_err(wl.as_f64(Y.cpu()), Y64)
+    assert e <= TOL, f"relative error {e:.3e}"
