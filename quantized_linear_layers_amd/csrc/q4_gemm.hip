@@ -1,4 +1,6 @@
-// W4A16 GEMM for large M (prefill): Y = X · dequant(W)ᵀ on 16-bit MFMA.
+// W4A16 GEMM for M > 16 (batched decode to prefill): Y = X · dequant(W)ᵀ on
+// 16-bit MFMA.  Described here for the prefill tile; the tile configurations
+// for fewer tokens (Cfg below) split K among the waves instead.
 //
 // With many tokens the layer is compute-bound ([LQ] "带宽与算力：Roofline":
 // the arithmetic intensity grows with the token count), and the dequant is
@@ -14,7 +16,7 @@
 //     workgroup;
 //   * K advances in blocks of 64 through a ring of 3 LDS stages filled by
 //     global_load_lds (no register staging), two blocks ahead: the X tile
-//     (shared by the 4 waves; 16-byte pieces XOR-swizzled by row so the MFMA
+//     (shared by the 8 waves; 16-byte pieces XOR-swizzled by row so the MFMA
 //     operand reads spread over the banks), and per wave its still-packed
 //     weight chunks and the group's scale and zero-point words;
 //   * the codes stay packed until they are in registers ([QK] §9.5) and are
