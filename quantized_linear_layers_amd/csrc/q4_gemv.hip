@@ -25,17 +25,24 @@
 //     operation, so one counter wait per group covers them and nothing else
 //     waits on the prefetch; the activation rows of a group are read from LDS
 //     once and used for all NT slices;
-//   * the codes stay packed until they are in registers ([QK] §9.5): an AND
-//     with 0x000F000F and an OR with the bit pattern of fp16 1024.0 (0x6400)
-//     or bf16 128.0 (0x4300) turns a pair of nibbles into the exact pair
-//     (off + q0, off + q1) ([QK] §9.6);
+//   * the codes stay packed until they are in registers ([QK] §9.5): one
+//     v_and_or_b32 per register (the mask 0x000F000F and the bit pattern of
+//     fp16 1024.0 (0x6400) or bf16 128.0 (0x4300) held in registers, since a
+//     three-operand instruction takes no 32-bit literal here) turns a pair of
+//     nibbles into the exact pair (off + q0, off + q1) ([QK] §9.6);
 //   * the 16-bit products and their fp32 sums run on the matrix unit
 //     (v_mfma_f32_16x16x32_{f16,bf16}, one row per token, up to 16 tokens),
 //     which leaves the vector ALU to the unpacking; the same A operand times
-//     a constant B = -(off + z) in a second accumulator chain removes the
-//     offset and the zero point exactly (the zero-point expansion of [LQ]'s
-//     W8A8 section and [VE] "二", applied per group), and the group scale is
+//     a constant B = -(off + z), accumulated into the same chain after each
+//     code step, removes the offset and the zero point (the zero-point
+//     expansion of [LQ]'s W8A8 section and [VE] "二", applied per group; the
+//     interleaving keeps the running sum small), and the group scale is
 //     applied once per group to the 4 accumulators of a lane;
+//   * the vector ALU is what bounds the loop once the weights stream at HBM
+//     rate, so the per-group instruction count is kept minimal: rows past M
+//     are not masked (each output row depends only on its own activation row,
+//     and rows past M are never stored), and one token is staged as a single
+//     256-byte row;
 //   * the waves of a workgroup split K and add their 16 x 16 tiles in LDS.
 #include <hip/hip_runtime.h>
 
@@ -71,19 +78,20 @@ __device__ inline f32x4 mfma(const uint4& a, const uint4& b, const f32x4& c) {
 }
 
 // word of 8 codes (code of k = 2i at bits 4i, of k = 2i + 1 at bits 16 + 4i)
-// -> 4 registers of 16-bit pairs (off + q_{2i}, off + q_{2i+1})
-template <bool BF16>
-__device__ inline uint4 unpack8(uint32_t w) {
-  const uint32_t magic = BF16 ? 0x43004300u : 0x64006400u;
-  return make_uint4((w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic, ((w >> 8) & 0x000F000Fu) | magic,
-                    ((w >> 12) & 0x000F000Fu) | magic);
+// -> 4 registers of 16-bit pairs (off + q_{2i}, off + q_{2i+1}); mask =
+// 0x000F000F and magic = the offset's bit pattern in both halves, passed in
+// registers so that each register is one v_and_or_b32
+__device__ inline uint4 unpack8(uint32_t w, uint32_t mask, uint32_t magic) {
+  return make_uint4((w & mask) | magic, ((w >> 4) & mask) | magic, ((w >> 8) & mask) | magic,
+                    ((w >> 12) & mask) | magic);
 }
 
+// the pair (-(off + z), -(off + z)) for a zero point z in 0..15: -(1024 + z)
+// is 0xE400 + z in fp16 and -(128 + z) is 0xC300 + z in bf16 (exact: z only
+// fills low mantissa bits)
 template <bool BF16>
 __device__ inline uint32_t neg_offset_pair(uint32_t z) {
-  const float v = -((BF16 ? 128.0f : 1024.0f) + (float)z);   // exact in both 16-bit types
-  const uint32_t h = BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
-  return h | (h << 16);
+  return z * 0x00010001u + (BF16 ? 0xC300C300u : 0xE400E400u);
 }
 
 // issues one 16-byte global -> LDS copy per lane (lane i writes lds + 16 i)
@@ -177,16 +185,17 @@ __device__ inline void after_wait(uint32_t& v) {
 // order, the NT weight chunks (1 KB each, lane l's 16 bytes at 16 l), the
 // scale-pair words and the zero-point words of the workgroup's 16 * NT
 // channels (256 B each: lane l copies the word of slice (l / 16) % NT,
-// channel l % 16) and 4 * MB activation rows of the group (1 KB per 4 rows).
+// channel l % 16) and the activation rows of the group: 4 * MB rows (1 KB per
+// 4 rows), or for MB = 0 the single row of one token (256 B, 4 bytes a lane).
 template <int NT, int MB>
 struct Slot {
   static constexpr int kW = 0;
   static constexpr int kS = NT * 1024;
   static constexpr int kZ = kS + 256;
   static constexpr int kX = kZ + 256;
-  static constexpr int kBytes = kX + MB * 1024;
-  static constexpr int kLoads = NT + 2 + MB;      // copies a wave issues per step
-  static constexpr int kRows = 4 * MB;
+  static constexpr int kBytes = kX + (MB == 0 ? 256 : MB * 1024);
+  static constexpr int kLoads = NT + 2 + (MB == 0 ? 1 : MB);   // copies a wave issues per step
+  static constexpr int kRows = MB == 0 ? 1 : 4 * MB;
 };
 
 #ifndef QL_GEMV_LDS_BUDGET
@@ -198,15 +207,17 @@ struct Slot {
 // decode layers with weights streamed from HBM: 8 waves per workgroup with
 // 1 - 2 groups in flight each stream best; deeper rings (more copies in flight
 // per compute unit, fewer workgroups per compute unit) are slower, as for a
-// plain streaming read.
+// plain streaming read.  The one-token slot (MB = 0) takes the depth of the
+// four-row slot: the depth is about copies in flight, not LDS space.
 template <int NT, int MB, int NW>
 constexpr int ring_depth() {
-  const int d = QL_GEMV_LDS_BUDGET / (NW * Slot<NT, MB>::kBytes);
+  const int d = QL_GEMV_LDS_BUDGET / (NW * Slot<NT, MB == 0 ? 1 : MB>::kBytes);
   return d > 9 ? 9 : d < 2 ? 2 : d;
 }
 
 // NT: 16-column slices per workgroup; MB: blocks of 4 activation rows staged
-// per group (4 * MB >= M); NW: waves per workgroup (they split K).
+// per group (4 * MB >= M; 0: the one row of M = 1); NW: waves per workgroup
+// (they split K).
 template <bool BF16, int NT, int MB, int NW>
 __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
   using SL = Slot<NT, MB>;
@@ -247,13 +258,19 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
   const int zshift = 8 * (cl & 3);                          // channel bases are multiples of 16
   // Activation rows: lane l copies row r = 4b + l/16 of block b into stored
   // piece l % 16, which holds the row's logical 16-byte piece (l % 16) ^ r
-  // (rows at or past M repeat row M - 1: a valid load; those rows are zeroed
-  // when read).
-  const uint16_t* xsrc[MB];
+  // (rows at or past M repeat row M - 1: a valid load whose products only
+  // reach output rows that are never stored).  MB = 0: lane l copies 4 bytes
+  // (2 values) of the one row, unswizzled (row 0's key is 0).
+  constexpr int kXB = MB == 0 ? 1 : MB;
+  const uint16_t* xsrc[kXB];
+  if constexpr (MB == 0) {
+    xsrc[0] = a.X + 2 * lane;                                             // + 128*g
+  } else {
 #pragma unroll
-  for (int b = 0; b < MB; ++b) {
-    const int r = 4 * b + blk;
-    xsrc[b] = a.X + (size_t)min(r, a.M - 1) * a.K + ((cl ^ r) & 15) * 8;   // + 128*g
+    for (int b = 0; b < MB; ++b) {
+      const int r = 4 * b + blk;
+      xsrc[b] = a.X + (size_t)min(r, a.M - 1) * a.K + ((cl ^ r) & 15) * 8;   // + 128*g
+    }
   }
 
   // LDS byte addresses of this lane's reads inside slot 0
@@ -265,7 +282,6 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
   // A operand of the 16x16x32 MFMA: lane l supplies row l % 16, k values
   // 8 * (l / 16) .. +8 of each 32-wide k step j, i.e. logical piece 4*blk + j
   const int rr = min(cl, SL::kRows - 1);
-  const uint32_t rmask = cl < a.M ? 0xFFFFFFFFu : 0u;
   uint32_t x_rd[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) x_rd[j] = rbase + SL::kX + rr * 256 + (((4 * blk + j) ^ rr) & 15) * 16;
@@ -278,9 +294,24 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
     for (int t = 0; t < NT; ++t) load_lds16(wsrc[t] + (size_t)g * 4 * np, dst + SL::kW + t * 1024);
     load_lds4(ssrc + (size_t)pr * np, dst + SL::kS);
     load_lds4(zsrc + (size_t)pr * (np / 4), dst + SL::kZ);
+    if constexpr (MB == 0) {
+      load_lds4(xsrc[0] + (size_t)g * kGroup, dst + SL::kX);
+    } else {
 #pragma unroll
-    for (int b = 0; b < MB; ++b) load_lds16(xsrc[b] + (size_t)g * kGroup, dst + SL::kX + b * 1024);
+      for (int b = 0; b < MB; ++b) load_lds16(xsrc[b] + (size_t)g * kGroup, dst + SL::kX + b * 1024);
+    }
   };
+
+  // the unpacking constants in registers (one v_and_or_b32 per register of
+  // 2 codes; a three-operand instruction takes no 32-bit literal here)
+  uint32_t umask, umagic;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(umask));
+  asm volatile("s_mov_b32 %0, %1" : "=s"(umagic) : "i"(BF16 ? 0x43004300 : 0x64006400));
+#else
+  umask = 0x000F000Fu;
+  umagic = BF16 ? 0x43004300u : 0x64006400u;
+#endif
 
   f32x4 acc[NT];
 #pragma unroll
@@ -300,10 +331,7 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
     }
     lds_wait();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      after_wait(xa[j]);
-      xa[j] &= rmask;
-    }
+    for (int j = 0; j < 4; ++j) after_wait(xa[j]);
     const int h = g & 1;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -311,17 +339,17 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
       after_wait(sv[t]);
       after_wait(zv[t]);
       const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[t] >> (16 * h)));
-      const uint32_t nz = neg_offset_pair<BF16>((zv[t] >> (zshift + 4 * h)) & 0xFu);
+      const uint32_t nz = neg_offset_pair<BF16>(__builtin_amdgcn_ubfe(zv[t], zshift + 4 * h, 4));
       const uint4 bz = make_uint4(nz, nz, nz, nz);
-      f32x4 t0 = {0.0f, 0.0f, 0.0f, 0.0f}, t1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 t0 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint4 x = __builtin_bit_cast(uint4, xa[j]);
-        t0 = mfma<BF16>(x, unpack8<BF16>(wv[t][j]), t0);
-        t1 = mfma<BF16>(x, bz, t1);
+        t0 = mfma<BF16>(x, unpack8(wv[t][j], umask, umagic), t0);
+        t0 = mfma<BF16>(x, bz, t0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t][i] += s * (t0[i] + t1[i]);
+      for (int i = 0; i < 4; ++i) acc[t][i] += s * t0[i];
     }
   };
 
@@ -387,7 +415,8 @@ hipError_t launch_cfg(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
 
 template <bool BF16, int NT>
 hipError_t launch_nt(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
-  // activation rows staged per group: 4, 8 or 16
+  // activation rows staged per group: 1, 4, 8 or 16
+  if (a.M == 1) return launch_cfg<BF16, NT, 0>(a, P, st);
   if (a.M <= 4) return launch_cfg<BF16, NT, 1>(a, P, st);
   if (a.M <= 8) return launch_cfg<BF16, NT, 2>(a, P, st);
   return launch_cfg<BF16, NT, 4>(a, P, st);
