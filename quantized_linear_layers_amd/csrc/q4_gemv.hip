@@ -187,13 +187,15 @@ __device__ inline void after_wait(uint32_t& v) {
 // channels (256 B each: lane l copies the word of slice (l / 16) % NT,
 // channel l % 16) and the activation rows of the group: 4 * MB rows (1 KB per
 // 4 rows), or for MB = 0 the single row of one token (256 B, 4 bytes a lane).
+constexpr int slot_bytes(int NT, int MB) { return NT * 1024 + 512 + (MB == 0 ? 256 : MB * 1024); }
+
 template <int NT, int MB>
 struct Slot {
   static constexpr int kW = 0;
   static constexpr int kS = NT * 1024;
   static constexpr int kZ = kS + 256;
   static constexpr int kX = kZ + 256;
-  static constexpr int kBytes = kX + (MB == 0 ? 256 : MB * 1024);
+  static constexpr int kBytes = slot_bytes(NT, MB);
   static constexpr int kLoads = NT + 2 + (MB == 0 ? 1 : MB);   // copies a wave issues per step
   static constexpr int kRows = MB == 0 ? 1 : 4 * MB;
 };
@@ -209,11 +211,16 @@ struct Slot {
 // per compute unit, fewer workgroups per compute unit) are slower, as for a
 // plain streaming read.  The one-token slot (MB = 0) takes the depth of the
 // four-row slot: the depth is about copies in flight, not LDS space.
-template <int NT, int MB, int NW>
-constexpr int ring_depth() {
-  const int d = QL_GEMV_LDS_BUDGET / (NW * Slot<NT, MB == 0 ? 1 : MB>::kBytes);
+constexpr int ring_depth_of(int NT, int MB, int NW) {
+  const int d = QL_GEMV_LDS_BUDGET / (NW * slot_bytes(NT, MB == 0 ? 1 : MB));
   return d > 9 ? 9 : d < 2 ? 2 : d;
 }
+template <int NT, int MB, int NW>
+constexpr int ring_depth() {
+  return ring_depth_of(NT, MB, NW);
+}
+// LDS of one workgroup (its staging rings)
+constexpr int gemv_lds_bytes(int NT, int MB, int NW) { return NW * ring_depth_of(NT, MB, NW) * slot_bytes(NT, MB); }
 
 // NT: 16-column slices per workgroup; MB: blocks of 4 activation rows staged
 // per group (4 * MB >= M; 0: the one row of M = 1); NW: waves per workgroup
@@ -224,6 +231,7 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
   constexpr int D = ring_depth<NT, MB, NW>();
   constexpr int kWaveBytes = D * SL::kBytes;
   static_assert(kWaveBytes >= NT * 64 * 16, "the reduction reuses a wave's staging area");
+  static_assert(NW * kWaveBytes == gemv_lds_bytes(NT, MB, NW), "the plan's LDS figure");
   static_assert(NT == 1 || NT == 2 || NT == 4, "slices per workgroup");
   __shared__ __align__(1024) uint8_t lds_all[NW * kWaveBytes];
 
@@ -413,13 +421,17 @@ hipError_t launch_cfg(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
   return hipGetLastError();
 }
 
+// activation-row blocks staged per group for M tokens: 0 (one row), 1, 2 or 4
+inline int row_blocks(int M) { return M == 1 ? 0 : M <= 4 ? 1 : M <= 8 ? 2 : 4; }
+
 template <bool BF16, int NT>
 hipError_t launch_nt(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
-  // activation rows staged per group: 1, 4, 8 or 16
-  if (a.M == 1) return launch_cfg<BF16, NT, 0>(a, P, st);
-  if (a.M <= 4) return launch_cfg<BF16, NT, 1>(a, P, st);
-  if (a.M <= 8) return launch_cfg<BF16, NT, 2>(a, P, st);
-  return launch_cfg<BF16, NT, 4>(a, P, st);
+  switch (row_blocks(a.M)) {
+    case 0: return launch_cfg<BF16, NT, 0>(a, P, st);
+    case 1: return launch_cfg<BF16, NT, 1>(a, P, st);
+    case 2: return launch_cfg<BF16, NT, 2>(a, P, st);
+    default: return launch_cfg<BF16, NT, 4>(a, P, st);
+  }
 }
 
 template <bool BF16>
@@ -434,16 +446,21 @@ hipError_t launch_dtype(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
 }  // namespace
 
 GemvPlan plan_q4_gemv(int M, int N, int K) {
-  (void)M;
   (void)K;
+  constexpr int kCUs = 256, kLdsPerCU = 160 * 1024;     // MI355X
   GemvPlan P;
   const Q4Layout L = q4_layout(N, K);
   const int slices = L.Np / 16;
   // widest column block that still leaves a workgroup for every compute unit
-  P.nt = (slices / 4 >= 256) ? 4 : (slices / 2 >= 256) ? 2 : 1;
+  P.nt = (slices / 4 >= kCUs) ? 4 : (slices / 2 >= kCUs) ? 2 : 1;
   // eight waves, except with four slices (the widest 70B layer), where four
-  // waves measured 4-9% faster
+  // waves measured 4-9% faster; and four when the eight-wave workgroups
+  // would not all be resident at once (their rings take too much LDS for
+  // the grid to fit on the compute units in one round: 16 tokens on the
+  // 4096 x 11008 layer measured 13.2 us with eight waves in two rounds)
   P.waves = P.nt == 4 ? 4 : 8;
+  const int grid = slices / P.nt;
+  if (P.waves == 8 && grid > kCUs * (kLdsPerCU / gemv_lds_bytes(P.nt, row_blocks(M), 8))) P.waves = 4;
 #ifdef QL_GEMV_SWEEP
   if (const char* e = getenv("QL_NT")) { int v = atoi(e); if (v == 1 || v == 2 || v == 4) P.nt = v; }
   if (const char* e = getenv("QL_W")) { int v = atoi(e); if (v == 4 || v == 8) P.waves = v; }
