@@ -352,10 +352,17 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
   float* row_s = reinterpret_cast<float*>(g_lds + kRowParams);
   int32_t* row_z = reinterpret_cast<int32_t*>(g_lds + kRowParams + BM * 4);
   __syncthreads();                               // every wave is done with the slots
+  // whether every zero point and column sum of the tile fits 24 bits, so that
+  // their product is one v_mul_i32_i24 (exact) instead of a quarter-rate
+  // 32-bit multiply; real zero points are 8-bit and |azp_adj| <= 128 K
+  constexpr int kI24 = 1 << 23;
+  bool wide = false;
   for (int r = tid; r < BM; r += 64 * kWaves) {
     const int m = min(m0 + r, a.M - 1);
     row_s[r] = e.s_a[e.s_a_vec ? m : 0];
-    row_z[r] = e.azp ? e.azp[m] : 0;
+    const int32_t z = e.azp ? e.azp[m] : 0;
+    row_z[r] = z;
+    wide |= z < -kI24 || z >= kI24;
   }
   float col_s[kNT], col_b[kNT];
   int32_t col_adj[kNT];
@@ -364,6 +371,7 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
     const int n = min(n0 + wn + nt * 32 + l32, a.N - 1);
     col_s[nt] = e.s_b[e.s_b_vec ? n : 0];
     col_adj[nt] = e.azp_adj ? e.azp_adj[n] : 0;
+    wide |= col_adj[nt] < -kI24 || col_adj[nt] >= kI24;
     float b = 0.0f;
     if (e.bias) {
       const uint16_t bb = static_cast<const uint16_t*>(e.bias)[n];
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
     }
     col_b[nt] = b;
   }
-  __syncthreads();
+  wide = __syncthreads_or(wide);
   const bool per_token_azp = e.azp != nullptr;
   auto value = [&](int mt, int nt, int el, int r) -> uint16_t {
     float c;
@@ -389,17 +397,47 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
     // pieces of a 128-byte row XOR-swizzled by row, conflict-free both ways)
     // and store them as 16-byte row pieces, 8 full lines per instruction
     uint8_t* region = reinterpret_cast<uint8_t*>(g_lds) + wave * kOutWave;
+    // the lane's 4 * kMT runs of 4 consecutive rows: their scales and zero
+    // points as 16-byte LDS reads
+    float4 rs[kMT][4];
+    int4 rz[kMT][4];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm + mt * 32 + 8 * q + 4 * half;
+        rs[mt][q] = *reinterpret_cast<const float4*>(row_s + r);
+        rz[mt][q] = *reinterpret_cast<const int4*>(row_z + r);
+      }
+    auto stage = [&](auto corr) {
 #pragma unroll
-        for (int el = 0; el < 16; ++el) {
-          const int rl = mt * 32 + 8 * (el >> 2) + 4 * half + (el & 3);   // row inside the wave tile
-          const int cl = nt * 32 + l32;                                   // column inside the wave tile
-          const uint16_t v = value(mt, nt, el, wm + rl);
-          *reinterpret_cast<uint16_t*>(region + rl * 128 + (((cl >> 3) ^ (rl & 7)) << 4) + (cl & 7) * 2) = v;
-        }
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+          for (int el = 0; el < 16; ++el) {
+            const int q = el >> 2, i = el & 3;
+            const float sr = i == 0 ? rs[mt][q].x : i == 1 ? rs[mt][q].y : i == 2 ? rs[mt][q].z : rs[mt][q].w;
+            const int zr = i == 0 ? rz[mt][q].x : i == 1 ? rz[mt][q].y : i == 2 ? rz[mt][q].z : rz[mt][q].w;
+            float c;
+            if constexpr (FP8)
+              c = acc[mt][nt][el];
+            else
+              c = (float)(acc[mt][nt][el] - corr(zr, col_adj[nt]));
+            const float v = sr * (col_s[nt] * c) + col_b[nt];
+            const uint16_t h =
+                OUT_BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+            const int rl = mt * 32 + 8 * q + 4 * half + i;                  // row inside the wave tile
+            const int cl = nt * 32 + l32;                                   // column inside the wave tile
+            *reinterpret_cast<uint16_t*>(region + rl * 128 + (((cl >> 3) ^ (rl & 7)) << 4) + (cl & 7) * 2) = h;
+          }
+    };
+    if (FP8 || !per_token_azp)
+      stage([](int, int adj) { return adj; });
+    else if (!wide)
+      stage([](int z, int adj) { return __mul24(z, adj); });
+    else
+      stage([](int z, int adj) { return z * adj; });
     uint16_t* out = static_cast<uint16_t*>(e.out);
 #pragma unroll
     for (int i = 0; i < (kMT * 32) / 8; ++i) {

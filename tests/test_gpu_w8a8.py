@@ -39,15 +39,21 @@ def check_quant(X, symmetric=False):
 
 
 def check_gemm(Aq, Bq, s_a, s_b, azp=None, adj=None, bias=None, out_dtype=torch.float16):
-    out, raw = ql.i8_gemm_scaled(cu(Aq), cu(Bq), cu(s_a), cu(s_b),
-                                 None if azp is None else cu(azp), None if adj is None else cu(adj),
-                                 None if bias is None else bias.cuda(), out_dtype=out_dtype, raw=True)
+    """With raw_out (per-element epilogue, the int32 accumulator kept) and
+    without it (tiles wholly inside Y stage their outputs through LDS and
+    store rows: the path the throughput figures time): both against the
+    oracle."""
+    args = (cu(Aq), cu(Bq), cu(s_a), cu(s_b), None if azp is None else cu(azp), None if adj is None else cu(adj),
+            None if bias is None else bias.cuda())
+    out, raw = ql.i8_gemm_scaled(*args, out_dtype=out_dtype, raw=True)
+    out_fast = ql.i8_gemm_scaled(*args, out_dtype=out_dtype)
     torch.cuda.synchronize()
     C, out64 = ow8.w8a8_linear(Aq, Bq, s_a, s_b, azp, adj, None if bias is None else wl.as_f64(bias))
     assert np.array_equal(raw.cpu().numpy().astype(np.int64), C)
-    od = wl.as_f64(out.cpu())
-    e = float(np.abs(od - out64).max() / np.abs(out64).max())
-    assert e <= TOL, f"relative error {e:.3e}"
+    for o in (out, out_fast):
+        od = wl.as_f64(o.cpu())
+        e = float(np.abs(od - out64).max() / np.abs(out64).max())
+        assert e <= TOL, f"relative error {e:.3e}"
 
 
 # ---------------------------------------------------------------- the workload
@@ -117,3 +123,21 @@ def test_gemm_extreme_codes():
     s_a = np.full(M, 1e-3, np.float32)
     s_b = np.full(N, 1e-4, np.float32)
     check_gemm(Aq, Bq, s_a, s_b)
+
+
+def test_gemm_wide_zero_points():
+    """Zero points and column sums past 24 bits (the epilogue then forms
+    azp * azp_adj with a 32-bit multiply): still exact.  Full 256 x 128 tiles,
+    so the row-staged store path is the one checked without raw_out."""
+    M, N, K = 256, 256, 512
+    r = np.random.default_rng(11)
+    Aq = r.integers(-128, 128, (M, K)).astype(np.int8)
+    Bq = np.zeros((N, K), np.int8)
+    Bq[:, :3] = r.integers(-1, 2, (N, 3))          # column sums in -3..3
+    azp = (r.integers(-1, 2, M) * ((1 << 23) + r.integers(0, 1 << 20, M))).astype(np.int32)
+    s_a = np.full(M, 1e-6, np.float32)
+    s_b = np.full(N, 1e-2, np.float32)
+    adj = ow8.azp_adj(Bq)
+    check_gemm(Aq, Bq, s_a, s_b, azp, adj)
+    wide_adj = adj.astype(np.int64) + (1 << 24)    # a column sum past 24 bits, any zero points
+    check_gemm(Aq, Bq, s_a, s_b, (azp % 64).astype(np.int32), wide_adj.astype(np.int32))
