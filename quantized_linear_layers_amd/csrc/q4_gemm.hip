@@ -87,11 +87,12 @@ using PrefillCfg = Cfg<8, 8, 1, 3>;
 
 struct GemmArgs {
   const uint16_t* X;
-  int M, K, N, Np;
-  const uint4* W;          // [Kp/32][Np] chunks
-  const uint32_t* S;       // [Kp/256][Np] scale pairs
-  const uint8_t* Z;        // [Kp/256][Np] zero pairs
-  uint16_t* Y;
+  int M, K, N, Np;         // N, Np: this launch's columns (real, padded)
+  int ldw, ldy;            // row strides in columns of the blob's rows and of Y
+  const uint4* W;          // [Kp/32][ldw] chunks
+  const uint32_t* S;       // [Kp/256][ldw] scale pairs
+  const uint8_t* Z;        // [Kp/256][ldw] zero pairs
+  uint16_t* Y;             // [M][ldy]
 };
 
 // ---- global -> LDS copies and counter waits
@@ -265,7 +266,7 @@ __device__ inline void fill(uint8_t* lds, const GemmArgs& a, const FillPlan<C>& 
 #pragma unroll
   for (int i = 0; i < C::kAFills; ++i) load_lds16(xb + f.x[i] + (uint32_t)kb * (BK * 2), st + f.xdst[i]);
   const uint32_t pr = kb >> 2;                              // pair of groups of this k block
-  const uint32_t np = a.Np;
+  const uint32_t np = a.ldw;
 #pragma unroll
   for (int d = 0; d < kNTW; ++d)
     load_lds16(wb + f.w[d] + (uint32_t)(2 * kb + f.wc[d]) * np * 16, st + f.wdst + d * 1024);
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(GemmArgs a) {
         const int m = m0 + 32 * mt + 8 * (e >> 2) + 4 * half + (e & 3);
         if (m < a.M) {
           const float v = fr.acc[mt][t][e];
-          a.Y[(size_t)m * a.N + n] =
+          a.Y[(size_t)m * a.ldy + n] =
               BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
         }
       }
@@ -558,6 +559,8 @@ hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const u
   a.K = K;
   a.N = N;
   a.Np = L.Np;
+  a.ldw = L.Np;
+  a.ldy = N;
   a.W = reinterpret_cast<const uint4*>(blob + L.w_off);
   a.S = reinterpret_cast<const uint32_t*>(blob + L.s_off);
   a.Z = blob + L.z_off;
@@ -566,8 +569,37 @@ hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const u
     case 32: return launch_cfg<Cfg<1, 1, 8, 3>>(a, bf16, st);
     case 64: return launch_cfg<Cfg<2, 2, 4, 3>>(a, bf16, st);
     case 128: return launch_cfg<Cfg<4, 4, 2, 3>>(a, bf16, st);
-    default: return launch_cfg<PrefillCfg>(a, bf16, st);
+    default: break;
   }
+  // 256 x 256 tiles, one workgroup per compute unit.  When their last round
+  // would leave at least half the compute units idle (the Llama-3-8B MLP
+  // layer: 896 tiles, 3.5 rounds), the columns of that round go to a second
+  // launch of 128 x 256 tiles, which fill every compute unit for about half a
+  // round's time.
+  constexpr int kCUs = 256;                                // MI355X
+  const int tm = (M + 255) / 256, tn = (N + 255) / 256;
+  const long tiles = (long)tm * tn;
+  const long rounds = (tiles + kCUs - 1) / kCUs;
+  const long last = tiles - (rounds - 1) * kCUs;
+  const int cm = tm > 0 ? (int)(((rounds - 1) * kCUs) / tm) : 0;   // column tiles of the main launch
+  const int n_off = cm * 256;
+  if (rounds >= 2 && 2 * last <= kCUs && cm >= 1 && cm < tn &&
+      (long)((M + 127) / 128) * ((N - n_off + 255) / 256) <= kCUs) {
+    GemmArgs main = a;
+    main.N = n_off;
+    main.Np = n_off;
+    GemmArgs tail = a;
+    tail.N = N - n_off;
+    tail.Np = L.Np - n_off;
+    tail.W += n_off;
+    tail.S += n_off;
+    tail.Z += n_off;
+    tail.Y += n_off;
+    const hipError_t e = launch_cfg<PrefillCfg>(main, bf16, st);
+    if (e != hipSuccess) return e;
+    return launch_cfg<Cfg<4, 8, 1, 3>>(tail, bf16, st);
+  }
+  return launch_cfg<PrefillCfg>(a, bf16, st);
 }
 
 }  // namespace ql

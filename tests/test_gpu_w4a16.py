@@ -110,6 +110,23 @@ def test_prefill_sampled():
     check(W, wl.activations(w, M, K, N), rows=rows, cols=cols)
 
 
+@pytest.mark.parametrize("M,K,N,dtype", [(1100, 256, 13400, torch.float16), (700, 384, 26000, torch.bfloat16)])
+def test_prefill_split_round(M, K, N, dtype):
+    """Grids of 256 x 256 tiles whose last round is at most half full: the
+    columns of that round run as 128 x 256 tiles in a second launch (ragged
+    rows and columns on both sides).  Every column past the split, the 64
+    before it and a sample of the rest are checked on every row."""
+    tm, tn = (M + 255) // 256, (N + 255) // 256
+    rounds = (tm * tn + 255) // 256
+    n_off = ((rounds - 1) * 256 // tm) * 256
+    assert rounds >= 2 and 2 * (tm * tn - (rounds - 1) * 256) <= 256 and n_off < N
+    r = np.random.default_rng(M + N)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
+    cols = np.union1d(np.arange(n_off - 64, N), r.choice(n_off, 192, replace=False))
+    check(W, X, cols=cols)
+
+
 # ---------------------------------------------------------------- ragged shapes and edges
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
