@@ -321,7 +321,8 @@ def cpu_baseline(budget_s=20.0):
             break
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of the 9 (M, K, N) decode cases of the 7B workload in {dt:.1f} s "
+            "sample": f"{done} case runs cycling over the 9 (M, K, N) decode cases of the 7B workload "
+                      f"({done / len(cases):.1f} steps) in {dt:.1f} s "
                       f"(explicit fp64 dequant + fp64 BLAS product per case; quantization untimed)"}
 
 
