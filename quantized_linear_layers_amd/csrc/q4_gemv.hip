@@ -446,13 +446,19 @@ hipError_t launch_dtype(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
 }  // namespace
 
 GemvPlan plan_q4_gemv(int M, int N, int K) {
-  (void)K;
   constexpr int kCUs = 256, kLdsPerCU = 160 * 1024;     // MI355X
   GemvPlan P;
   const Q4Layout L = q4_layout(N, K);
   const int slices = L.Np / 16;
-  // widest column block that still leaves a workgroup for every compute unit
-  P.nt = (slices / 4 >= kCUs) ? 4 : (slices / 2 >= kCUs) ? 2 : 1;
+  // widest column block that still leaves a workgroup for every compute unit;
+  // except for one token and a short K (at most 4 groups a wave), where one
+  // slice per workgroup (three resident per compute unit) overlaps the
+  // workgroups' fixed start and finish
+  const int gpw = (K / kGroup + 7) / 8;
+  if (M == 1 && gpw <= 4)
+    P.nt = 1;
+  else
+    P.nt = (slices / 4 >= kCUs) ? 4 : (slices / 2 >= kCUs) ? 2 : 1;
   // eight waves, except with four slices (the widest 70B layer), where four
   // waves measured 4-9% faster; and four when the eight-wave workgroups
   // would not all be resident at once (their rings take too much LDS for
