@@ -183,21 +183,26 @@ __device__ inline void after_wait(uint32_t& v) {
 
 // One step of one wave = one 128-wide group: the staging slot holds, in this
 // order, the NT weight chunks (1 KB each, lane l's 16 bytes at 16 l), the
-// scale-pair words and the zero-point words of the workgroup's 16 * NT
-// channels (256 B each: lane l copies the word of slice (l / 16) % NT,
-// channel l % 16) and the activation rows of the group: 4 * MB rows (1 KB per
-// 4 rows), or for MB = 0 the single row of one token (256 B, 4 bytes a lane).
-constexpr int slot_bytes(int NT, int MB) { return NT * 1024 + 512 + (MB == 0 ? 256 : MB * 1024); }
+// activation rows of the group (4 * MB rows, 1 KB per 4 rows) and a 1 KB
+// block copied by one 16-byte-per-lane copy: the scale-pair words of the
+// workgroup's 16 * NT channels (64 NT bytes) and their zero-point bytes
+// (16 NT bytes), preceded for MB = 0 by the single row of one token (256 B).
+// One copy instead of three keeps the per-group copy count (each copy
+// instruction costs the address unit the same whatever its width) at NT + 1
+// for one token and NT + MB + 1 otherwise.
+constexpr int slot_bytes(int NT, int MB) { return NT * 1024 + (MB == 0 ? 0 : MB * 1024) + 1024; }
 
 template <int NT, int MB>
 struct Slot {
   static constexpr int kW = 0;
-  static constexpr int kS = NT * 1024;
-  static constexpr int kZ = kS + 256;
-  static constexpr int kX = kZ + 256;
+  static constexpr int kX = NT * 1024;                          // activation rows
+  static constexpr int kC = kX + (MB == 0 ? 0 : MB * 1024);    // the combined 1 KB copy
+  static constexpr int kS = kC + (MB == 0 ? 256 : 0);          // scale words
+  static constexpr int kZ = kS + 64 * NT;                      // zero-point bytes
   static constexpr int kBytes = slot_bytes(NT, MB);
-  static constexpr int kLoads = NT + 2 + (MB == 0 ? 1 : MB);   // copies a wave issues per step
+  static constexpr int kLoads = NT + (MB == 0 ? 0 : MB) + 1;   // copies a wave issues per step
   static constexpr int kRows = MB == 0 ? 1 : 4 * MB;
+  static_assert(kZ + 16 * NT <= kC + 1024, "the combined copy's block");
 };
 
 #ifndef QL_GEMV_LDS_BUDGET
@@ -211,8 +216,10 @@ struct Slot {
 // per compute unit, fewer workgroups per compute unit) are slower, as for a
 // plain streaming read.  The one-token slot (MB = 0) takes the depth of the
 // four-row slot: the depth is about copies in flight, not LDS space.
+// (the depth keeps its calibration: the budget over NT + 1.5 + max(MB, 1) KB
+// per slot, the slot size the depths were measured with)
 constexpr int ring_depth_of(int NT, int MB, int NW) {
-  const int d = QL_GEMV_LDS_BUDGET / (NW * slot_bytes(NT, MB == 0 ? 1 : MB));
+  const int d = QL_GEMV_LDS_BUDGET / (NW * (NT * 1024 + 512 + (MB == 0 ? 1 : MB) * 1024));
   return d > 9 ? 9 : d < 2 ? 2 : d;
 }
 template <int NT, int MB, int NW>
@@ -257,28 +264,45 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
     const int n = (cb * NT + t) * 16 + cl;                  // output channel of this lane in slice t
     wsrc[t] = a.W + (size_t)blk * np + n;                   // + 4*Np*g for group g
   }
-  // scale and zero words: lane l copies those of slice (l / 16) % NT, channel
-  // l % 16; the zero-point byte of a channel is read as the aligned word
-  // holding it
-  const int nsz = (cb * NT + (blk % NT)) * 16 + cl;
-  const uint32_t* ssrc = a.S + nsz;                                          // + Np*(g/2)
-  const uint32_t* zsrc = reinterpret_cast<const uint32_t*>(a.Z + (nsz & ~3));   // + Np/4 words per pair
+  // The combined copy: lane l copies 16 bytes.  For MB = 0, lanes 0..15 copy
+  // the token's 16-byte pieces of the group, then (from lane c0 = 16 for
+  // MB = 0, 0 otherwise) 4 NT lanes copy the scale words of the workgroup's
+  // channels (4 each) and NT lanes their zero-point bytes (16 each); the
+  // remaining lanes repeat lane c0's source.  Per group, a lane's source
+  // moves by g * cg + (g / 2) * cp bytes.
+  const int n0 = cb * NT * 16;                              // first channel of the workgroup
+  constexpr int c0 = MB == 0 ? 16 : 0;
+  const char* csrc;
+  uint32_t cg = 0, cp = 0;
+  {
+    const int j = lane - c0;
+    if (MB == 0 && lane < 16) {
+      csrc = reinterpret_cast<const char*>(a.X) + 16 * lane;
+      cg = 2 * kGroup;
+    } else if (j >= 0 && j < 4 * NT) {
+      csrc = reinterpret_cast<const char*>(a.S + n0) + 16 * j;
+      cp = 4 * (uint32_t)np;
+    } else if (j >= 4 * NT && j < 5 * NT) {
+      csrc = reinterpret_cast<const char*>(a.Z + n0) + 16 * (j - 4 * NT);
+      cp = (uint32_t)np;
+    } else {
+      csrc = reinterpret_cast<const char*>(a.S + n0);
+      cp = 4 * (uint32_t)np;
+    }
+  }
+  // the zero-point byte of a channel is read as the aligned word holding it
   const int zshift = 8 * (cl & 3);                          // channel bases are multiples of 16
-  // Activation rows: lane l copies row r = 4b + l/16 of block b into stored
-  // piece l % 16, which holds the row's logical 16-byte piece (l % 16) ^ r
-  // (rows at or past M repeat row M - 1: a valid load whose products only
-  // reach output rows that are never stored).  MB = 0: lane l copies 4 bytes
-  // (2 values) of the one row, unswizzled (row 0's key is 0).
+  // Activation rows (MB >= 1): lane l copies row r = 4b + l/16 of block b
+  // into stored piece l % 16, which holds the row's logical 16-byte piece
+  // (l % 16) ^ r (rows at or past M repeat row M - 1: a valid load whose
+  // products only reach output rows that are never stored).  The one row of
+  // MB = 0 travels in the combined copy, unswizzled (row 0's key is 0).
   constexpr int kXB = MB == 0 ? 1 : MB;
   const uint16_t* xsrc[kXB];
-  if constexpr (MB == 0) {
-    xsrc[0] = a.X + 2 * lane;                                             // + 128*g
-  } else {
 #pragma unroll
-    for (int b = 0; b < MB; ++b) {
-      const int r = 4 * b + blk;
-      xsrc[b] = a.X + (size_t)min(r, a.M - 1) * a.K + ((cl ^ r) & 15) * 8;   // + 128*g
-    }
+  for (int b = 0; b < kXB; ++b) {
+    const int r = 4 * b + blk;
+    xsrc[b] = a.X + (size_t)min(r, a.M - 1) * a.K + ((cl ^ r) & 15) * 8;   // + 128*g
   }
 
   // LDS byte addresses of this lane's reads inside slot 0
@@ -286,7 +310,7 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
   const uint32_t rbase = (uint32_t)(uintptr_t)(lds_ptr)ring;
   const uint32_t w_rd = rbase + SL::kW + lane * 16;
   const uint32_t s_rd = rbase + SL::kS + cl * 4;          // + 64 * t for slice t
-  const uint32_t z_rd = rbase + SL::kZ + cl * 4;
+  const uint32_t z_rd = rbase + SL::kZ + (cl & ~3);       // + 16 * t for slice t
   // A operand of the 16x16x32 MFMA: lane l supplies row l % 16, k values
   // 8 * (l / 16) .. +8 of each 32-wide k step j, i.e. logical piece 4*blk + j
   const int rr = min(cl, SL::kRows - 1);
@@ -300,14 +324,11 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
     const int pr = g >> 1;
 #pragma unroll
     for (int t = 0; t < NT; ++t) load_lds16(wsrc[t] + (size_t)g * 4 * np, dst + SL::kW + t * 1024);
-    load_lds4(ssrc + (size_t)pr * np, dst + SL::kS);
-    load_lds4(zsrc + (size_t)pr * (np / 4), dst + SL::kZ);
-    if constexpr (MB == 0) {
-      load_lds4(xsrc[0] + (size_t)g * kGroup, dst + SL::kX);
-    } else {
+    if constexpr (MB > 0) {
 #pragma unroll
       for (int b = 0; b < MB; ++b) load_lds16(xsrc[b] + (size_t)g * kGroup, dst + SL::kX + b * 1024);
     }
+    load_lds16(csrc + (uint32_t)g * cg + (uint32_t)pr * cp, dst + SL::kC);
   };
 
   // the unpacking constants in registers (one v_and_or_b32 per register of
@@ -335,7 +356,7 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
     for (int t = 0; t < NT; ++t) {
       wv[t] = lds_read16(w_rd + so + t * 1024);
       sv[t] = lds_read4(s_rd + so + t * 64);
-      zv[t] = lds_read4(z_rd + so + t * 64);
+      zv[t] = lds_read4(z_rd + so + t * 16);
     }
     lds_wait();
 #pragma unroll
