@@ -44,7 +44,7 @@ MALL_DEFEAT_BYTES = 1 << 30
 # what the same counter reads for a plain device copy of known size in the
 # same run.  It belongs to one version of the kernel source: when the source
 # hash differs, the figure is stale and `traffic` is reported as null.
-TRAFFIC = {"source_sha256": "4f6fb7614c2f483a05dba3306bd1fae6e24b8fc3b21131a8e364faee083ccb9e",
+TRAFFIC = {"source_sha256": "a520aa56e5ef08ed818808b749d50a30805789505bc0bd79ee906c7941d1fbd3",
            "bytes_per_launch": 19388072}
 
 

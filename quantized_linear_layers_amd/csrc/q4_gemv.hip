@@ -10,21 +10,23 @@
 //     partial sums ever leave the workgroup (cross-workgroup reductions need
 //     device-scope cache write-backs on this multi-XCD part, which cost far
 //     more than the layer itself); NT (1, 2 or 4) is the largest that still
-//     gives every compute unit a workgroup;
+//     gives every compute unit a workgroup (one slice for one token on a
+//     short K, where more, smaller workgroups overlap their fixed costs);
 //   * lane l of a wave reads output channel l % 16 of each of its NT 16-column
 //     slices, K-block l / 16: one 16-byte load per lane and slice covers 4
 //     consecutive 32-channel chunks x 16 channels = one 128-wide group, four
 //     256-byte runs of the chunk-major blob, where all channels at one K
 //     position are contiguous, so the waves of all workgroups that are at the
 //     same point of K read one contiguous window (what HBM streams best);
-//   * every operand of a group (the NT weight chunks, their scale and zero
-//     words and the activation rows the tokens need: 4, 8 or 16 of them) is
-//     copied straight from global memory into a per-wave ring of D LDS slots
-//     (global_load_lds, no register staging), D - 1 groups ahead of the group
-//     being multiplied; all copies are the same kind of vector-memory
-//     operation, so one counter wait per group covers them and nothing else
-//     waits on the prefetch; the activation rows of a group are read from LDS
-//     once and used for all NT slices;
+//   * every operand of a group (the NT weight chunks, their scale words and
+//     zero-point bytes and the activation rows the tokens need: 1, 4, 8 or 16
+//     of them) is copied straight from global memory into a per-wave ring of
+//     D LDS slots (global_load_lds, no register staging), D - 1 groups ahead
+//     of the group being multiplied; the scales, zero points and a single
+//     token's row share one copy instruction; all copies are the same kind of
+//     vector-memory operation, so one counter wait per group covers them and
+//     nothing else waits on the prefetch; the activation rows of a group are
+//     read from LDS once and used for all NT slices;
 //   * the codes stay packed until they are in registers ([QK] §9.5): one
 //     v_and_or_b32 per register (the mask 0x000F000F and the bit pattern of
 //     fp16 1024.0 (0x6400) or bf16 128.0 (0x4300) held in registers, since a
@@ -41,8 +43,7 @@
 //   * the vector ALU is what bounds the loop once the weights stream at HBM
 //     rate, so the per-group instruction count is kept minimal: rows past M
 //     are not masked (each output row depends only on its own activation row,
-//     and rows past M are never stored), and one token is staged as a single
-//     256-byte row;
+//     and rows past M are never stored);
 //   * the waves of a workgroup split K and add their 16 x 16 tiles in LDS.
 #include <hip/hip_runtime.h>
 
