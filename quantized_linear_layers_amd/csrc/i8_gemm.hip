@@ -264,9 +264,18 @@ __device__ inline void kstep(const I8Args& a, const FillPlan& f, Acc<FP8> (&acc)
   __builtin_amdgcn_s_barrier();                  // every wave's loads of block kb landed,
                                                  // and every wave finished block kb - 1
   constexpr int F = (S + kStages - 1) % kStages;
-  fill<F>(f, min(kb + kStages - 1, nkb - 1), a.K);
-#pragma unroll
-  for (int hh = 0; hh < kHalves; ++hh) mma_block<S, FP8>(acc, ard[hh], brd[hh], half, a.K - kb * BK - 64 * hh);
+  // the refill's copies are issued a share before each half's MFMAs: a wave
+  // stalls on a copy until the address unit takes it, and issuing all of
+  // them at once held the whole block's arithmetic back
+  const int fb = min(kb + kStages - 1, nkb - 1);
+  static_for<0, kHalves>([&](auto HH) {
+    constexpr int hh = HH;
+    static_for<hh * kLoads / kHalves, (hh + 1) * kLoads / kHalves>([&](auto I) {
+      const int k = min(fb * BK + f.p16[I], a.K - 16);
+      load_lds16(f.src[I] + k, g_lds + F * kSlot + f.dst[I]);
+    });
+    mma_block<S, FP8>(acc, ard[hh], brd[hh], half, a.K - kb * BK - 64 * hh);
+  });
 }
 
 // the last (nkb mod kStages) blocks, slots 0, 1, ... in order
