@@ -180,9 +180,9 @@ __device__ inline void after_wait(i32x4& v) {
 //         (pieces 2 (l / 32) + j, j = 0, 1)
 __device__ inline int frag_piece(bool fp8, int j, int half) { return fp8 ? 2 * half + j : 2 * j + half; }
 
-template <int S, bool FP8>
+template <int S, bool FP8, typename Mid>
 __device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard)[2], const uint32_t (&brd)[2],
-                                 int half, int kvalid) {
+                                 int half, int kvalid, Mid&& mid) {
   if constexpr (FP8) {
     i32x4 af[2][kMT], bf[2][kNT];
 #pragma unroll
@@ -206,7 +206,7 @@ __device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard
       for (int t = 0; t < kNT; ++t) after_wait(bf[j][t]);
     }
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         const i32x8 a8 = __builtin_shufflevector(af[0][mt], af[1][mt], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -214,6 +214,8 @@ __device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard
         // format codes 0, 0: both operands FP8 E4M3; no block scales
         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[mt][nt], 0, 0, 0, 0, 0, 0);
       }
+      if (mt == 0) mid();
+    }
     return;
   } else {
   // operand layout of the 32x32x32 int8 MFMA: lane l supplies row/column l%32,
@@ -248,6 +250,7 @@ __device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt)
         acc[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][mt], bf[ks][nt], acc[mt][nt], 0, 0, 0);
+    if (ks == 0) mid();
   }
   }
 }
@@ -268,13 +271,22 @@ __device__ inline void kstep(const I8Args& a, const FillPlan& f, Acc<FP8> (&acc)
   // stalls on a copy until the address unit takes it, and issuing all of
   // them at once held the whole block's arithmetic back
   const int fb = min(kb + kStages - 1, nkb - 1);
-  static_for<0, kHalves>([&](auto HH) {
-    constexpr int hh = HH;
-    static_for<hh * kLoads / kHalves, (hh + 1) * kLoads / kHalves>([&](auto I) {
+  auto copies = [&](auto I0, auto I1) {
+    static_for<I0, I1>([&](auto I) {
       const int k = min(fb * BK + f.p16[I], a.K - 16);
       load_lds16(f.src[I] + k, g_lds + F * kSlot + f.dst[I]);
     });
-    mma_block<S, FP8>(acc, ard[hh], brd[hh], half, a.K - kb * BK - 64 * hh);
+  };
+  // four shares: before each half's fragment reads and after its first MFMAs
+  constexpr int kQ = kLoads / (2 * kHalves), kR = kLoads - 2 * kHalves * kQ;   // kR shares get one more
+  static_for<0, kHalves>([&](auto HH) {
+    constexpr int hh = HH;
+    constexpr int q0 = 2 * hh, q1 = 2 * hh + 1;
+    constexpr int b0 = q0 * kQ + (q0 < kR ? q0 : kR), e0 = b0 + kQ + (q0 < kR ? 1 : 0);
+    constexpr int b1 = e0, e1 = b1 + kQ + (q1 < kR ? 1 : 0);
+    copies(std::integral_constant<int, b0>{}, std::integral_constant<int, e0>{});
+    mma_block<S, FP8>(acc, ard[hh], brd[hh], half, a.K - kb * BK - 64 * hh,
+                      [&] { copies(std::integral_constant<int, b1>{}, std::integral_constant<int, e1>{}); });
   });
 }
 
