@@ -79,6 +79,10 @@ struct Cfg {
   static constexpr int kLoads = kAFills + 2 * kNTW;      // copies per wave and stage
   static constexpr int kXBuf = kWaves >= 8 ? 1 : 2;      // X fragment buffers per wave
   static constexpr int kRed = (WK - 1) * WN * kMT * 4096;  // partial tiles of K-groups 1 .. WK-1
+  // refill copies spread over the k steps (small tiles), or all issued at
+  // once after the barrier (the prefill tile: there the second wave of each
+  // SIMD covers the issue, and spreading them measured 1.6% slower)
+  static constexpr bool kSpread = kMT < 8;
   static_assert(kAFills >= 1 && kATile % (1024 * WN) == 0, "X blocks per wave");
   static_assert(kRed <= kLds, "the K-group reduction reuses the stages");
   static_assert(kLds <= 160 * 1024, "LDS per workgroup");
@@ -258,6 +262,30 @@ struct FillPlan {
   int wdst, szdst;              // byte offsets of the wave's weight and scale/zero areas
 };
 
+// copies B .. E - 1 of a wave's kLoads copies of k block kb into stage S, in
+// the order: kAFills X blocks, kNTW weight chunks, kNTW scale/zero words
+template <class C, int S, int B, int E>
+__device__ __forceinline__ void fill_range(uint8_t* lds, const GemmArgs& a, const FillPlan<C>& f, int kb) {
+  uint8_t* st = lds + S * C::kStage;
+  const uint32_t pr = kb >> 2;                              // pair of groups of this k block
+  const uint32_t np = a.ldw;
+  static_for<B, E>([&](auto I) {
+    constexpr int i = I;
+    if constexpr (i < C::kAFills) {
+      load_lds16(reinterpret_cast<const char*>(a.X) + f.x[i] + (uint32_t)kb * (BK * 2), st + f.xdst[i]);
+    } else if constexpr (i < C::kAFills + kNTW) {
+      constexpr int d = i - C::kAFills;
+      load_lds16(reinterpret_cast<const char*>(a.W) + f.w[d] + (uint32_t)(2 * kb + f.wc[d]) * np * 16,
+                 st + f.wdst + d * 1024);
+    } else {
+      constexpr int d = i - C::kAFills - kNTW;
+      // scale rows hold one word per column, zero rows one byte per column
+      const char* szb = f.isz[d] ? reinterpret_cast<const char*>(a.Z) : reinterpret_cast<const char*>(a.S);
+      load_lds4(szb + f.sz[d] + pr * (f.isz[d] ? np : np * 4), st + f.szdst + d * 256);
+    }
+  });
+}
+
 template <class C, int S>
 __device__ inline void fill(uint8_t* lds, const GemmArgs& a, const FillPlan<C>& f, int kb) {
   uint8_t* st = lds + S * C::kStage;
@@ -290,9 +318,11 @@ struct Frag {
 //           column tile 0; + 32 kNTW * 16 per chunk, + 512 per column tile
 //   szrd:   LDS address (stage 0) of the lane's scale word of column tile 0;
 //           + 128 kNTW for its zero word, + 128 per column tile
-template <class C, bool BF16, int S>
-__device__ inline void compute(Frag<C>& fr, int kb, const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd,
-                               int zshift) {
+//   share(j): issues the j-th share of the refill of another stage (j = 0..3,
+//           at the start of k step j, after its LDS reads are issued)
+template <class C, bool BF16, int S, typename Share>
+__device__ __forceinline__ void compute(Frag<C>& fr, int kb, const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd,
+                               int zshift, Share&& share) {
   constexpr int kMT = C::kMT, kXBuf = C::kXBuf;
   constexpr int SO = S * C::kStage;
   const uint32_t wst = wrd + SO, szst = szrd + SO;
@@ -308,6 +338,7 @@ __device__ inline void compute(Frag<C>& fr, int kb, const uint32_t (&xrd)[4], ui
   });
   u32x4 xa[kXBuf][kMT];
   static_for<0, kMT>([&](auto MT) { xa[0][MT] = lds_read16<MT * 4096>(xrd[0] + SO); });
+  share(std::integral_constant<int, 0>{});
   wait_lgkm<0>();                                // words, scales, zeros and step 0's X landed
   const int h = (kb >> 1) & 1;                   // group of the block inside its pair
   float s[kNTW], nzs[kNTW];
@@ -332,10 +363,12 @@ __device__ inline void compute(Frag<C>& fr, int kb, const uint32_t (&xrd)[4], ui
     if constexpr (kXBuf == 1 && j > 0) {
       // one X buffer (two waves per SIMD hide the read latency)
       static_for<0, kMT>([&](auto MT) { xa[0][MT] = lds_read16<MT * 4096>(xrd[j] + SO); });
+      share(J);
       wait_lgkm<0>();
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) after_wait(xa[0][mt]);
     }
+    if constexpr (kXBuf == 2 && j > 0) share(J);
     // X of step j + 1 in flight while step j multiplies
     if constexpr (kXBuf == 2 && j < 3)
       static_for<0, kMT>([&](auto MT) { xa[cur ^ 1][MT] = lds_read16<MT * 4096>(xrd[j + 1] + SO); });
@@ -372,14 +405,31 @@ __device__ inline void compute(Frag<C>& fr, int kb, const uint32_t (&xrd)[4], ui
 // that is never multiplied), then multiply.  Every wave of the workgroup
 // takes the same number of steps, so the barriers match.
 template <class C, bool BF16, int S>
-__device__ inline void kstep(uint8_t* lds, Frag<C>& fr, const GemmArgs& a, const FillPlan<C>& f, int i, int kb0,
-                             int cnt, int nkb, const uint32_t (&xrd)[4], uint32_t wrd, uint32_t szrd, int zshift) {
+__device__ __forceinline__ void kstep(uint8_t* lds, Frag<C>& fr, const GemmArgs& a, const FillPlan<C>& f, int i,
+                                      int kb0, int cnt, int nkb, const uint32_t (&xrd)[4], uint32_t wrd,
+                                      uint32_t szrd, int zshift) {
   // this wave's copies of step i have landed once only the later steps' remain
   wait_vm<(C::kStages - 2) * C::kLoads>();
   __builtin_amdgcn_s_barrier();   // every wave's copies of step i landed; step i - 1 fully read
   constexpr int F = (S + C::kStages - 1) % C::kStages;
-  fill<C, F>(lds, a, f, min(kb0 + i + C::kStages - 1, nkb - 1));
-  if (i < cnt) compute<C, BF16, S>(fr, kb0 + i, xrd, wrd, szrd, zshift);
+  const int kbf = min(kb0 + i + C::kStages - 1, nkb - 1);
+  // with kSpread the refill's copies go out in four shares, one per k step:
+  // a wave stalls on a copy until the address unit takes it, and issuing
+  // them all at once after the barrier held a small tile's arithmetic back
+  constexpr int kQ = C::kLoads / 4, kR = C::kLoads % 4;     // the first kR shares take one more
+  auto share = [&](auto J) {
+    constexpr int q = J;
+    constexpr int b = q * kQ + (q < kR ? q : kR), e = b + kQ + (q < kR ? 1 : 0);
+    fill_range<C, F, b, e>(lds, a, f, kbf);
+  };
+  if constexpr (!C::kSpread) {
+    fill<C, F>(lds, a, f, kbf);
+    if (i < cnt) compute<C, BF16, S>(fr, kb0 + i, xrd, wrd, szrd, zshift, [](auto) {});
+  } else if (i < cnt) {
+    compute<C, BF16, S>(fr, kb0 + i, xrd, wrd, szrd, zshift, share);
+  } else {
+    fill<C, F>(lds, a, f, kbf);
+  }
 }
 
 template <class C, bool BF16>
