@@ -92,6 +92,24 @@ def copy_calibration(mib):
     del src, dst
 
 
+def warm(fn_list, ms=30.0, cap=5000):
+    """Runs the launches back to back for about `ms` of GPU time, so that the
+    timed ones start at the clock a sustained load settles at (an idle part
+    ramps its clock up over the first milliseconds of work)."""
+    s = torch.cuda.current_stream()
+    a, b = _events()
+    a.record(s)
+    for fn in fn_list:
+        fn(0)
+    b.record(s)
+    torch.cuda.synchronize()
+    n = min(cap, max(1, int(ms / max(a.elapsed_time(b), 1e-3))))
+    for i in range(n):
+        for fn in fn_list:
+            fn(i)
+    torch.cuda.synchronize()
+
+
 def time_launches(fn_list, reps, stream):
     """Eager launches, each bracketed by HIP events on `stream`; returns mean ms per entry."""
     tot = np.zeros(len(fn_list))
@@ -212,11 +230,7 @@ def bench_w8a8(ql, reps):
     fq = lambda r: ql.i8_quant_per_token(X)
     fg = lambda r: ql.i8_gemm_scaled(Aq, Bq, s_a, s_b, azp, adj, bias, out=out)
     fn = lambda r: ql.i8_rmsnorm_quant_per_token(X, gamma, 1e-5)
-    for _ in range(3):
-        fq(0)
-        fg(0)
-        fn(0)
-    torch.cuda.synchronize()
+    warm([fq, fg, fn])
     tq, tg, tn = time_launches([fq, fg, fn], reps, stream)
     ops = 2.0 * M * N * K
     qbytes = M * K * 2 + M * K + M * 4 + M * 4
@@ -240,10 +254,7 @@ def bench_f8(ql, reps):
     out = torch.empty((M, N), dtype=torch.float16, device="cuda")
     fq = lambda r: ql.f8_quant_per_token(X)
     fg = lambda r: ql.f8_gemm_scaled(Aq, Bq, s_a, s_b, bias, out=out)
-    for _ in range(3):
-        fq(0)
-        fg(0)
-    torch.cuda.synchronize()
+    warm([fq, fg])
     tq, tg = time_launches([fq, fg], reps, torch.cuda.current_stream())
     ops = 2.0 * M * N * K
     return {"workload": w.name + ", FP8 E4M3 codes", "M": M, "K": K, "N": N,
@@ -259,9 +270,7 @@ def bench_w4_prefill(ql, reps):
     X = wl.activations(w, M, K, N).cuda()
     Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
     f = lambda r: ql.q4_gemm(X, blobs[0], N, Y=Y)
-    for _ in range(2):
-        f(0)
-    torch.cuda.synchronize()
+    warm([f])
     (t,) = time_launches([f], reps, torch.cuda.current_stream())
     ops = 2.0 * M * N * K
     return {"workload": w.name, "M": M, "K": K, "N": N, "us": round(t * 1e3, 1),
@@ -282,9 +291,7 @@ def bench_mid_m(ql, reps):
             Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
             launchers = [ql.q4_gemm_launcher(X, blobs[r], N, Y) for r in range(R)]
             fns = [lambda r, f=f: f() for f in launchers]
-            for f in launchers:
-                f()
-            torch.cuda.synchronize()
+            warm(fns)
             t = float(np.mean(time_launches(fns, reps, torch.cuda.current_stream())))
             per_case[f"{M}x{K}x{N}"] = {"us": round(t * 1e3, 2),
                                         "TFLOPS": round(2.0 * M * N * K / (t * 1e-3) / 1e12, 1),
@@ -359,13 +366,13 @@ def main():
                               "kernel_GBps": round(r70["kernel_gbs"], 1),
                               "frac_hbm": round(r70["kernel_gbs"] / HBM_PEAK_GBS, 4), "per_case": r70["per_case"]}
         print(f"# decode_70b: kernels {r70['kernel_gbs']:.1f} GB/s", flush=True)
-        also["w8a8_prefill"] = bench_w8a8(ql, 20)
+        also["w8a8_prefill"] = bench_w8a8(ql, 50)
         print(f"# w8a8: {also['w8a8_prefill']}", flush=True)
-        also["w8a8_fp8_prefill"] = bench_f8(ql, 20)
+        also["w8a8_fp8_prefill"] = bench_f8(ql, 50)
         print(f"# w8a8 fp8: {also['w8a8_fp8_prefill']}", flush=True)
-        also["w4a16_prefill"] = bench_w4_prefill(ql, 10)
+        also["w4a16_prefill"] = bench_w4_prefill(ql, 20)
         print(f"# w4a16 prefill: {also['w4a16_prefill']}", flush=True)
-        also["w4a16_mid_m"] = bench_mid_m(ql, 10)
+        also["w4a16_mid_m"] = bench_mid_m(ql, 20)
         print(f"# w4a16 mid-M: {also['w4a16_mid_m']}", flush=True)
 
     cpu = None if args.no_cpu else cpu_baseline()
