@@ -1,6 +1,6 @@
 // Dynamic per-token activation quantization (int8 asymmetric / symmetric and
 // FP8 E4M3), optionally fused with the RMSNorm that produces the row: one
-// wave per row.
+// workgroup of four waves per row.
 //
 // The row's range is found with one reduction ([LQ] "校准：静态与动态":
 // per-token absmax/range at run time costs one extra reduction), then the
@@ -8,13 +8,15 @@
 // in IEEE fp32 with round-half-to-even, so every code is decided exactly as a
 // scalar CPU implementation of the same steps decides it.
 //
-// A wave owns a row: its lanes read 16-byte pieces of it (lane l: pieces
-// l, l + 64, ...; 64 lanes x 16 bytes = one contiguous kilobyte per load), up
-// to kLanePieces of them stay in registers between the reduction and the
-// quantization (so the row is read from HBM once for K <= 4096; the rest of a
-// longer row is read again, mostly from the L2), and the
-// reductions are wave shuffles: no LDS, no barriers, and four rows per
-// workgroup that never wait for each other.
+// A workgroup owns a row: its threads read 16-byte pieces of it (thread t:
+// pieces t, t + 256, ...; a wave's 64 lanes read one contiguous kilobyte per
+// load), up to kLanePieces of them stay in registers between the reduction
+// and the quantization (so the row is read from HBM once for K <= 4096; the
+// rest of a longer row is read again, mostly from the L2).  The reductions
+// are wave shuffles followed by one exchange of the four wave totals through
+// LDS.  Splitting a row over four waves, rather than giving each wave a row,
+// keeps eight waves per SIMD in flight at a few thousand rows, so one row's
+// arithmetic runs while another's loads are outstanding.
 //
 // x / s with a cheap exact rounding.  The codes are functions of the
 // correctly rounded fp32 quotient x / s.  With r = 1 / s and t = x * r (both
@@ -30,8 +32,9 @@
 namespace ql {
 namespace {
 
-constexpr int kRowWaves = 4;       // rows (one per wave) per workgroup
-constexpr int kLanePieces = 8;     // 8-value pieces per lane held in registers (K <= 4096)
+constexpr int kRowWaves = 4;                    // waves per row (one workgroup per row)
+constexpr int kRowThreads = 64 * kRowWaves;
+constexpr int kLanePieces = 2;                  // 8-value pieces per thread held in registers (K <= 4096)
 
 __device__ inline float half_lo(uint32_t v, bool bf16) {
   return bf16 ? __builtin_bit_cast(float, v << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
@@ -99,20 +102,61 @@ __device__ inline void piece_values(uint4 p, uint4 g, float inv, float (&y)[8]) 
 // reduction of the activation quantization fused into the operator that
 // produces the activations; [LQ] "QuaRot：把整个残差流旋转掉" for the form
 // of RMSNorm).
+// Sums of one value per thread over the workgroup: wave shuffles, then the
+// wave totals through LDS, added in wave order, so every thread gets the same
+// result.
+__device__ inline double block_sum(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowWaves; ++w) t += red[w];
+  return t;
+}
+template <bool ASYM>
+__device__ inline void block_range(float& mn, float& mx, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    if constexpr (ASYM) mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = mn;
+    red[kRowWaves + (threadIdx.x >> 6)] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    mn = fminf(mn, red[w]);
+    mx = fmaxf(mx, red[kRowWaves + w]);
+  }
+}
+
+// MODE 0: int8 (ASYM selects the zero point); MODE 1: FP8 E4M3 (symmetric,
+// s = max(absmax, 1e-5) / 448, code = E4M3 rounding of x / s).  NORM: the
+// row is first normalized as y = (x * inv) * gamma with
+// inv = 1 / sqrt(fp32(sum of x^2 in fp64 / K) + eps)  ([QK] §9.9: the per-row
+// reduction of the activation quantization fused into the operator that
+// produces the activations; [LQ] "QuaRot：把整个残差流旋转掉" for the form
+// of RMSNorm).  One workgroup per row.
 template <bool BF16, bool ASYM, int MODE, bool NORM>
-__global__ __launch_bounds__(64 * kRowWaves) void quant_rows_kernel(const uint16_t* __restrict__ X,
-                                                                     const uint16_t* __restrict__ gamma, float eps,
-                                                                     int M, int K, int8_t* __restrict__ Aq,
-                                                                     float* __restrict__ s_a,
-                                                                     int32_t* __restrict__ azp) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * kRowWaves + (int)(threadIdx.x >> 6);
-  if (m >= M) return;                            // a whole wave; nothing here synchronizes waves
+__global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(const uint16_t* __restrict__ X,
+                                                                 const uint16_t* __restrict__ gamma, float eps,
+                                                                 int M, int K, int8_t* __restrict__ Aq,
+                                                                 float* __restrict__ s_a,
+                                                                 int32_t* __restrict__ azp) {
+  __shared__ double red_ss[kRowWaves];
+  __shared__ float red_range[2 * kRowWaves];
+  const int tid = threadIdx.x;
+  const int m = blockIdx.x;
   const uint4* xv = reinterpret_cast<const uint4*>(X + (size_t)m * K);
   const uint4* gv = reinterpret_cast<const uint4*>(gamma);
   const int pieces = K / 8;
 
-  // the lane's register-resident pieces, converted to fp32 once (zero past the row)
+  // the thread's register-resident pieces tid + kRowThreads * r, converted to
+  // fp32 once (zero past the row)
   float y[kLanePieces][8];
   uint4 g[kLanePieces];
   // every load is issued before the first wait: indices past the row re-read
@@ -120,18 +164,19 @@ __global__ __launch_bounds__(64 * kRowWaves) void quant_rows_kernel(const uint16
   uint4 xp[kLanePieces];
 #pragma unroll
   for (int r = 0; r < kLanePieces; ++r) {
-    const int pc = min(lane + 64 * r, pieces - 1);
+    const int pc = min(tid + kRowThreads * r, pieces - 1);
     xp[r] = xv[pc];
     if constexpr (NORM) g[r] = gv[pc];
   }
 #pragma unroll
   for (int r = 0; r < kLanePieces; ++r) {
-    const uint32_t keep = lane + 64 * r < pieces ? 0xFFFFFFFFu : 0u;
+    const uint32_t keep = tid + kRowThreads * r < pieces ? 0xFFFFFFFFu : 0u;
     xp[r] = make_uint4(xp[r].x & keep, xp[r].y & keep, xp[r].z & keep, xp[r].w & keep);
     if constexpr (NORM) g[r] = make_uint4(g[r].x & keep, g[r].y & keep, g[r].z & keep, g[r].w & keep);
     else g[r] = make_uint4(0, 0, 0, 0);
     piece_values<BF16, false>(xp[r], xp[r], 1.0f, y[r]);
   }
+  constexpr int kHeld = kRowThreads * kLanePieces;           // pieces held in registers
 
   // ---- RMSNorm: mean square from the fp64 sum of the exact squares
   float inv = 1.0f;
@@ -141,15 +186,13 @@ __global__ __launch_bounds__(64 * kRowWaves) void quant_rows_kernel(const uint16
     for (int r = 0; r < kLanePieces; ++r)
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss += (double)y[r][i] * (double)y[r][i];
-    for (int p = lane + 64 * kLanePieces; p < pieces; p += 64) {
+    for (int p = tid + kHeld; p < pieces; p += kRowThreads) {
       float t[8];
       piece_values<BF16, false>(xv[p], xv[p], 1.0f, t);
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss += (double)t[i] * (double)t[i];
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-    ss = __shfl(ss, 0);                          // one value for the whole row
+    ss = block_sum(ss, red_ss);
     const float ms = (float)(ss / (double)K);
     inv = 1.0f / sqrtf(ms + eps);
 #pragma unroll
@@ -178,16 +221,12 @@ __global__ __launch_bounds__(64 * kRowWaves) void quant_rows_kernel(const uint16
   };
 #pragma unroll
   for (int r = 0; r < kLanePieces; ++r) fold8(y[r]);         // zero pieces are inside the range
-  for (int p = lane + 64 * kLanePieces; p < pieces; p += 64) {
+  for (int p = tid + kHeld; p < pieces; p += kRowThreads) {
     float t[8];
     piece_values<BF16, NORM>(xv[p], NORM ? gv[p] : make_uint4(0, 0, 0, 0), inv, t);
     fold8(t);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    if constexpr (ASYM) mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
+  block_range<ASYM>(mn, mx, red_range);
 
   float s, z;
   if constexpr (ASYM) {
@@ -197,7 +236,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void quant_rows_kernel(const uint16
     s = fmaxf(mx, 1e-5f) / (MODE == 1 ? 448.0f : 127.0f);
     z = 0.0f;
   }
-  if (lane == 0) {
+  if (tid == 0) {
     s_a[m] = s;
     if constexpr (ASYM) azp[m] = (int32_t)z;
   }
@@ -231,10 +270,10 @@ __global__ __launch_bounds__(64 * kRowWaves) void quant_rows_kernel(const uint16
   uint2* qo = reinterpret_cast<uint2*>(Aq + (size_t)m * K);
 #pragma unroll
   for (int r = 0; r < kLanePieces; ++r) {
-    const int p = lane + 64 * r;
+    const int p = tid + kRowThreads * r;
     if (p < pieces) qo[p] = quant(y[r]);
   }
-  for (int p = lane + 64 * kLanePieces; p < pieces; p += 64) {
+  for (int p = tid + kHeld; p < pieces; p += kRowThreads) {
     float t[8];
     piece_values<BF16, NORM>(xv[p], NORM ? gv[p] : make_uint4(0, 0, 0, 0), inv, t);
     qo[p] = quant(t);
@@ -246,7 +285,7 @@ hipError_t launch_rows(const void* X, bool bf16, int M, int K, const void* gamma
                        int32_t* azp, hipStream_t st) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* g = static_cast<const uint16_t*>(gamma);
-  const dim3 grid((M + kRowWaves - 1) / kRowWaves), block(64 * kRowWaves);
+  const dim3 grid(M), block(kRowThreads);
   if (bf16) {
     if (azp)
       hipLaunchKernelGGL((quant_rows_kernel<true, true, MODE, NORM>), grid, block, 0, st, x, g, eps, M, K, Aq, s_a, azp);
