@@ -110,22 +110,24 @@ def warm(fn_list, ms=30.0, cap=5000):
     torch.cuda.synchronize()
 
 
-def time_launches(fn_list, reps, stream):
-    """Eager launches, each bracketed by HIP events on `stream`; returns mean ms per entry."""
-    tot = np.zeros(len(fn_list))
-    pairs = [[_events() for _ in fn_list] for _ in range(reps)]
-    for r in range(reps):
-        for i, fn in enumerate(fn_list):
-            a, b = pairs[r][i]
-            a.record(stream)
+def time_launches(fn_list, reps, stream, warm_ms=10.0):
+    """Mean ms per launch of each entry: fn(0) .. fn(reps - 1) back to back
+    between two HIP events on `stream`, one entry at a time, each after
+    `warm_ms` of its own launches (so every kernel is timed at the clock its
+    own load settles at, not at the one the previous entry left).  The
+    entries are launchers with their arguments marshalled once, so the host
+    stays ahead of the device and the interval holds nothing but the kernels."""
+    out = np.zeros(len(fn_list))
+    for i, fn in enumerate(fn_list):
+        warm([fn], warm_ms)
+        a, b = _events()
+        a.record(stream)
+        for r in range(reps):
             fn(r)
-            b.record(stream)
-    torch.cuda.synchronize()
-    for r in range(reps):
-        for i in range(len(fn_list)):
-            a, b = pairs[r][i]
-            tot[i] += a.elapsed_time(b)
-    return tot / reps
+        b.record(stream)
+        torch.cuda.synchronize()
+        out[i] = a.elapsed_time(b) / reps
+    return out
 
 
 def bench_decode(ql, wname, steps, warmup, use_graphs=False):
@@ -198,8 +200,8 @@ def bench_decode(ql, wname, steps, warmup, use_graphs=False):
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / steps
 
-    # per-kernel durations (eager, event-bracketed) for the roofline
-    fns = [(lambda r, c=c: launch(c, r % R)) for c in cases]
+    # per-case durations (each case alone, back to back over the weight copies)
+    fns = [(lambda r, i=i: launchers[r % R][i]()) for i in range(len(cases))]
     per = time_launches(fns, max(steps, 10), stream)
     kern_ms = float(per.sum())
     per_case = []
@@ -215,21 +217,32 @@ def bench_decode(ql, wname, steps, warmup, use_graphs=False):
     }
 
 
+def _activation_copies(X):
+    """Copies of an activation tensor that together exceed the last-level
+    cache, so that a loop over them reads its inputs from HBM."""
+    return [X.clone() for _ in range(_copies_for(X.numel() * X.element_size()))]
+
+
 def bench_w8a8(ql, reps):
     w = wl.WORKLOADS["w8a8_prefill"]
     M, (K, N) = w.Ms[0], w.shapes[0]
     X = wl.activations(w, M, K, N).cuda()
+    Xs = _activation_copies(X)
     Bq, s_b = ql.i8_quant_weight_host(torch.from_numpy(wl.weight(w, K, N)))
     adj = ql.i8_azp_adj(Bq)
     Bq, s_b, adj = Bq.cuda(), s_b.cuda(), adj.cuda()
     bias = wl.bias(w, N).cuda()
     Aq, s_a, azp = ql.i8_quant_per_token(X)
+    Aq2, s_a2, azp2 = ql.i8_quant_per_token(X)   # the timed quant launches write here
     out = torch.empty((M, N), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
     gamma = wl.norm_weight(w, K).cuda()
-    fq = lambda r: ql.i8_quant_per_token(X)
-    fg = lambda r: ql.i8_gemm_scaled(Aq, Bq, s_a, s_b, azp, adj, bias, out=out)
-    fn = lambda r: ql.i8_rmsnorm_quant_per_token(X, gamma, 1e-5)
+    lq = [ql.launcher("i8_quant_per_token", x, x.dtype, M, K, Aq2, s_a2, azp2) for x in Xs]
+    ln = [ql.launcher("i8_rmsnorm_quant_per_token", x, x.dtype, M, K, gamma, 1e-5, Aq2, s_a2, azp2) for x in Xs]
+    lg = ql.launcher("i8_gemm_scaled", Aq, Bq, M, N, K, s_a, M, s_b, N, azp, adj, bias, out, torch.float16, None)
+    fq = lambda r: lq[r % len(lq)]()
+    fg = lambda r: lg()
+    fn = lambda r: ln[r % len(ln)]()
     warm([fq, fg, fn])
     tq, tg, tn = time_launches([fq, fg, fn], reps, stream)
     ops = 2.0 * M * N * K
@@ -251,9 +264,12 @@ def bench_f8(ql, reps):
     Bq, s_b = Bq.cuda(), s_b.cuda()
     bias = wl.bias(w, N).cuda()
     Aq, s_a = ql.f8_quant_per_token(X)
+    Aq2, s_a2 = ql.f8_quant_per_token(X)         # the timed quant launches write here
     out = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    fq = lambda r: ql.f8_quant_per_token(X)
-    fg = lambda r: ql.f8_gemm_scaled(Aq, Bq, s_a, s_b, bias, out=out)
+    lq = [ql.launcher("f8_quant_per_token", x, x.dtype, M, K, Aq2, s_a2) for x in _activation_copies(X)]
+    lg = ql.launcher("f8_gemm_scaled", Aq, Bq, M, N, K, s_a, M, s_b, N, bias, out, torch.float16)
+    fq = lambda r: lq[r % len(lq)]()
+    fg = lambda r: lg()
     warm([fq, fg])
     tq, tg = time_launches([fq, fg], reps, torch.cuda.current_stream())
     ops = 2.0 * M * N * K
@@ -269,7 +285,8 @@ def bench_w4_prefill(ql, reps):
     _, blobs = _prepare_w4(ql, w, K, N, 1)
     X = wl.activations(w, M, K, N).cuda()
     Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
-    f = lambda r: ql.q4_gemm(X, blobs[0], N, Y=Y)
+    lf = ql.q4_gemm_launcher(X, blobs[0], N, Y)
+    f = lambda r: lf()
     warm([f])
     (t,) = time_launches([f], reps, torch.cuda.current_stream())
     ops = 2.0 * M * N * K

@@ -246,6 +246,37 @@ def q4_gemm_launcher(X, packed, N, Y, group=GROUP, stream=None):
     return launch
 
 
+def launcher(name, *args, stream=None):
+    """Returns a callable that calls the device entry point `name` (i8_gemm_scaled,
+    i8_quant_per_token, ...) with its arguments marshalled once: a tensor
+    becomes its data pointer, a torch dtype its ql_dtype code, None a NULL
+    pointer, other values pass unchanged, and the stream argument (torch's
+    current stream unless one is given) is appended.  For tight launch loops,
+    where the checks and output allocations of the functions above would take
+    more host time than the kernel takes on the device; the caller keeps the
+    tensors alive, and the C entry point still validates every call."""
+    f = getattr(lib(), name)
+    tensors = [a for a in args if isinstance(a, torch.Tensor)]
+    if not tensors or any(t.device.type != "cuda" for t in tensors):
+        raise QLError(f"{name}: launcher needs device tensors")
+    conv = []
+    for a in args:
+        if isinstance(a, torch.Tensor):
+            conv.append(C.c_void_p(a.data_ptr()))
+        elif isinstance(a, torch.dtype):
+            conv.append(_dtype_code(a))
+        else:
+            conv.append(a)
+    conv.append(_stream(tensors[0], stream))
+
+    def launch(*_):
+        rc = f(*conv)
+        if rc != 0:
+            _check(rc, name)
+
+    return launch
+
+
 # ---------------------------------------------------------------- W8A8
 
 def i8_quant_weight_host(W):

@@ -304,3 +304,13 @@ def test_q4_act_order_validation():
     assert L.q4_permute_columns(P, 0, 4, 16, P, FAKE_MIS, None) == QL_ERR_ALIGN
     assert L.q4_permute_columns(P, 0, 4, 16, P, P, None) == QL_ERR_UNSUPPORTED      # X == Xp
     assert L.q4_permute_columns(None, 0, 0, 16, None, None, None) == QL_OK
+
+
+def test_launcher_rejects_host_tensors():
+    """ql.launcher marshals device buffers only; host tensors are refused
+    before anything reaches the library."""
+    X = torch.zeros((4, 16), dtype=torch.float16)
+    with pytest.raises(ql.QLError):
+        ql.launcher("i8_quant_per_token", X, X.dtype, 4, 16, X, X, X)
+    with pytest.raises(ql.QLError):
+        ql.launcher("i8_quant_per_token", 1, 2, 3)

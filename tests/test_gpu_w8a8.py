@@ -141,3 +141,31 @@ def test_gemm_wide_zero_points():
     check_gemm(Aq, Bq, s_a, s_b, azp, adj)
     wide_adj = adj.astype(np.int64) + (1 << 24)    # a column sum past 24 bits, any zero points
     check_gemm(Aq, Bq, s_a, s_b, (azp % 64).astype(np.int32), wide_adj.astype(np.int32))
+
+
+def test_launcher_matches_the_binding():
+    """The pre-marshalled launcher (used for tight launch loops) gives the
+    same bytes as the checked binding, for the quant and the GEMM entry
+    points, on two calls in a row."""
+    w = wl.WORKLOADS["w8a8_prefill"]
+    M, K, N = 300, 1024, 384
+    X = wl.activations(w, M, K, N).cuda()
+    Aq, s_a, azp = ql.i8_quant_per_token(X)
+    Aq2, s_a2, azp2 = torch.empty_like(Aq), torch.empty_like(s_a), torch.empty_like(azp)
+    lq = ql.launcher("i8_quant_per_token", X, X.dtype, M, K, Aq2, s_a2, azp2)
+    Bq, s_b = ql.i8_quant_weight_host(torch.from_numpy(wl.weight(w, K, N)))
+    adj = ql.i8_azp_adj(Bq)
+    Bq, s_b, adj = Bq.cuda(), s_b.cuda(), adj.cuda()
+    bias = wl.bias(w, N).cuda()
+    out = ql.i8_gemm_scaled(Aq, Bq, s_a, s_b, azp, adj, bias)
+    out2 = torch.empty_like(out)
+    lg = ql.launcher("i8_gemm_scaled", Aq2, Bq, M, N, K, s_a2, M, s_b, N, azp2, adj, bias, out2, out.dtype, None)
+    for _ in range(2):
+        lq()
+        lg()
+        torch.cuda.synchronize()
+        assert torch.equal(Aq2, Aq) and torch.equal(azp2, azp)
+        assert torch.equal(s_a2.view(torch.int32), s_a.view(torch.int32))
+        assert torch.equal(out2, out)
+        for t in (Aq2, s_a2, azp2, out2):
+            t.zero_()
