@@ -194,29 +194,36 @@ __device__ inline uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
 }
 
-// hides a value from the optimizer (keeps the byte-lane form of the split
-// nibbles, which converts to float in one instruction per byte)
-__device__ inline uint32_t opaque(uint32_t v) {
+// a constant materialized in a vector register, out of the optimizer's sight
+__device__ inline uint32_t in_vgpr(uint32_t v) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" : "+v"(v));
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(v));
 #endif
   return v;
 }
 
 // One word of 8 codes (code i at nibble position (i & 1) * 4 + (i >> 1)) ->
 // the MFMA B operand of 8 consecutive k: register r = (k 2r, k 2r + 1), each
-// s * (q - z) rounded once to the 16-bit type.  Splitting the word into its
-// low and high nibbles puts codes 0, 4, 1, 5 and 2, 6, 3, 7 in byte lanes,
-// which convert to float one byte at a time.
+// s * (q - z) rounded once to the 16-bit type.  Masking (w >> 4r) with
+// 0x000F000F and setting the bits of fp16 1024.0 puts nibbles r and r + 4
+// (codes 2r and 2r + 1) into the two halves of a register as the exact fp16
+// values 1024 + q.  One fused multiply-add per value with its fp16 operand,
+// (1024 + q) * s + noff, where noff = -(1024 + z) * s is exact in fp32 (an
+// 11-bit integer times an fp16 scale), yields s * (q - z) exactly (at most
+// 15 significant bits), which is then rounded once to the 16-bit type.
+//   mask, magic: 0x000F000F and 0x64006400 in registers (see in_vgpr), so
+//   that each register takes one v_and_or_b32, which has no literal form
 template <bool BF16>
-__device__ inline u32x4 dequant8(uint32_t w, float s, float nzs) {
-  const uint32_t lo = opaque(w & 0x0F0F0F0Fu), hi = opaque((w >> 4) & 0x0F0F0F0Fu);
-  const float c0 = (float)(lo & 0xFFu), c4 = (float)((lo >> 8) & 0xFFu);
-  const float c1 = (float)((lo >> 16) & 0xFFu), c5 = (float)(lo >> 24);
-  const float c2 = (float)(hi & 0xFFu), c6 = (float)((hi >> 8) & 0xFFu);
-  const float c3 = (float)((hi >> 16) & 0xFFu), c7 = (float)(hi >> 24);
-  return u32x4{pack2<BF16>(fmaf(c0, s, nzs), fmaf(c1, s, nzs)), pack2<BF16>(fmaf(c2, s, nzs), fmaf(c3, s, nzs)),
-               pack2<BF16>(fmaf(c4, s, nzs), fmaf(c5, s, nzs)), pack2<BF16>(fmaf(c6, s, nzs), fmaf(c7, s, nzs))};
+__device__ inline u32x4 dequant8(uint32_t w, float s, float noff, uint32_t mask, uint32_t magic) {
+  u32x4 out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t h = ((w >> (4 * r)) & mask) | magic;
+    const float lo = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu)), s, noff);
+    const float hi = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16)), s, noff);
+    out[r] = pack2<BF16>(lo, hi);
+  }
+  return out;
 }
 
 template <bool BF16>
@@ -349,14 +356,15 @@ __device__ __forceinline__ void compute(Frag<C>& fr, int kb, const uint32_t (&xr
     after_wait(sv[t]);
     after_wait(zv[t]);
     s[t] = (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[t] >> (16 * h)));
-    nzs[t] = -(float)((zv[t] >> (zshift + 4 * h)) & 0xFu) * s[t];
+    nzs[t] = -(1024.0f + (float)((zv[t] >> (zshift + 4 * h)) & 0xFu)) * s[t];   // exact
   }
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) after_wait(xa[0][mt]);
   // B operands of step j: chunk j / 2, word j % 2 of the lane's pair
   u32x4 b[2][kNTW];
+  const uint32_t mask = in_vgpr(0x000F000Fu), magic = in_vgpr(0x64006400u);
 #pragma unroll
-  for (int t = 0; t < kNTW; ++t) b[0][t] = dequant8<BF16>(wv[0][t][0], s[t], nzs[t]);
+  for (int t = 0; t < kNTW; ++t) b[0][t] = dequant8<BF16>(wv[0][t][0], s[t], nzs[t], mask, magic);
   static_for<0, 4>([&](auto J) {
     constexpr int j = J;
     constexpr int cur = kXBuf == 2 ? (j & 1) : 0;
@@ -377,7 +385,7 @@ __device__ __forceinline__ void compute(Frag<C>& fr, int kb, const uint32_t (&xr
     if constexpr (j < 3) {
 #pragma unroll
       for (int t = 0; t < kNTW; ++t)
-        b[(j & 1) ^ 1][t] = dequant8<BF16>(wv[(j + 1) >> 1][t][(j + 1) & 1], s[t], nzs[t]);
+        b[(j & 1) ^ 1][t] = dequant8<BF16>(wv[(j + 1) >> 1][t][(j + 1) & 1], s[t], nzs[t], mask, magic);
     }
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
