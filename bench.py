@@ -45,7 +45,7 @@ MALL_DEFEAT_BYTES = 1 << 30
 # same run.  It belongs to one version of the kernel source: when the source
 # hash differs, the figure is stale and `traffic` is reported as null.
 TRAFFIC = {"source_sha256": "a520aa56e5ef08ed818808b749d50a30805789505bc0bd79ee906c7941d1fbd3",
-           "bytes_per_launch": 19388044}
+           "bytes_per_launch": 19387913}
 
 
 def w4a16_bytes(M, K, N, group=128, e=2):
@@ -92,6 +92,9 @@ def copy_calibration(mib):
     del src, dst
 
 
+WARM_MS = 10.0                    # warm-up per timed kernel (--warm-ms)
+
+
 def warm(fn_list, ms=30.0, cap=5000):
     """Runs the launches back to back for about `ms` of GPU time, so that the
     timed ones start at the clock a sustained load settles at (an idle part
@@ -110,7 +113,7 @@ def warm(fn_list, ms=30.0, cap=5000):
     torch.cuda.synchronize()
 
 
-def time_launches(fn_list, reps, stream, warm_ms=10.0):
+def time_launches(fn_list, reps, stream, warm_ms=None):
     """Mean ms per launch of each entry: fn(0) .. fn(reps - 1) back to back
     between two HIP events on `stream`, one entry at a time, each after
     `warm_ms` of its own launches (so every kernel is timed at the clock its
@@ -119,7 +122,7 @@ def time_launches(fn_list, reps, stream, warm_ms=10.0):
     stays ahead of the device and the interval holds nothing but the kernels."""
     out = np.zeros(len(fn_list))
     for i, fn in enumerate(fn_list):
-        warm([fn], warm_ms)
+        warm([fn], WARM_MS if warm_ms is None else warm_ms)
         a, b = _events()
         a.record(stream)
         for r in range(reps):
@@ -243,7 +246,6 @@ def bench_w8a8(ql, reps):
     fq = lambda r: lq[r % len(lq)]()
     fg = lambda r: lg()
     fn = lambda r: ln[r % len(ln)]()
-    warm([fq, fg, fn])
     tq, tg, tn = time_launches([fq, fg, fn], reps, stream)
     ops = 2.0 * M * N * K
     qbytes = M * K * 2 + M * K + M * 4 + M * 4
@@ -270,7 +272,6 @@ def bench_f8(ql, reps):
     lg = ql.launcher("f8_gemm_scaled", Aq, Bq, M, N, K, s_a, M, s_b, N, bias, out, torch.float16)
     fq = lambda r: lq[r % len(lq)]()
     fg = lambda r: lg()
-    warm([fq, fg])
     tq, tg = time_launches([fq, fg], reps, torch.cuda.current_stream())
     ops = 2.0 * M * N * K
     return {"workload": w.name + ", FP8 E4M3 codes", "M": M, "K": K, "N": N,
@@ -287,7 +288,6 @@ def bench_w4_prefill(ql, reps):
     Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
     lf = ql.q4_gemm_launcher(X, blobs[0], N, Y)
     f = lambda r: lf()
-    warm([f])
     (t,) = time_launches([f], reps, torch.cuda.current_stream())
     ops = 2.0 * M * N * K
     return {"workload": w.name, "M": M, "K": K, "N": N, "us": round(t * 1e3, 1),
@@ -308,7 +308,6 @@ def bench_mid_m(ql, reps):
             Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
             launchers = [ql.q4_gemm_launcher(X, blobs[r], N, Y) for r in range(R)]
             fns = [lambda r, f=f: f() for f in launchers]
-            warm(fns)
             t = float(np.mean(time_launches(fns, reps, torch.cuda.current_stream())))
             per_case[f"{M}x{K}x{N}"] = {"us": round(t * 1e3, 2),
                                         "TFLOPS": round(2.0 * M * N * K / (t * 1e-3) / 1e12, 1),
@@ -351,16 +350,20 @@ def cpu_baseline(budget_s=20.0):
 
 
 def main():
+    global WARM_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS, metavar="MS",
+                    help="back-to-back launches of a kernel before its timed block (small under a profiler)")
     ap.add_argument("--graphs", action="store_true", help="replay the decode steps as HIP graphs")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for byte counters)")
     args = ap.parse_args()
+    WARM_MS = args.warm_ms
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer would shard "
               "column-parallel with no exchange); run with --gpus 1", file=sys.stderr)
