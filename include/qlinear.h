@@ -193,6 +193,18 @@ int q4_unpack(const void* packed, size_t packed_bytes, int N, int K, int group,
 int q4_gemm(const void* X, int x_dtype, int M, int K, int N,
             const void* packed, size_t packed_bytes, int group, void* Y, void* stream);
 
+/*
+ * q4_gemm_tile_shape — which workgroup tile q4_gemm uses for an M x N x K
+ * product (host; a diagnostic for tests and tuning, no device work).
+ * *rows, *cols: the tile's rows and columns (256 x 256 … 32 x 32, also
+ * 64 x 128 and 32 x 64) for M > 16; 0, 0 for M <= 16 (the decode kernel).
+ * The choice depends on the shape only ([LQ] W4A16 section: the batch size
+ * decides between the bandwidth- and compute-bound regimes).
+ * Errors: QL_ERR_NULL; QL_ERR_SHAPE unless M >= 0, N > 0, K > 0,
+ *         K % 128 == 0.
+ */
+int q4_gemm_tile_shape(int M, int N, int K, int* rows, int* cols);
+
 /* -------------------------------------------------------------------------
  * Act-order (g_idx).  [LQ] GPTQ section, "工程细节", its act-order item:
  * input channels are quantized in decreasing activation energy, groups are

@@ -44,6 +44,7 @@ def lib():
             "q4_pack": (I, [P, P, P, I, I, I, P, Z]),
             "q4_unpack": (I, [P, Z, I, I, I, P, P, P]),
             "q4_gemm": (I, [P, I, I, I, I, P, Z, I, P, P]),
+            "q4_gemm_tile_shape": (I, [I, I, I, P, P]),
             "q4_quantize_act_order_host": (I, [P, I, I, I, P, P, P, P]),
             "q4_pack_act_order": (I, [P, P, P, P, I, I, I, P, Z, P]),
             "q4_permute_columns": (I, [P, I, I, I, P, P, P]),
@@ -222,6 +223,14 @@ def q4_permute_columns(X, perm, Xp=None, stream=None):
 def q4_gemm_act_order(X, packed, perm, N, group=GROUP, Y=None, stream=None):
     """Y = X · dequant(W)ᵀ for an act-order blob: q4_permute_columns, then q4_gemm."""
     return q4_gemm(q4_permute_columns(X, perm, stream=stream), packed, N, group, Y, stream)
+
+
+def q4_gemm_tile_shape(M, N, K):
+    """(rows, cols) of the workgroup tile q4_gemm uses for M x N x K; (0, 0)
+    when M <= 16 (the decode kernel)."""
+    r, c = C.c_int(0), C.c_int(0)
+    _check(lib().q4_gemm_tile_shape(M, N, K, C.byref(r), C.byref(c)), "q4_gemm_tile_shape")
+    return r.value, c.value
 
 
 def q4_gemm_launcher(X, packed, N, Y, group=GROUP, stream=None):

@@ -74,6 +74,19 @@ int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed,
   return hip_status("q4_gemm", ql::launch_q4_gemm(X, bf16, M, K, N, static_cast<const uint8_t*>(packed), L, Y, st));
 }
 
+int q4_gemm_tile_shape(int M, int N, int K, int* rows, int* cols) {
+  if (!rows || !cols) return ql::set_error(QL_ERR_NULL, "q4_gemm_tile_shape: NULL rows or cols");
+  if (M < 0 || N <= 0 || K <= 0 || K % ql::kGroup)
+    return ql::set_error(QL_ERR_SHAPE, "q4_gemm_tile_shape: need M >= 0, N > 0, K > 0, K %% 128 == 0 (got %d, %d, %d)",
+                         M, N, K);
+  if (M <= ql::kGemvMaxM) {
+    *rows = *cols = 0;
+    return QL_OK;
+  }
+  ql::gemm_tile_shape(M, N, K, rows, cols);
+  return QL_OK;
+}
+
 int q4_permute_columns(const void* X, int x_dtype, int M, int K, const int32_t* perm, void* Xp, void* stream) {
   if (M < 0 || K <= 0 || K % 8)
     return ql::set_error(QL_ERR_SHAPE, "q4_permute_columns: need M >= 0, K > 0, K %% 8 == 0 (got %d, %d)", M, K);

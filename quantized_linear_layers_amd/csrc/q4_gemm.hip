@@ -581,32 +581,54 @@ hipError_t launch_cfg(const GemmArgs& a, bool bf16, hipStream_t st) {
 
 }  // namespace
 
-// Square tile edge for an M x N x K product.  Every tile size has 8 waves and
-// the same LDS stages, so one workgroup fills a compute unit, and with few
-// tokens its K loop runs at a near-constant time per stage (two stages in
-// flight: memory round trips, not arithmetic, set the pace).  The estimate is
+// Workgroup tiles of the large-M kernel, largest first.  Every configuration
+// has 8 waves and about 126-130 KB of LDS stages, so one workgroup fills a
+// compute unit, and with few tokens its K loop runs at a near-constant time
+// per step (memory round trips, not arithmetic, set the pace).  step: that
+// time in us, measured on the Llama-2 7B / 70B layers.  The two non-square
+// tiles spend fewer LDS bytes per stage on activations (half the columns'
+// share of each stage instead of four fifths), so their rings hold five
+// stages.
+struct TileOpt {
+  int bm, bn, wk;
+  double step;
+};
+constexpr TileOpt kTiles[] = {
+    {256, 256, 1, 1.38},   // Cfg<8, 8, 1, 3>
+    {128, 128, 2, 0.92},   // Cfg<4, 4, 2, 3>
+    {64, 128, 2, 0.72},    // Cfg<2, 4, 2, 5>
+    {64, 64, 4, 0.76},     // Cfg<2, 2, 4, 3>
+    {32, 64, 4, 0.62},     // Cfg<1, 2, 4, 5>
+    {32, 32, 8, 0.72},     // Cfg<1, 1, 8, 3>
+};
+constexpr int kNumTiles = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
+
+// Tile (index into kTiles) for an M x N x K product: the smallest estimate
 // rounds x (ramp + K steps of a K-group x step time), with 256 workgroups a
-// round and the step times measured on the Llama-2 7B / 70B layers (0.72,
-// 0.76, 0.92 and 1.38 us for tiles 32 .. 256, ramp 2.5 us); the smallest
-// estimate wins, ties going to the larger tile.
+// round and a ramp of 2.5 us a round; ties go to the earlier (larger) tile.
 int gemm_tile(int M, int N, int K) {
 #ifdef QL_GEMM_TILE
   if (const char* e = getenv("QL_GEMM_TILE")) return atoi(e);
 #endif
   const long nkb = K / BK;
-  int best = 256;
+  int best = 0;
   double best_cost = 0.0;
-  for (int t = 256; t >= 32; t /= 2) {
-    const long wk = 256 / t;                             // K-groups of the tile's configuration
-    const long wgs = (long)((M + t - 1) / t) * ((N + t - 1) / t);
-    const double step = t == 256 ? 1.38 : t == 128 ? 0.92 : t == 64 ? 0.76 : 0.72;
-    const double cost = (double)((wgs + 255) / 256) * (2.5 + (double)((nkb + wk - 1) / wk) * step);
-    if (t == 256 || cost < best_cost) {
+  for (int t = 0; t < kNumTiles; ++t) {
+    const TileOpt& o = kTiles[t];
+    const long wgs = (long)((M + o.bm - 1) / o.bm) * ((N + o.bn - 1) / o.bn);
+    const double cost = (double)((wgs + 255) / 256) * (2.5 + (double)((nkb + o.wk - 1) / o.wk) * o.step);
+    if (t == 0 || cost < best_cost) {
       best = t;
       best_cost = cost;
     }
   }
   return best;
+}
+
+void gemm_tile_shape(int M, int N, int K, int* rows, int* cols) {
+  const TileOpt& o = kTiles[gemm_tile(M, N, K)];
+  *rows = o.bm;
+  *cols = o.bn;
 }
 
 hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const uint8_t* blob, const Q4Layout& L,
@@ -624,9 +646,11 @@ hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const u
   a.Z = blob + L.z_off;
   a.Y = static_cast<uint16_t*>(Y);
   switch (gemm_tile(M, N, K)) {
-    case 32: return launch_cfg<Cfg<1, 1, 8, 3>>(a, bf16, st);
-    case 64: return launch_cfg<Cfg<2, 2, 4, 3>>(a, bf16, st);
-    case 128: return launch_cfg<Cfg<4, 4, 2, 3>>(a, bf16, st);
+    case 1: return launch_cfg<Cfg<4, 4, 2, 3>>(a, bf16, st);
+    case 2: return launch_cfg<Cfg<2, 4, 2, 5>>(a, bf16, st);
+    case 3: return launch_cfg<Cfg<2, 2, 4, 3>>(a, bf16, st);
+    case 4: return launch_cfg<Cfg<1, 2, 4, 5>>(a, bf16, st);
+    case 5: return launch_cfg<Cfg<1, 1, 8, 3>>(a, bf16, st);
     default: break;
   }
   // 256 x 256 tiles, one workgroup per compute unit.  When their last round

@@ -82,8 +82,10 @@ struct GemvPlan {
 
 GemvPlan plan_q4_gemv(int M, int N, int K);
 
-// square tile edge the large-M kernel uses for an M x N x K product (32 .. 256)
+// workgroup tile the large-M kernel uses for an M x N x K product: index
+// into its table, and the tile's rows and columns
 int gemm_tile(int M, int N, int K);
+void gemm_tile_shape(int M, int N, int K, int* rows, int* cols);
 // token counts served by the decode-family kernel; larger M takes the GEMM
 constexpr int kGemvMaxM = 16;
 hipError_t launch_q4_gemv(const void* X, bool bf16, int M, int K, int N,

@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -314,3 +314,22 @@ def test_launcher_rejects_host_tensors():
         ql.launcher("i8_quant_per_token", X, X.dtype, 4, 16, X, X, X)
     with pytest.raises(ql.QLError):
         ql.launcher("i8_quant_per_token", 1, 2, 3)
+
+
+def test_q4_gemm_tile_shape():
+    """The tile diagnostic: the decode kernel for M <= 16, a square or one of
+    the two non-square tiles above, and the documented errors."""
+    assert ql.q4_gemm_tile_shape(16, 4096, 4096) == (0, 0)
+    assert ql.q4_gemm_tile_shape(4096, 14336, 4096) == (256, 256)
+    assert ql.q4_gemm_tile_shape(32, 11008, 4096) == (32, 64)
+    assert ql.q4_gemm_tile_shape(128, 11008, 4096) == (64, 128)
+    assert ql.q4_gemm_tile_shape(32, 4096, 4096) == (32, 32)
+    for M in (17, 64, 200, 1000):
+        for N in (72, 4096, 11008):
+            assert ql.q4_gemm_tile_shape(M, N, 4096) in {(256, 256), (128, 128), (64, 128), (64, 64), (32, 64),
+                                                        (32, 32)}
+    L = ql.lib()
+    r, c = C.c_int(), C.c_int()
+    assert L.q4_gemm_tile_shape(32, 64, 100, C.byref(r), C.byref(c)) == QL_ERR_SHAPE
+    assert L.q4_gemm_tile_shape(32, 0, 128, C.byref(r), C.byref(c)) == QL_ERR_SHAPE
+    assert L.q4_gemm_tile_shape(32, 64, 128, None, C.byref(c)) == QL_ERR_NULL

@@ -86,9 +86,10 @@ def test_mid_m_7b(M, K, N):
     check(wl.weight(w, K, N), wl.activations(w, M, K, N))
 
 
-# shapes whose token and channel counts select each square tile of the large-M
-# kernel (32, 64, 128: the K range split among 8, 4, 2 K-groups of waves,
-# with uneven and empty runs for K = 1152 and 384); 256 is the prefill test
+# shapes whose token and channel counts select the tiles of the large-M kernel
+# (32 x 32, 32 x 64, 64 x 64, 64 x 128, 128 x 128: the K range split among
+# 8, 4, 4, 2, 2 K-groups of waves, with uneven and empty runs for K = 1152
+# and 384); 256 x 256 is the prefill test
 @pytest.mark.parametrize("M,K,N,dtype", [(200, 1152, 1000, torch.float16), (77, 384, 4160, torch.bfloat16),
                                          (256, 1152, 4096, torch.float16), (300, 2560, 4000, torch.bfloat16),
                                          (512, 1152, 8192, torch.bfloat16), (400, 384, 8000, torch.float16)])
@@ -97,6 +98,24 @@ def test_gemm_tiles(M, K, N, dtype):
     W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
     X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
     cols = np.sort(r.choice(N, min(N, 512), replace=False))
+    check(W, X, cols=cols)
+
+
+# shapes that select the two non-square tiles (32 x 64 with the K range split
+# among 4 K-groups, 64 x 128 among 2): ragged M, N and K, uneven K-group runs;
+# every column of the last (partial) column tile is checked, plus a sample
+@pytest.mark.parametrize("M,K,N,dtype,tile", [
+    (17, 128, 72, torch.float16, (32, 64)), (33, 1152, 4160, torch.bfloat16, (32, 64)),
+    (40, 128, 1000, torch.float16, (32, 64)), (17, 4224, 11000, torch.bfloat16, (32, 64)),
+    (70, 2560, 11000, torch.float16, (64, 128)), (100, 6016, 8200, torch.bfloat16, (64, 128)),
+    (127, 128, 4160, torch.float16, (64, 128)), (33, 128, 8200, torch.bfloat16, (64, 128))])
+def test_nonsquare_tiles(M, K, N, dtype, tile):
+    assert ql.q4_gemm_tile_shape(M, N, K) == tile
+    r = np.random.default_rng(M * 7 + K + N)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
+    tail = np.arange(max(0, N - 200), N)
+    cols = np.union1d(np.sort(r.choice(N, min(N, 384), replace=False)), tail)
     check(W, X, cols=cols)
 
 
