@@ -333,3 +333,17 @@ def test_q4_gemm_tile_shape():
     assert L.q4_gemm_tile_shape(32, 64, 100, C.byref(r), C.byref(c)) == QL_ERR_SHAPE
     assert L.q4_gemm_tile_shape(32, 0, 128, C.byref(r), C.byref(c)) == QL_ERR_SHAPE
     assert L.q4_gemm_tile_shape(32, 64, 128, None, C.byref(c)) == QL_ERR_NULL
+
+
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++17")])
+def test_header_compiles_standalone(lang, std):
+    """include/qlinear.h is self-contained plain C (and C++): no torch or HIP
+    types cross the boundary."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    r = subprocess.run([cc, std, "-Wall", "-Werror", "-fsyntax-only", "-x", lang,
+                        os.path.join(ROOT, "include", "qlinear.h")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
