@@ -179,6 +179,19 @@ def test_i8_weight_prep_vs_oracle():
     assert np.array_equal(adj.numpy(), ow8.azp_adj(Bq_o))
 
 
+def test_i8_weight_prep_lq_worked_example(gold):
+    """The library's weight quantizer on [LQ]'s W8A8 worked example: the rows
+    on the printed grid (absmax 1.1 and 0.9, each holding the code 127) give
+    the printed codes and the printed scales 0.008661 / 0.007087."""
+    g = gold("lq_w8a8_example.json")
+    Wq = np.array(g["Wq"], np.float64)
+    Wf = (Wq * (np.array(g["w_absmax"]) / g["qmax"])[:, None]).astype(np.float32)
+    Bq, s_b = ql.i8_quant_weight_host(torch.from_numpy(Wf))
+    assert Bq.tolist() == g["Wq"]
+    assert np.round(s_b.numpy().astype(np.float64), 6).tolist() == g["s_w_printed"]
+    assert ql.i8_azp_adj(Bq).tolist() == [int(v) for v in Wq.sum(axis=1)]
+
+
 def test_f8_validation():
     L = ql.lib()
     P = FAKE

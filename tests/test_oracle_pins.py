@@ -185,6 +185,15 @@ def test_lq_w8a8_example():
     b = g["int32_bound"]
     assert 127 * 127 == b["max_product"]
     assert round(b["max_product"] * b["K"], -6) == b["approx_sum"]
+    # the printed weight codes and scales are what the per-channel weight
+    # quantizer gives.  The page prints each row's absmax and codes but not
+    # the fp weights; both rows hold the extreme code 127, so the row on the
+    # printed grid, Wq[n] * absmax[n] / 127, has exactly the printed absmax.
+    Wf = (Wq.astype(np.float64) * (np.array(g["w_absmax"]) / g["qmax"])[:, None]).astype(np.float32)
+    assert np.abs(Wf).max(axis=1).tolist() == pytest.approx(g["w_absmax"], rel=1e-7)
+    Bq, s_b = w8.quant_weight_per_channel_sym(Wf)
+    assert Bq.tolist() == g["Wq"]
+    assert np.round(s_b.astype(np.float64), 6).tolist() == g["s_w_printed"]
     # the printed activation codes are what the symmetric per-token quantizer
     # gives for a row whose absmax is the printed one (the row's own max
     # element maps to the extreme code)

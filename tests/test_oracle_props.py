@@ -224,6 +224,7 @@ def test_per_token_asym_invariants():
     X = nu.to_f16(RNG.standard_normal((16, 512)) + 0.3).astype(np.float32)
     X[3] = 0.0                                  # all-zero row: clamped range
     X[4] = np.abs(X[4])                         # non-negative row: mn = 0
+    X[5] = np.abs(X[5]) + np.float32(2.0)       # a row far from 0: the range is widened to contain it
     Aq, s_a, azp = w8.quant_per_token_asym(X)
     assert azp.min() >= -128 and azp.max() <= 127
     deq = s_a[:, None].astype(np.float64) * (Aq.astype(np.float64) - azp[:, None])
@@ -236,6 +237,9 @@ def test_per_token_asym_invariants():
     # real zero is exact: x = 0 maps to code azp
     assert np.all(Aq[3] == azp[3])
     assert azp[4] == -128
+    # [LQ] "线性量化": z is an integer code so that real 0 lies on a tick; for
+    # a row far from 0 that needs the widened range [0, max]
+    assert azp[5] == -128 and s_a[5] == np.float32(X[5].max() / np.float32(255))
     assert s_a[3] == np.float32(np.float32(1e-5) / np.float32(255))
 
 
