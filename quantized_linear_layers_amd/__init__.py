@@ -103,6 +103,44 @@ def _dev(t, dtype=None, name="tensor"):
     return t
 
 
+def _shape(t, shape, name):
+    """The C entry points see only pointers: every buffer's extent is checked here."""
+    if tuple(t.shape) != tuple(shape):
+        raise QLError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _same_device(name, *ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise QLError(f"{name}: operands on different devices {sorted(map(str, devs))}")
+
+
+def _epilogue_operands(name, M, N, s_a, s_b, azp, azp_adj, bias, out_dtype, out):
+    """Checks the epilogue vectors and the output of a scaled GEMM against (M, N)."""
+    _dev(s_a, torch.float32, "s_a")
+    _dev(s_b, torch.float32, "s_b")
+    if s_a.numel() not in (1, M):
+        raise QLError(f"{name}: s_a has {s_a.numel()} entries, expected 1 or M={M}")
+    if s_b.numel() not in (1, N):
+        raise QLError(f"{name}: s_b has {s_b.numel()} entries, expected 1 or N={N}")
+    if azp is not None:
+        _dev(azp, torch.int32, "azp")
+        if azp.numel() != M:
+            raise QLError(f"{name}: azp has {azp.numel()} entries, expected M={M}")
+    if azp_adj is not None:
+        _dev(azp_adj, torch.int32, "azp_adj")
+        if azp_adj.numel() != N:
+            raise QLError(f"{name}: azp_adj has {azp_adj.numel()} entries, expected N={N}")
+    if bias is not None:
+        _dev(bias, out_dtype, "bias")
+        if bias.numel() != N:
+            raise QLError(f"{name}: bias has {bias.numel()} entries, expected N={N}")
+    if out is not None:
+        _dev(out, out_dtype, "out")
+        _shape(out, (M, N), f"{name}: out")
+
+
 # ---------------------------------------------------------------- W4A16 offline (host)
 
 def q4_quantize_host(W, group=GROUP):
@@ -161,11 +199,15 @@ def q4_gemm(X, packed, N, group=GROUP, Y=None, stream=None):
     """Y[M, N] = X[M, K] · dequant(W)ᵀ; X fp16/bf16 on the device, packed from q4_pack."""
     X = _dev(X, name="X")
     _dev(packed, torch.uint8, "packed")
+    if X.dim() != 2:
+        raise QLError(f"q4_gemm: X must be 2-D, got shape {tuple(X.shape)}")
     M, K = X.shape
     if Y is None:
         Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
     else:
         _dev(Y, X.dtype, "Y")
+        _shape(Y, (M, N), "q4_gemm: Y")
+    _same_device("q4_gemm", X, packed, Y)
     _check(lib().q4_gemm(_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group, _ptr(Y),
                          _stream(X, stream)), "q4_gemm")
     return Y
@@ -215,6 +257,7 @@ def q4_permute_columns(X, perm, Xp=None, stream=None):
         Xp = torch.empty_like(X)
     else:
         _dev(Xp, X.dtype, "Xp")
+        _shape(Xp, (M, K), "q4_permute_columns: Xp")
     _check(lib().q4_permute_columns(_ptr(X), _dtype_code(X.dtype), M, K, _ptr(perm), _ptr(Xp), _stream(X, stream)),
            "q4_permute_columns")
     return Xp
@@ -342,17 +385,14 @@ def i8_gemm_scaled(Aq, Bq, s_a, s_b, azp=None, azp_adj=None, bias=None, out_dtyp
     With raw=True also returns the int32 corrected accumulator."""
     _dev(Aq, torch.int8, "Aq")
     _dev(Bq, torch.int8, "Bq")
-    _dev(s_a, torch.float32, "s_a")
-    _dev(s_b, torch.float32, "s_b")
-    for t, n in ((azp, "azp"), (azp_adj, "azp_adj")):
-        if t is not None:
-            _dev(t, torch.int32, n)
-    if bias is not None:
-        _dev(bias, out_dtype, "bias")
+    if Aq.dim() != 2 or Bq.dim() != 2:
+        raise QLError("i8_gemm_scaled: Aq and Bq must be 2-D")
     M, K = Aq.shape
     N = Bq.shape[0]
     if Bq.shape[1] != K:
         raise QLError("Aq and Bq disagree on K")
+    _epilogue_operands("i8_gemm_scaled", M, N, s_a, s_b, azp, azp_adj, bias, out_dtype, out)
+    _same_device("i8_gemm_scaled", Aq, Bq, s_a, s_b, azp, azp_adj, bias, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=Aq.device)
     rawt = torch.empty((M, N), dtype=torch.int32, device=Aq.device) if raw else None
@@ -389,14 +429,14 @@ def f8_gemm_scaled(Aq, Bq, s_a, s_b, bias=None, out_dtype=torch.float16, out=Non
     """out[M, N] = s_a * s_b * (e4m3(Aq)·e4m3(Bq)ᵀ) + bias, on the device."""
     _dev(Aq, torch.uint8, "Aq")
     _dev(Bq, torch.uint8, "Bq")
-    _dev(s_a, torch.float32, "s_a")
-    _dev(s_b, torch.float32, "s_b")
-    if bias is not None:
-        _dev(bias, out_dtype, "bias")
+    if Aq.dim() != 2 or Bq.dim() != 2:
+        raise QLError("f8_gemm_scaled: Aq and Bq must be 2-D")
     M, K = Aq.shape
     N = Bq.shape[0]
     if Bq.shape[1] != K:
         raise QLError("Aq and Bq disagree on K")
+    _epilogue_operands("f8_gemm_scaled", M, N, s_a, s_b, None, None, bias, out_dtype, out)
+    _same_device("f8_gemm_scaled", Aq, Bq, s_a, s_b, bias, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=Aq.device)
     _check(lib().f8_gemm_scaled(_ptr(Aq), _ptr(Bq), M, N, K, _ptr(s_a), s_a.numel(), _ptr(s_b), s_b.numel(),
