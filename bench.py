@@ -1,29 +1,35 @@
 """Throughput of the quantized linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-also]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-also] [--no-per-case]
 
-The main line is the W4A16 decode GEMV on the Llama-2-7B-shaped layers
-(M in {1, 4, 16} x (K, N) in {(4096, 4096), (4096, 11008), (11008, 4096)},
-g = 128, fp16 activations with 1% outlier channels).  One step runs all nine
-(M, K, N) cases once.  `value` is the effective bandwidth of a whole step:
-algorithmic bytes (packed weights + fp16 scales + 4-bit zeros + X + Y) over
-the step's wall time, inputs resident in HBM.  Each step reads a different
-copy of the weights (copies rotate so that the working set exceeds 1 GiB, four
-times the 256 MB Infinity Cache), so the weights come from HBM, not cache.
+The main line is the W4A16 decode GEMV on the Llama-2-70B-shaped layers, the
+bandwidth-bound case (M in {1, 8} x (K, N) in {(8192, 8192), (8192, 28672),
+(28672, 8192)}, g = 128, bf16 activations and output, fp16 scales).  One step
+runs all six (M, K, N) cases once, in that order.  `value` is the effective
+bandwidth of a whole step: algorithmic bytes (packed weights + fp16 scales +
+4-bit zeros + X + Y) over the step's time, inputs resident in HBM.  Every
+launch of a case reads its own copy of the weights, and a copy is read again
+only after more than 1 GiB of other weights (four times the 256 MB Infinity
+Cache), so the weights come from HBM, not from cache.
 
-The steps are launched on one stream with their arguments marshalled once
-(--graphs replays them as HIP graphs instead, one graph per weight copy, after
-checking every graph's outputs bit-for-bit against eager launches; on this
-stack graph replay of these short kernels measured slower than stream
-launches).  The step contains only the decode kernel, so the roofline
-object's mean launch duration is the timed region's elapsed time (HIP events
-on the launch stream) over its launches.  `per_case_eager` adds a second pass of eager launches,
-each bracketed by HIP events (which adds the event overhead to each figure).
-The `also` object holds the other workloads (70B decode, W8A8 prefill GEMM
-with int8 and with FP8 codes, W4A16 prefill GEMM).
+The steps are launched back to back on one stream with their arguments
+marshalled once; the timed region is bracketed by HIP events recorded on that
+stream.  The step holds nothing but the decode kernel's launches, so the
+roofline object's mean launch duration is the timed region's elapsed time over
+its launches.  Before the W warm-up steps the step runs for about 250 ms, so
+the timed steps start in the state a sustained load settles in.
+
+Beside it, in the same process: each case timed alone (back-to-back launches
+over the weight copies), and a plain streaming read of the same weight bytes
+(`ql_read_probe`, the achievable HBM read rate) timed the same way, per case
+and as a whole step: the read ceiling the decode kernel is measured against.
+The `also` object holds the other workloads (7B decode step, W8A8 prefill GEMM
+with int8 and with FP8 codes, W4A16 prefill GEMM, W4A16 mid-M), and
+`cpu_baseline` the untuned oracle on the host cores.
 """
 
 import argparse
+import functools
 import json
 import os
 import sys
@@ -39,13 +45,19 @@ MFMA_PEAK = {"bf16": 2.5e15, "f16": 2.5e15, "i8": 5.0e15, "fp8": 5.0e15}   # den
 METRIC = "W4A16 GEMV effective GB/s (% HBM peak); W8A8/W4A16 GEMM TOPS (% MFMA peak)"
 MALL_DEFEAT_BYTES = 1 << 30
 
-# HBM traffic of the decode kernel per launch (mean over the nine cases of a
+# HBM traffic of the decode kernel per launch (mean over the six cases of a
 # step), from two counter runs (FETCH_SIZE, then WRITE_SIZE) each scaled by
 # what the same counter reads for a plain device copy of known size in the
 # same run.  It belongs to one version of the kernel source: when the source
 # hash differs, the figure is stale and `traffic` is reported as null.
-TRAFFIC = {"source_sha256": "a520aa56e5ef08ed818808b749d50a30805789505bc0bd79ee906c7941d1fbd3",
-           "bytes_per_launch": 19387981}
+TRAFFIC = None
+
+
+@functools.lru_cache(maxsize=None)
+def _weight(w, K, N):
+    """fp32 weight draw of a workload's layer, drawn once per process (the
+    70B layers take seconds each to draw)."""
+    return wl.weight(w, K, N)
 
 
 def w4a16_bytes(M, K, N, group=128, e=2):
@@ -60,14 +72,26 @@ def _events():
 
 
 def _prepare_w4(ql, w, K, N, copies):
-    W = wl.weight(w, K, N)
+    W = _weight(w, K, N)
     wq, s, z = ql.q4_quantize_host(torch.from_numpy(W))
     blob = ql.q4_pack(wq, s, z, N, K)
     return W, [blob.to("cuda") for _ in range(copies)]
 
 
 def _copies_for(total_bytes):
-    return max(2, -(-MALL_DEFEAT_BYTES // max(total_bytes, 1)))
+    """Copies of a buffer of total_bytes such that a loop over them reads more
+    than MALL_DEFEAT_BYTES of other copies before it reads one again."""
+    return max(2, -(-(MALL_DEFEAT_BYTES + total_bytes) // max(total_bytes, 1)))
+
+
+# plain-read probe configurations (mode, workgroups); the fastest per layer is
+# the read ceiling (grid-stride reads win on tens of MB, one contiguous chunk
+# per workgroup on hundreds)
+READ_PROBES = ((0, 2048), (1, 512), (1, 1024))
+# back-to-back steps before the W warm-up steps: the first tens of
+# milliseconds of work after the weights are prepared run slower (measured:
+# 147 us for the 70B step after 30 ms of warm-up, 118-121 us after 60 ms more)
+STEP_WARM_MS = 250.0
 
 
 def _kernel_source_sha():
@@ -133,91 +157,96 @@ def time_launches(fn_list, reps, stream, warm_ms=None):
     return out
 
 
-def bench_decode(ql, wname, steps, warmup, use_graphs=False):
-    """Runs a W4A16 decode workload; returns a dict of results."""
+def bench_decode(ql, wname, steps, warmup, per_case=True):
+    """Runs a W4A16 decode workload; returns a dict of results.
+
+    Every layer (K, N) gets R copies of its blob.  Case j of the layer's nM
+    token counts in step r reads copy (r * nM + j) % R, so a copy is read again
+    only after R - 1 other reads of that layer, and R is chosen so that those
+    and the other layers' reads in between exceed MALL_DEFEAT_BYTES; the
+    per-case loops cycle over the same copies, which also exceed it alone."""
     w = wl.WORKLOADS[wname]
     cases = w.all_cases()
+    nM = len(w.Ms)
     shapes = list(w.shapes)
-    blob_bytes = sum(ql.q4_packed_bytes(N, K) for (K, N) in shapes)
-    R = _copies_for(blob_bytes)
-    blobs = {}
-    for (K, N) in shapes:
-        _, blobs[(K, N)] = _prepare_w4(ql, w, K, N, R)
+    lb = {(K, N): ql.q4_packed_bytes(N, K) for (K, N) in shapes}
+    step_wbytes = nM * sum(lb.values())
+    need_step = -(-nM * (MALL_DEFEAT_BYTES + max(lb.values())) // step_wbytes)
+    R = {L: max(nM + 1, need_step, _copies_for(lb[L])) for L in shapes}
+    blobs = {L: _prepare_w4(ql, w, L[0], L[1], R[L])[1] for L in shapes}
     X = {c: wl.activations(w, c[0], c[1], c[2]).cuda() for c in cases}
     Y = {c: torch.empty((c[0], c[2]), dtype=X[c].dtype, device="cuda") for c in cases}
     stream = torch.cuda.current_stream()
-    # launchers with the arguments marshalled once (the host cost of a
-    # launch must stay below the kernel's few microseconds)
-    launchers = [[ql.q4_gemm_launcher(X[c], blobs[(c[1], c[2])][r], c[2], Y[c]) for c in cases] for r in range(R)]
+    # launchers with the arguments marshalled once (the host cost of a launch
+    # must stay below the kernel's microseconds)
+    gemv = {c: [ql.q4_gemm_launcher(X[c], b, c[2], Y[c]) for b in blobs[(c[1], c[2])]] for c in cases}
+    probe = {(L, p): [ql.read_probe_launcher(b, p[1], p[0]) for b in blobs[L]] for L in shapes for p in READ_PROBES}
 
-    def launch(c, r):
-        M, K, N = c
-        ql.q4_gemm(X[c], blobs[(K, N)][r], N, Y=Y[c])
+    def copy_of(c, r):
+        L = (c[1], c[2])
+        return (r * nM + w.Ms.index(c[0])) % R[L]
 
     def step(r):
-        if use_graphs:            # capture runs on its own stream: marshal per call
-            for c in cases:
-                launch(c, r)
-        else:
-            for f in launchers[r]:
-                f()
+        for c in cases:
+            gemv[c][copy_of(c, r)]()
 
-    for r in range(min(R, warmup + 1)):
-        step(r)
-    torch.cuda.synchronize()
-    bytes_step = sum(w4a16_bytes(*c) for c in cases)
+    best = {}                    # fastest probe configuration of each layer
 
-    graphs = None
-    if use_graphs:
-        ref = {}
-        for r in range(R):
-            step(r)
-            torch.cuda.synchronize()
-            ref[r] = {c: Y[c].clone() for c in cases}
-        graphs = []
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(r)
-            graphs.append(g)
+    def probe_step(r):
+        for c in cases:
+            probe[((c[1], c[2]), best[(c[1], c[2])])][copy_of(c, r)]()
+
+    def timed(fn, n):
+        warm([fn], STEP_WARM_MS)
+        for i in range(warmup):
+            fn(i)
+        a, b = _events()
+        a.record(stream)
+        for i in range(n):
+            fn(warmup + i)
+        b.record(stream)
         torch.cuda.synchronize()
-        for rep in range(2):                      # every replay must equal the eager result
-            for r in range(R):
-                for c in cases:
-                    Y[c].zero_()
-                graphs[r].replay()
-                torch.cuda.synchronize()
-                for c in cases:
-                    if not torch.equal(Y[c], ref[r][c]):
-                        raise RuntimeError(f"graph replay {rep} of copy {r} differs from eager on case {c}")
+        return a.elapsed_time(b) / n
 
-    run = (lambda i: graphs[i % R].replay()) if graphs else (lambda i: step(i % R))
-    for i in range(warmup):
-        run(i)
-    torch.cuda.synchronize()
-    a, b = _events()
-    a.record(stream)
-    for i in range(steps):
-        run(i)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms_step = a.elapsed_time(b) / steps
-
-    # per-case durations (each case alone, back to back over the weight copies)
-    fns = [(lambda r, i=i: launchers[r % R][i]()) for i in range(len(cases))]
-    per = time_launches(fns, max(steps, 10), stream)
-    kern_ms = float(per.sum())
-    per_case = []
-    for c, ms in zip(cases, per):
+    bytes_step = sum(w4a16_bytes(*c) for c in cases)
+    ms_step = timed(step, steps)
+    res = {"cases": cases, "bytes_step": bytes_step, "ms_step": ms_step,
+           "value_gbs": bytes_step / (ms_step * 1e-3) / 1e9,
+           "copies": {f"{K}x{N}": R[(K, N)] for (K, N) in shapes}}
+    if not per_case:
+        return res
+    # the plain read of each layer's weight copies, back to back, in every
+    # probe configuration; the fastest is that layer's read ceiling
+    read_ms = {}
+    for L in shapes:
+        n = R[L]
+        t = {p: time_launches([lambda i, f=probe[(L, p)], n=n: f[i % n]()], max(steps, 2 * n), stream)[0]
+             for p in READ_PROBES}
+        best[L] = min(t, key=t.get)
+        read_ms[L] = t[best[L]]
+    # the plain read of the same weight bytes, as a whole step
+    ms_probe = timed(probe_step, steps)
+    wbytes = sum(lb[(c[1], c[2])] for c in cases)
+    res["read_ceiling_step"] = {"us": round(ms_probe * 1e3, 2),
+                                "weight_GBps": round(wbytes / (ms_probe * 1e-3) / 1e9, 1),
+                                "frac_hbm": round(wbytes / (ms_probe * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "step_us_over_read_us": round(ms_step / ms_probe, 4),
+                                "probe_per_layer": {f"{K}x{N}": {"mode": best[(K, N)][0], "workgroups": best[(K, N)][1]}
+                                                    for (K, N) in shapes}}
+    # each case alone, back to back over its weight copies
+    out, kern = [], 0.0
+    for c in cases:
+        L, n = (c[1], c[2]), R[(c[1], c[2])]
+        ms = time_launches([lambda i, c=c, n=n: gemv[c][i % n]()], max(steps, 2 * n), stream)[0]
+        kern += ms
         gbs = w4a16_bytes(*c) / (ms * 1e-3) / 1e9
-        per_case.append({"M": c[0], "K": c[1], "N": c[2], "us": round(ms * 1e3, 3),
-                         "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
-    return {
-        "cases": cases, "bytes_step": bytes_step, "ms_step": ms_step,
-        "value_gbs": bytes_step / (ms_step * 1e-3) / 1e9,
-        "kernel_ms_step": kern_ms, "kernel_gbs": bytes_step / (kern_ms * 1e-3) / 1e9,
-        "per_case": per_case, "copies": R, "graphs": bool(graphs),
-    }
+        rd = lb[L] / (read_ms[L] * 1e-3) / 1e9
+        out.append({"M": c[0], "K": c[1], "N": c[2], "us": round(ms * 1e3, 3), "GBps": round(gbs, 1),
+                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "read_us": round(read_ms[L] * 1e3, 3),
+                    "read_GBps": round(rd, 1), "frac_of_read": round(gbs / rd, 4)})
+    res["per_case"] = out
+    res["kernel_ms_step"] = kern
+    return res
 
 
 def _activation_copies(X):
@@ -317,37 +346,71 @@ def bench_mid_m(ql, reps):
     return {"workload": w.name, "per_case": per_case}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s=20.0):
-    """The oracle (explicit dequant + fp64 product), untuned, on the host cores,
-    over whole steps of the 7B decode workload until about budget_s seconds."""
+    """The oracle as it is (untuned) on the host cores.
+
+    W4A16 (the headline's unit): explicit fp64 dequant + fp64 BLAS product,
+    whole cases of the 70B decode workload in step order until about budget_s
+    seconds (the codes of a layer are prepared, untimed, when the sample first
+    reaches it).  W8A8: per-token quant + exact integer product + epilogue on
+    the M = 2048, K = N = 4096 workload, median of 3."""
     from oracle import w4a16 as ow4
+    from oracle import w8a8 as ow8
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count() or 1
-    w = wl.WORKLOADS["decode_7b"]
+    w = wl.WORKLOADS["decode_70b"]
     cases = w.all_cases()
     prep = {}
-    for (K, N) in w.shapes:
-        prep[(K, N)] = ow4.quantize_w4(wl.weight(w, K, N))
-    Xs = {c: wl.as_f64(wl.activations(w, *c)) for c in cases}
-    nbytes, t0, done = 0, time.perf_counter(), 0
-    while True:
-        for c in cases:
-            q, s, z = prep[(c[1], c[2])]
-            ow4.w4a16_linear(Xs[c], q, s, z)
-            nbytes += w4a16_bytes(*c)
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} case runs cycling over the 9 (M, K, N) decode cases of the 7B workload "
-                      f"({done / len(cases):.1f} steps) in {dt:.1f} s "
-                      f"(explicit fp64 dequant + fp64 BLAS product per case; quantization untimed)"}
+    nbytes, done, busy = 0, 0, 0.0
+    while busy < budget_s:
+        c = cases[done % len(cases)]
+        L = (c[1], c[2])
+        if L not in prep:
+            prep[L] = ow4.quantize_w4(_weight(w, *L))
+        X = wl.as_f64(wl.activations(w, *c))
+        t0 = time.perf_counter()
+        ow4.w4a16_linear(X, *prep[L])
+        busy += time.perf_counter() - t0
+        nbytes += w4a16_bytes(*c)
+        done += 1
+    del prep
+    # W8A8: quantize the activations, exact integer product, epilogue
+    w8 = wl.WORKLOADS["w8a8_prefill"]
+    M, (K, N) = w8.Ms[0], w8.shapes[0]
+    Xf = wl.as_f64(wl.activations(w8, M, K, N)).astype(np.float32)
+    Bq, s_b = ow8.quant_weight_per_channel_sym(wl.weight(w8, K, N))
+    adj = ow8.azp_adj(Bq)
+    bias = wl.as_f64(wl.bias(w8, N))
+    t8 = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        Aq, s_a, azp = ow8.quant_per_token_asym(Xf)
+        ow8.w8a8_linear(Aq, Bq, s_a, s_b, azp, adj, bias)
+        t8.append(time.perf_counter() - t0)
+    t8m = float(np.median(t8))
+    return {"value": round(nbytes / busy / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} whole cases of the 70B decode workload in step order "
+                      f"({done / len(cases):.2f} steps), {busy:.1f} s of oracle time (explicit fp64 dequant + "
+                      f"fp64 BLAS product per case; quantization untimed)",
+            "cpu_model": _cpu_model(), "blas_threads": int(threads),
+            "w8a8": {"workload": w8.name, "median_of_3_s": round(t8m, 4),
+                     "GOPS": round(2.0 * M * N * K / t8m / 1e9, 2),
+                     "what": "per-token asymmetric int8 quant + exact integer product (fp64 BLAS on integer "
+                             "values) + zero-point correction and epilogue"}}
 
 
 def main():
@@ -358,9 +421,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-per-case", action="store_true",
+                    help="time only the main step (no per-case or read-ceiling blocks)")
     ap.add_argument("--warm-ms", type=float, default=WARM_MS, metavar="MS",
-                    help="back-to-back launches of a kernel before its timed block (small under a profiler)")
-    ap.add_argument("--graphs", action="store_true", help="replay the decode steps as HIP graphs")
+                    help="back-to-back launches of a kernel before its timed block in the per-kernel figures")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for byte counters)")
     args = ap.parse_args()
@@ -377,16 +441,20 @@ def main():
 
     if args.copy_calib > 0:
         copy_calibration(args.copy_calib)
-    main_res = bench_decode(ql, "decode_7b", args.steps, args.warmup, use_graphs=args.graphs)
-    print(f"# decode_7b: {main_res['value_gbs']:.1f} GB/s per step, kernels {main_res['kernel_gbs']:.1f} GB/s",
-          flush=True)
+    main_res = bench_decode(ql, "decode_70b", args.steps, args.warmup, per_case=not args.no_per_case)
+    print(f"# decode_70b: {main_res['value_gbs']:.1f} GB/s per step", flush=True)
+    if "per_case" in main_res:
+        print(f"# decode_70b read ceiling: {main_res['read_ceiling_step']}", flush=True)
+        print(f"# decode_70b per case: {main_res['per_case']}", flush=True)
     also = {}
     if not args.no_also:
-        r70 = bench_decode(ql, "decode_70b", max(10, args.steps // 2), args.warmup, use_graphs=args.graphs)
-        also["decode_70b"] = {"workload": wl.WORKLOADS["decode_70b"].name, "step_GBps": round(r70["value_gbs"], 1),
-                              "kernel_GBps": round(r70["kernel_gbs"], 1),
-                              "frac_hbm": round(r70["kernel_gbs"] / HBM_PEAK_GBS, 4), "per_case": r70["per_case"]}
-        print(f"# decode_70b: kernels {r70['kernel_gbs']:.1f} GB/s", flush=True)
+        r7 = bench_decode(ql, "decode_7b", args.steps, args.warmup)
+        also["decode_7b"] = {"workload": wl.WORKLOADS["decode_7b"].name, "step_GBps": round(r7["value_gbs"], 1),
+                             "ms_step": round(r7["ms_step"], 5),
+                             "frac_hbm": round(r7["value_gbs"] / HBM_PEAK_GBS, 4),
+                             "read_ceiling_step": r7["read_ceiling_step"], "per_case": r7["per_case"]}
+        print(f"# decode_7b: {r7['value_gbs']:.1f} GB/s per step", flush=True)
+        del r7
         also["w8a8_prefill"] = bench_w8a8(ql, 50)
         print(f"# w8a8: {also['w8a8_prefill']}", flush=True)
         also["w8a8_fp8_prefill"] = bench_f8(ql, 50)
@@ -405,6 +473,7 @@ def main():
     traffic = None
     if TRAFFIC is not None and TRAFFIC["source_sha256"] == _kernel_source_sha():
         traffic = TRAFFIC["bytes_per_launch"]
+    w70 = wl.WORKLOADS["decode_70b"]
     line = {
         "metric": METRIC,
         "value": round(main_res["value_gbs"], 2),
@@ -416,18 +485,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded N(0, 0.02) fp32 weights quantized to uint4 g=128; fp16 N(0, 1) "
-                "activations with 1% channels x20)",
-        "config": {"workload": wl.WORKLOADS["decode_7b"].name, "cases_MKN": main_res["cases"], "group": 128,
-                   "bytes_per_step": main_res["bytes_step"], "weight_copies": main_res["copies"],
-                   "hip_graphs": main_res["graphs"]},
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 0.015) fp32 weights quantized to uint4 g=128 with fp16 scales; "
+                "bf16 N(0, 1) activations)",
+        "config": {"workload": w70.name, "cases_MKN": main_res["cases"], "group": 128,
+                   "bytes_per_step": main_res["bytes_step"], "weight_copies": main_res["copies"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "q4_gemv_kernel",
                      "algorithmic_bytes_per_launch": round(main_res["bytes_step"] / launches),
                      "launch_us_mean": round(launch_ms * 1e3, 3),
-                     "per_case_eager": main_res["per_case"]},
+                     "read_ceiling_step": main_res.get("read_ceiling_step"),
+                     "per_case": main_res.get("per_case")},
         "cpu_baseline": cpu,
         "also": also,
     }

@@ -414,6 +414,27 @@ int f8_gemm_scaled(const uint8_t* Aq, const uint8_t* Bq, int M, int N, int K,
                    const float* s_a, int s_a_len, const float* s_b, int s_b_len,
                    const void* bias, void* out, int out_dtype, void* stream);
 
+/* =========================================================================
+ * Measurement aid
+ * ========================================================================= */
+
+/*
+ * ql_read_probe — a plain streaming read of `bytes` bytes at src (device):
+ * the achievable HBM read rate on this part, against which the decode kernel
+ * is measured in the same run ([QK] §9.1: batch-1 decode reads every weight
+ * once per token, so its time is at least the weight bytes over the memory
+ * bandwidth; [LQ] "带宽与算力：Roofline").  workgroups: grid size in
+ * [1, 65536] of 256 threads; mode 0: every thread reads 16-byte pieces at
+ * the grid stride; mode 1: every workgroup reads one contiguous chunk of
+ * bytes / workgroups.  Non-temporal 16-byte loads, 8 in flight per thread.
+ * sink: device buffer of 4 * workgroups uint32 words, overwritten with an XOR
+ * of the bytes read (so the loads cannot be elided).  Nothing else is
+ * written.
+ * Errors: QL_ERR_SHAPE unless bytes is a positive multiple of 16, workgroups
+ *         in range and mode 0 or 1; QL_ERR_NULL; QL_ERR_ALIGN; QL_ERR_HIP.
+ */
+int ql_read_probe(const void* src, size_t bytes, uint32_t* sink, int workgroups, int mode, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,6 +56,7 @@ def lib():
             "f8_quant_weight_host": (I, [P, I, I, P, P]),
             "f8_quant_per_token": (I, [P, I, I, I, P, P, P]),
             "f8_gemm_scaled": (I, [P, P, I, I, I, P, I, P, I, P, P, I, P]),
+            "ql_read_probe": (I, [P, Z, P, I, I, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -443,3 +444,27 @@ def f8_gemm_scaled(Aq, Bq, s_a, s_b, bias=None, out_dtype=torch.float16, out=Non
                                 _ptr(bias), _ptr(out), _dtype_code(out_dtype), _stream(Aq, stream)),
            "f8_gemm_scaled")
     return out
+
+
+# ---------------------------------------------------------------- measurement aid
+
+def read_probe_launcher(src, workgroups, mode=0, nbytes=None, stream=None):
+    """Checks a device buffer once and returns a callable that streams
+    `nbytes` of it (all of it by default) through ql_read_probe: the plain
+    HBM read rate the decode kernel is compared with (mode 0: grid-stride
+    reads, mode 1: one contiguous chunk per workgroup)."""
+    _dev(src, name="src")
+    nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if nbytes > src.numel() * src.element_size() or nbytes % 16:
+        raise QLError(f"ql_read_probe: {nbytes} bytes is not a multiple of 16 within the buffer")
+    sink = torch.empty(4 * workgroups, dtype=torch.int32, device=src.device)
+    f = lib().ql_read_probe
+    args = (_ptr(src), nbytes, _ptr(sink), int(workgroups), int(mode), _stream(src, stream))
+
+    def launch(*_):
+        rc = f(*args)
+        if rc != 0:
+            _check(rc, "ql_read_probe")
+
+    launch.sink = sink                # keeps the sink alive with the callable
+    return launch

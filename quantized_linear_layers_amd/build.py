@@ -33,6 +33,7 @@ SOURCES = {
     "i8_quant.hip": ["-ffp-contract=off"],
     "i8_gemm.hip": [],
     "act_order.hip": [],
+    "read_probe.hip": [],
 }
 
 

@@ -181,4 +181,17 @@ int f8_gemm_scaled(const uint8_t* Aq, const uint8_t* Bq, int M, int N, int K, co
   return hip_status("f8_gemm_scaled", ql::launch_f8_gemm(Aq, Bq, M, N, K, e, static_cast<hipStream_t>(stream)));
 }
 
+int ql_read_probe(const void* src, size_t bytes, uint32_t* sink, int workgroups, int mode, void* stream) {
+  if (bytes == 0 || bytes % 16)
+    return ql::set_error(QL_ERR_SHAPE, "ql_read_probe: bytes=%zu must be a positive multiple of 16", bytes);
+  if (workgroups < 1 || workgroups > 65536)
+    return ql::set_error(QL_ERR_SHAPE, "ql_read_probe: workgroups=%d must be in [1, 65536]", workgroups);
+  if (mode != 0 && mode != 1) return ql::set_error(QL_ERR_SHAPE, "ql_read_probe: mode=%d must be 0 or 1", mode);
+  if (!src || !sink) return ql::set_error(QL_ERR_NULL, "ql_read_probe: NULL src or sink");
+  if (!aligned16(src) || !aligned16(sink))
+    return ql::set_error(QL_ERR_ALIGN, "ql_read_probe: src and sink must be 16-byte aligned");
+  return hip_status("ql_read_probe",
+                    ql::launch_read_probe(src, bytes, sink, workgroups, mode, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -35,9 +35,6 @@
 
 #include "ql_internal.h"
 
-#ifdef QL_GEMM_TILE
-#include <cstdlib>
-#endif
 
 namespace ql {
 namespace {
@@ -607,9 +604,6 @@ constexpr int kNumTiles = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
 // rounds x (ramp + K steps of a K-group x step time), with 256 workgroups a
 // round and a ramp of 2.5 us a round; ties go to the earlier (larger) tile.
 int gemm_tile(int M, int N, int K) {
-#ifdef QL_GEMM_TILE
-  if (const char* e = getenv("QL_GEMM_TILE")) return atoi(e);
-#endif
   const long nkb = K / BK;
   int best = 0;
   double best_cost = 0.0;

@@ -120,4 +120,10 @@ hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K,
 hipError_t launch_f8_gemm(const uint8_t* A, const uint8_t* B, int M, int N, int K,
                           const I8Epi& e, hipStream_t st);
 
+// plain streaming read of `bytes` bytes (a multiple of 16): the achievable
+// HBM read rate; sink receives read_probe_sink_words(workgroups) words
+int read_probe_sink_words(int workgroups);
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int workgroups, int mode,
+                             hipStream_t st);
+
 }  // namespace ql

@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -360,3 +360,16 @@ def test_header_compiles_standalone(lang, std):
     r = subprocess.run([cc, std, "-Wall", "-Werror", "-fsyntax-only", "-x", lang,
                         os.path.join(ROOT, "include", "qlinear.h")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_read_probe_validation():
+    L = ql.lib()
+    P = FAKE
+    assert L.ql_read_probe(P, 0, P, 64, 0, None) == QL_ERR_SHAPE          # no bytes
+    assert L.ql_read_probe(P, 24, P, 64, 0, None) == QL_ERR_SHAPE         # not a multiple of 16
+    assert L.ql_read_probe(P, 1 << 20, P, 0, 0, None) == QL_ERR_SHAPE     # no workgroups
+    assert L.ql_read_probe(P, 1 << 20, P, 65537, 0, None) == QL_ERR_SHAPE
+    assert L.ql_read_probe(P, 1 << 20, P, 64, 2, None) == QL_ERR_SHAPE    # unknown mode
+    assert L.ql_read_probe(None, 1 << 20, P, 64, 0, None) == QL_ERR_NULL
+    assert L.ql_read_probe(P, 1 << 20, None, 64, 1, None) == QL_ERR_NULL
+    assert L.ql_read_probe(FAKE_MIS, 1 << 20, P, 64, 0, None) == QL_ERR_ALIGN

@@ -1,8 +1,10 @@
 """The binding rejects operands whose extent, dtype or device disagrees with
 the shapes it passes to the C ABI (which receives only pointers and sizes and
-so cannot see a short or mis-shaped buffer).  Every case raises before the
-library is called: no kernel is launched."""
+so cannot see a short or mis-shaped buffer): every such case raises before
+the library is called, so no kernel is launched.  And the read probe (the
+measurement aid) folds every word of the bytes it is given."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -88,3 +90,19 @@ def test_permute_rejects_bad_output():
         ql.q4_permute_columns(X, perm, Xp=dev((4, 255), torch.float16))
     with pytest.raises(ql.QLError):
         ql.q4_permute_columns(X, dev(255, torch.int32))
+
+
+@pytest.mark.parametrize("mode,wgs,nbytes", [(0, 2048, 35 << 20), (1, 512, 35 << 20), (0, 7, 4096 + 48),
+                                             (1, 300, (1 << 20) + 16), (1, 64, 64)])
+def test_read_probe_reads_every_byte(mode, wgs, nbytes):
+    """The measurement aid really reads the buffer: the XOR of its sink words
+    equals the XOR of all 32-bit words of the bytes it was given (each word is
+    folded exactly once, whatever the pattern)."""
+    g = torch.Generator().manual_seed(nbytes + mode)
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, ((nbytes + 1024) // 4,), dtype=torch.int32, generator=g)
+    f = ql.read_probe_launcher(buf.cuda(), wgs, mode, nbytes=nbytes)
+    f()
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(buf[: nbytes // 4].numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(f.sink.cpu().numpy().view(np.uint32))
+    assert got == want
