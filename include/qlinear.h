@@ -32,7 +32,8 @@
  *     stream).  It validates its arguments on the host, then enqueues its
  *     kernels and returns without synchronizing.
  *   - The caller owns every buffer.  The library never allocates, frees or
- *     retains device memory, and keeps no device state between calls.
+ *     retains device memory, and keeps no device state between calls
+ *     (scratch space comes in as a caller-owned workspace argument).
  *   - Every function returns a ql_status.  Nothing aborts or throws across
  *     the ABI.  On a non-OK return nothing was launched and nothing was
  *     written, and ql_last_error() describes the failure (per thread).
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define QL_ABI_VERSION 1
+#define QL_ABI_VERSION 2
 
 typedef enum {
   QL_OK = 0,
@@ -181,29 +182,46 @@ int q4_unpack(const void* packed, size_t packed_bytes, int N, int K, int group,
  * packed  device blob from q4_pack for (N, K, group), of packed_bytes bytes
  *         (at least q4_packed_bytes(N, K, group)).
  * Y       [M][N] out, same dtype as X, device.
+ * workspace, ws_bytes  caller-owned device scratch for a split of K across
+ *         workgroups (fp32 partial results, then a pass that adds them and
+ *         rounds once to x_dtype), or NULL.  q4_gemm_workspace_bytes gives the
+ *         size; NULL runs the layer without a K split (same result up to the
+ *         fp32 summation order, possibly slower).  Its contents on entry do
+ *         not matter; calls that share one workspace must not overlap.
  * M <= 16 runs the decode kernel (each workgroup owns 16 * NT output
- * channels for all of K); larger M the LDS-tiled MFMA GEMM.  Neither needs
- * device scratch.  M == 0 or N == 0 is a no-op returning QL_OK.
+ * channels for all of K); larger M the LDS-tiled MFMA GEMM, with K split
+ * across workgroups when few tokens would leave compute units idle.
+ * M == 0 or N == 0 is a no-op returning QL_OK.
  * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M, N >= 0, K > 0,
  *         K % group == 0; QL_ERR_UNSUPPORTED unless group == 128, and for
  *         M > 16 when X (M*K*2 bytes) or the blob exceeds 4 GiB;
- *         QL_ERR_SIZE if packed_bytes < q4_packed_bytes(N, K, group);
- *         QL_ERR_ALIGN; QL_ERR_HIP.
+ *         QL_ERR_SIZE if packed_bytes < q4_packed_bytes(N, K, group) or a
+ *         workspace is given with ws_bytes < q4_gemm_workspace_bytes(M, N, K,
+ *         group); QL_ERR_ALIGN; QL_ERR_HIP.
  */
 int q4_gemm(const void* X, int x_dtype, int M, int K, int N,
-            const void* packed, size_t packed_bytes, int group, void* Y, void* stream);
+            const void* packed, size_t packed_bytes, int group, void* Y,
+            void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * q4_gemm_tile_shape — which workgroup tile q4_gemm uses for an M x N x K
- * product (host; a diagnostic for tests and tuning, no device work).
- * *rows, *cols: the tile's rows and columns (256 x 256 … 32 x 32, also
- * 64 x 128 and 32 x 64) for M > 16; 0, 0 for M <= 16 (the decode kernel).
+ * q4_gemm_workspace_bytes — bytes of workspace q4_gemm uses for an M x N x K
+ * layer (host; 0 when its plan does not split K, and for invalid sizes).
+ */
+size_t q4_gemm_workspace_bytes(int M, int N, int K, int group);
+
+/*
+ * q4_gemm_tile_shape — the plan q4_gemm uses for an M x N x K product, with
+ * a workspace (with_workspace != 0) or without one (host; a diagnostic for
+ * tests and tuning, no device work).
+ * *rows, *cols: the workgroup tile (256 x 256 … 32 x 32, also 64 x 128 and
+ * 32 x 64) for M > 16; 0, 0 for M <= 16 (the decode kernel).  *splits (if
+ * splits != NULL): the number of K splits across workgroups (1 = none).
  * The choice depends on the shape only ([LQ] W4A16 section: the batch size
  * decides between the bandwidth- and compute-bound regimes).
- * Errors: QL_ERR_NULL; QL_ERR_SHAPE unless M >= 0, N > 0, K > 0,
- *         K % 128 == 0.
+ * Errors: QL_ERR_NULL (rows or cols); QL_ERR_SHAPE unless M >= 0, N > 0,
+ *         K > 0, K % 128 == 0.
  */
-int q4_gemm_tile_shape(int M, int N, int K, int* rows, int* cols);
+int q4_gemm_tile_shape(int M, int N, int K, int with_workspace, int* rows, int* cols, int* splits);
 
 /* -------------------------------------------------------------------------
  * Act-order (g_idx).  [LQ] GPTQ section, "工程细节", its act-order item:

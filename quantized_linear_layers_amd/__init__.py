@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libqlinear.so")
 
 QL_F16, QL_BF16 = 0, 1
 GROUP = 128
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 
@@ -43,8 +43,9 @@ def lib():
             "q4_packed_bytes": (Z, [I, I, I]),
             "q4_pack": (I, [P, P, P, I, I, I, P, Z]),
             "q4_unpack": (I, [P, Z, I, I, I, P, P, P]),
-            "q4_gemm": (I, [P, I, I, I, I, P, Z, I, P, P]),
-            "q4_gemm_tile_shape": (I, [I, I, I, P, P]),
+            "q4_gemm": (I, [P, I, I, I, I, P, Z, I, P, P, Z, P]),
+            "q4_gemm_workspace_bytes": (Z, [I, I, I, I]),
+            "q4_gemm_tile_shape": (I, [I, I, I, I, P, P, P]),
             "q4_quantize_act_order_host": (I, [P, I, I, I, P, P, P, P]),
             "q4_pack_act_order": (I, [P, P, P, P, I, I, I, P, Z, P]),
             "q4_permute_columns": (I, [P, I, I, I, P, P, P]),
@@ -196,8 +197,25 @@ def q4_unpack(blob, N, K, group=GROUP):
 
 # ---------------------------------------------------------------- W4A16 forward (device)
 
-def q4_gemm(X, packed, N, group=GROUP, Y=None, stream=None):
-    """Y[M, N] = X[M, K] · dequant(W)ᵀ; X fp16/bf16 on the device, packed from q4_pack."""
+def q4_gemm_workspace_bytes(M, N, K, group=GROUP):
+    """Bytes of device workspace q4_gemm uses for an M x N x K layer (0: none)."""
+    return int(lib().q4_gemm_workspace_bytes(M, N, K, group))
+
+
+def _workspace(M, N, K, group, device, workspace):
+    need = q4_gemm_workspace_bytes(M, N, K, group)
+    if workspace is not None:
+        _dev(workspace, torch.uint8, "workspace")
+        if workspace.numel() < need:
+            raise QLError(f"q4_gemm: workspace has {workspace.numel()} bytes, needs {need}")
+        return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device) if need else None
+
+
+def q4_gemm(X, packed, N, group=GROUP, Y=None, workspace=None, stream=None):
+    """Y[M, N] = X[M, K] · dequant(W)ᵀ; X fp16/bf16 on the device, packed from q4_pack.
+    workspace: a uint8 device buffer of at least q4_gemm_workspace_bytes(M, N, K)
+    bytes, or None (then one is allocated when the plan splits K)."""
     X = _dev(X, name="X")
     _dev(packed, torch.uint8, "packed")
     if X.dim() != 2:
@@ -208,9 +226,10 @@ def q4_gemm(X, packed, N, group=GROUP, Y=None, stream=None):
     else:
         _dev(Y, X.dtype, "Y")
         _shape(Y, (M, N), "q4_gemm: Y")
-    _same_device("q4_gemm", X, packed, Y)
+    ws = _workspace(M, N, K, group, X.device, workspace)
+    _same_device("q4_gemm", X, packed, Y, ws)
     _check(lib().q4_gemm(_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group, _ptr(Y),
-                         _stream(X, stream)), "q4_gemm")
+                         _ptr(ws), 0 if ws is None else ws.numel(), _stream(X, stream)), "q4_gemm")
     return Y
 
 
@@ -266,36 +285,47 @@ def q4_permute_columns(X, perm, Xp=None, stream=None):
 
 def q4_gemm_act_order(X, packed, perm, N, group=GROUP, Y=None, stream=None):
     """Y = X · dequant(W)ᵀ for an act-order blob: q4_permute_columns, then q4_gemm."""
-    return q4_gemm(q4_permute_columns(X, perm, stream=stream), packed, N, group, Y, stream)
+    return q4_gemm(q4_permute_columns(X, perm, stream=stream), packed, N, group, Y, stream=stream)
 
 
-def q4_gemm_tile_shape(M, N, K):
+def q4_gemm_tile_shape(M, N, K, with_workspace=True):
     """(rows, cols) of the workgroup tile q4_gemm uses for M x N x K; (0, 0)
     when M <= 16 (the decode kernel)."""
-    r, c = C.c_int(0), C.c_int(0)
-    _check(lib().q4_gemm_tile_shape(M, N, K, C.byref(r), C.byref(c)), "q4_gemm_tile_shape")
-    return r.value, c.value
+    return q4_gemm_plan(M, N, K, with_workspace)[:2]
 
 
-def q4_gemm_launcher(X, packed, N, Y, group=GROUP, stream=None):
+def q4_gemm_plan(M, N, K, with_workspace=True):
+    """(rows, cols, splits): q4_gemm's workgroup tile and K splits for M x N x K
+    with a workspace or without one; (0, 0, 1) when M <= 16 (the decode kernel)."""
+    r, c, s = C.c_int(0), C.c_int(0), C.c_int(0)
+    _check(lib().q4_gemm_tile_shape(M, N, K, int(bool(with_workspace)), C.byref(r), C.byref(c), C.byref(s)),
+           "q4_gemm_tile_shape")
+    return r.value, c.value, s.value
+
+
+def q4_gemm_launcher(X, packed, N, Y, group=GROUP, workspace=None, stream=None):
     """Checks the operands of q4_gemm once and returns a callable that
     launches it again on the same buffers with the arguments already
     marshalled (for tight launch loops: the C entry point still validates
-    every call)."""
+    every call).  The workspace (allocated here when None and needed) lives
+    with the callable."""
     X = _dev(X, name="X")
     _dev(packed, torch.uint8, "packed")
     _dev(Y, X.dtype, "Y")
     M, K = X.shape
     if tuple(Y.shape) != (M, N):
         raise QLError(f"q4_gemm: Y has shape {tuple(Y.shape)}, expected {(M, N)}")
+    ws = _workspace(M, N, K, group, X.device, workspace)
     f = lib().q4_gemm
-    args = (_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group, _ptr(Y), _stream(X, stream))
+    args = (_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group, _ptr(Y), _ptr(ws),
+            0 if ws is None else ws.numel(), _stream(X, stream))
 
     def launch():
         rc = f(*args)
         if rc != 0:
             _check(rc, "q4_gemm")
 
+    launch.workspace = ws
     return launch
 
 

@@ -45,45 +45,85 @@ const char* ql_last_error(void) { return ql::g_last_error.c_str(); }
 
 int ql_abi_version(void) { return QL_ABI_VERSION; }
 
-int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed, size_t packed_bytes, int group,
-            void* Y, void* stream) {
+namespace {
+
+// checks shared by q4_gemm and q4_gemm_no_alloc; on QL_OK with *run set the
+// layer is non-empty and its blob layout is in *L
+int q4_gemm_check(const char* fn, const void* X, int x_dtype, int M, int K, int N, const void* packed,
+                  size_t packed_bytes, int group, const void* Y, ql::Q4Layout* L, bool* run) {
+  *run = false;
   if (M < 0 || N < 0 || K <= 0)
-    return ql::set_error(QL_ERR_SHAPE, "q4_gemm: need M >= 0, N >= 0, K > 0 (got %d, %d, %d)", M, N, K);
+    return ql::set_error(QL_ERR_SHAPE, "%s: need M >= 0, N >= 0, K > 0 (got %d, %d, %d)", fn, M, N, K);
   if (group != ql::kGroup)
-    return ql::set_error(QL_ERR_UNSUPPORTED, "q4_gemm: group=%d; this build supports group=128", group);
-  if (K % group) return ql::set_error(QL_ERR_SHAPE, "q4_gemm: K=%d is not a multiple of group=%d", K, group);
-  if (!valid_dtype(x_dtype)) return ql::set_error(QL_ERR_DTYPE, "q4_gemm: x_dtype=%d", x_dtype);
+    return ql::set_error(QL_ERR_UNSUPPORTED, "%s: group=%d; this build supports group=128", fn, group);
+  if (K % group) return ql::set_error(QL_ERR_SHAPE, "%s: K=%d is not a multiple of group=%d", fn, K, group);
+  if (!valid_dtype(x_dtype)) return ql::set_error(QL_ERR_DTYPE, "%s: x_dtype=%d", fn, x_dtype);
   if (M == 0 || N == 0) return QL_OK;
-  if (!X || !packed || !Y) return ql::set_error(QL_ERR_NULL, "q4_gemm: NULL X, packed or Y");
+  if (!X || !packed || !Y) return ql::set_error(QL_ERR_NULL, "%s: NULL X, packed or Y", fn);
   if (!aligned16(X) || !aligned16(packed) || !aligned16(Y))
-    return ql::set_error(QL_ERR_ALIGN, "q4_gemm: X, packed and Y must be 16-byte aligned");
-  const ql::Q4Layout L = ql::q4_layout(N, K);
-  if (packed_bytes < L.bytes)
-    return ql::set_error(QL_ERR_SIZE, "q4_gemm: packed_bytes=%zu < %zu for N=%d K=%d", packed_bytes, L.bytes, N, K);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf16 = x_dtype == QL_BF16;
-  if (M <= ql::kGemvMaxM) {
-    const ql::GemvPlan P = ql::plan_q4_gemv(M, N, K);
-    return hip_status("q4_gemm", ql::launch_q4_gemv(X, bf16, M, K, N, static_cast<const uint8_t*>(packed),
-                                                     L, P, Y, st));
-  }
+    return ql::set_error(QL_ERR_ALIGN, "%s: X, packed and Y must be 16-byte aligned", fn);
+  *L = ql::q4_layout(N, K);
+  if (packed_bytes < L->bytes)
+    return ql::set_error(QL_ERR_SIZE, "%s: packed_bytes=%zu < %zu for N=%d K=%d", fn, packed_bytes, L->bytes, N, K);
   // the large-M kernel addresses X and the weights with 32-bit byte offsets
-  if ((size_t)M * K * 2 > 0xFFFFFFFFu || L.bytes > 0xFFFFFFFFu)
-    return ql::set_error(QL_ERR_UNSUPPORTED, "q4_gemm: M*K*2 = %zu bytes or a packed blob of %zu bytes exceeds 4 GiB",
-                         (size_t)M * K * 2, L.bytes);
-  return hip_status("q4_gemm", ql::launch_q4_gemm(X, bf16, M, K, N, static_cast<const uint8_t*>(packed), L, Y, st));
+  if (M > ql::kGemvMaxM && ((size_t)M * K * 2 > 0xFFFFFFFFu || L->bytes > 0xFFFFFFFFu))
+    return ql::set_error(QL_ERR_UNSUPPORTED, "%s: M*K*2 = %zu bytes or a packed blob of %zu bytes exceeds 4 GiB", fn,
+                         (size_t)M * K * 2, L->bytes);
+  *run = true;
+  return QL_OK;
 }
 
-int q4_gemm_tile_shape(int M, int N, int K, int* rows, int* cols) {
+// launches a checked layer; ws: the plan's workspace (null: no K split)
+int q4_gemm_launch(const char* fn, const void* X, int x_dtype, int M, int K, int N, const void* packed,
+                   const ql::Q4Layout& L, void* Y, const ql::GemmPlan* plan, float* ws, hipStream_t st) {
+  const bool bf16 = x_dtype == QL_BF16;
+  const uint8_t* blob = static_cast<const uint8_t*>(packed);
+  if (M <= ql::kGemvMaxM)
+    return hip_status(fn, ql::launch_q4_gemv(X, bf16, M, K, N, blob, L, ql::plan_q4_gemv(M, N, K), Y, st));
+  return hip_status(fn, ql::launch_q4_gemm(X, bf16, M, K, N, blob, L, *plan, Y, ws, st));
+}
+
+}  // namespace
+
+size_t q4_gemm_workspace_bytes(int M, int N, int K, int group) {
+  if (M <= ql::kGemvMaxM || N <= 0 || K <= 0 || group != ql::kGroup || K % group) return 0;
+  return ql::gemm_workspace_bytes(ql::plan_q4_gemm(M, N, K, 8), M, N);
+}
+
+int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed, size_t packed_bytes, int group,
+            void* Y, void* workspace, size_t ws_bytes, void* stream) {
+  ql::Q4Layout L;
+  bool run;
+  const int rc = q4_gemm_check("q4_gemm", X, x_dtype, M, K, N, packed, packed_bytes, group, Y, &L, &run);
+  if (rc != QL_OK || !run) return rc;
+  if (workspace && !aligned16(workspace))
+    return ql::set_error(QL_ERR_ALIGN, "q4_gemm: the workspace must be 16-byte aligned");
+  ql::GemmPlan plan{0, 1, 0};
+  if (M > ql::kGemvMaxM) {
+    // without a workspace the layer runs unsplit (a valid, possibly slower plan)
+    plan = ql::plan_q4_gemm(M, N, K, workspace ? 8 : 1);
+    const size_t need = ql::gemm_workspace_bytes(plan, M, N);
+    if (ws_bytes < need)
+      return ql::set_error(QL_ERR_SIZE, "q4_gemm: ws_bytes=%zu < %zu (q4_gemm_workspace_bytes) for M=%d N=%d K=%d",
+                           ws_bytes, need, M, N, K);
+  }
+  return q4_gemm_launch("q4_gemm", X, x_dtype, M, K, N, packed, L, Y, &plan, static_cast<float*>(workspace),
+                        static_cast<hipStream_t>(stream));
+}
+
+int q4_gemm_tile_shape(int M, int N, int K, int with_workspace, int* rows, int* cols, int* splits) {
   if (!rows || !cols) return ql::set_error(QL_ERR_NULL, "q4_gemm_tile_shape: NULL rows or cols");
   if (M < 0 || N <= 0 || K <= 0 || K % ql::kGroup)
     return ql::set_error(QL_ERR_SHAPE, "q4_gemm_tile_shape: need M >= 0, N > 0, K > 0, K %% 128 == 0 (got %d, %d, %d)",
                          M, N, K);
   if (M <= ql::kGemvMaxM) {
     *rows = *cols = 0;
+    if (splits) *splits = 1;
     return QL_OK;
   }
-  ql::gemm_tile_shape(M, N, K, rows, cols);
+  const ql::GemmPlan p = ql::plan_q4_gemm(M, N, K, with_workspace ? 8 : 1);
+  ql::gemm_tile_shape(p, rows, cols);
+  if (splits) *splits = p.splits;
   return QL_OK;
 }
 

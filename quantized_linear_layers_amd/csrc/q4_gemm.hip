@@ -94,6 +94,8 @@ struct GemmArgs {
   const uint32_t* S;       // [Kp/256][ldw] scale pairs
   const uint8_t* Z;        // [Kp/256][ldw] zero pairs
   uint16_t* Y;             // [M][ldy]
+  int kbs;                 // K blocks per split: split s = blockIdx.y takes blocks s * kbs .. (s + 1) * kbs - 1
+  float* P;                // split-K partial tiles [gridDim.y][M][ldy] (fp32), or null: store Y
 };
 
 // ---- global -> LDS copies and counter waits
@@ -406,18 +408,18 @@ __device__ __forceinline__ void compute(Frag<C>& fr, int kb, const uint32_t (&xr
 
 // Step i of a K-group's run (the run's block kb0 + i, present if i < cnt):
 // wait for its copies, refill the stage read one step earlier with the block
-// kStages - 1 steps ahead (clamped to the layer's last block: a valid copy
-// that is never multiplied), then multiply.  Every wave of the workgroup
+// kStages - 1 steps ahead (clamped to the layer's last block kblast: a valid
+// copy that is never multiplied), then multiply.  Every wave of the workgroup
 // takes the same number of steps, so the barriers match.
 template <class C, bool BF16, int S>
 __device__ __forceinline__ void kstep(uint8_t* lds, Frag<C>& fr, const GemmArgs& a, const FillPlan<C>& f, int i,
-                                      int kb0, int cnt, int nkb, const uint32_t (&xrd)[4], uint32_t wrd,
+                                      int kb0, int cnt, int kblast, const uint32_t (&xrd)[4], uint32_t wrd,
                                       uint32_t szrd, int zshift) {
   // this wave's copies of step i have landed once only the later steps' remain
   wait_vm<(C::kStages - 2) * C::kLoads>();
   __builtin_amdgcn_s_barrier();   // every wave's copies of step i landed; step i - 1 fully read
   constexpr int F = (S + C::kStages - 1) % C::kStages;
-  const int kbf = min(kb0 + i + C::kStages - 1, nkb - 1);
+  const int kbf = min(kb0 + i + C::kStages - 1, kblast);
   // with kSpread the refill's copies go out in four shares, one per k step:
   // a wave stalls on a copy until the address unit takes it, and issuing
   // them all at once after the barrier held a small tile's arithmetic back
@@ -448,10 +450,13 @@ __global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(GemmArgs a) {
   tile_of(blockIdx.x, (a.M + C::BM - 1) / C::BM, (a.N + C::BN - 1) / C::BN, mtile, ntile);
   const int m0 = mtile * C::BM, n0 = ntile * C::BN;
   const int nw0 = n0 + 32 * kNTW * wn;           // first column of this wave
-  const int nkb = a.K / BK;
+  const int kblast = a.K / BK - 1;
+  // this workgroup's split of K: blocks sb0 .. sb0 + nkb - 1 (possibly none)
+  const int sb0 = min(kblast + 1, (int)blockIdx.y * a.kbs);
+  const int nkb = min(kblast + 1, sb0 + a.kbs) - sb0;
   // this K-group's run of blocks: kb0 .. kb0 + cnt - 1 (every run takes `steps` steps)
   const int steps = (nkb + C::WK - 1) / C::WK;
-  const int kb0 = min(nkb, wk * steps), cnt = min(nkb, kb0 + steps) - kb0;
+  const int kb0 = sb0 + min(nkb, wk * steps), cnt = min(sb0 + nkb, kb0 + steps) - kb0;
   const int kgoff = wk * C::kKGroup;             // this K-group's part of every stage
 
   // ---- copy plan.  X: the stage's 32 blocks of 1 KB (8 rows x 128 bytes),
@@ -508,14 +513,14 @@ __global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(GemmArgs a) {
       for (int e = 0; e < 16; ++e) fr.acc[i][t][e] = 0.0f;
 
   // prologue: steps 0 .. kStages - 2 in flight (clamped to the last block)
-  static_for<0, kStages - 1>([&](auto J) { fill<C, J>(lds, a, f, min(kb0 + (int)J, nkb - 1)); });
+  static_for<0, kStages - 1>([&](auto J) { fill<C, J>(lds, a, f, min(kb0 + (int)J, kblast)); });
 
   int i = 0;
   for (; i + kStages <= steps; i += kStages)
     static_for<0, kStages>(
-        [&](auto S) { kstep<C, BF16, S>(lds, fr, a, f, i + S, kb0, cnt, nkb, xrd, wrd, szrd, zshift); });
+        [&](auto S) { kstep<C, BF16, S>(lds, fr, a, f, i + S, kb0, cnt, kblast, xrd, wrd, szrd, zshift); });
   static_for<0, kStages - 1>([&](auto S) {
-    if (i + S < steps) kstep<C, BF16, S>(lds, fr, a, f, i + S, kb0, cnt, nkb, xrd, wrd, szrd, zshift);
+    if (i + S < steps) kstep<C, BF16, S>(lds, fr, a, f, i + S, kb0, cnt, kblast, xrd, wrd, szrd, zshift);
   });
   wait_vm<0>();                                  // no copy may still target LDS at exit
 
@@ -547,7 +552,10 @@ __global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(GemmArgs a) {
     }
   }
 
-  // ---- store: acc element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32
+  // ---- store: acc element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32; with a K split the fp32 partial tile goes to the split's
+  // slice of P instead (added and rounded by splitk_reduce_kernel)
+  float* part = a.P ? a.P + (size_t)blockIdx.y * a.M * a.ldy : nullptr;
 #pragma unroll
   for (int t = 0; t < kNTW; ++t) {
     const int n = nw0 + 32 * t + l32;
@@ -559,20 +567,63 @@ __global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(GemmArgs a) {
         const int m = m0 + 32 * mt + 8 * (e >> 2) + 4 * half + (e & 3);
         if (m < a.M) {
           const float v = fr.acc[mt][t][e];
-          a.Y[(size_t)m * a.ldy + n] =
-              BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+          if (part)
+            part[(size_t)m * a.ldy + n] = v;
+          else
+            a.Y[(size_t)m * a.ldy + n] =
+                BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
         }
       }
   }
 }
 
+// Y = the 16-bit rounding of the sum of the S fp32 partial results P[s]
+// (split s of K), added in split order: 4 consecutive elements per thread,
+// the last partial group element by element.
+template <bool BF16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int S, size_t MN,
+                                                            uint16_t* __restrict__ Y) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  auto cvt = [](float v) {
+    return BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+  };
+  if (i + 4 <= MN) {
+    float4 acc = *reinterpret_cast<const float4*>(P + i);
+    for (int s = 1; s < S; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(P + (size_t)s * MN + i);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const uint2 o = make_uint2(cvt(acc.x) | ((uint32_t)cvt(acc.y) << 16), cvt(acc.z) | ((uint32_t)cvt(acc.w) << 16));
+    *reinterpret_cast<uint2*>(Y + i) = o;
+  } else {
+    for (size_t j = i; j < MN; ++j) {
+      float acc = P[j];
+      for (int s = 1; s < S; ++s) acc += P[(size_t)s * MN + j];
+      Y[j] = cvt(acc);
+    }
+  }
+}
+
 template <class C>
-hipError_t launch_cfg(const GemmArgs& a, bool bf16, hipStream_t st) {
+hipError_t launch_cfg(const GemmArgs& a, bool bf16, hipStream_t st, int splits = 1) {
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
   if (bf16)
-    hipLaunchKernelGGL((q4_gemm_kernel<C, true>), dim3(tiles), dim3(64 * C::kWaves), 0, st, a);
+    hipLaunchKernelGGL((q4_gemm_kernel<C, true>), dim3(tiles, splits), dim3(64 * C::kWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((q4_gemm_kernel<C, false>), dim3(tiles), dim3(64 * C::kWaves), 0, st, a);
+    hipLaunchKernelGGL((q4_gemm_kernel<C, false>), dim3(tiles, splits), dim3(64 * C::kWaves), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const float* P, int S, size_t MN, uint16_t* Y, bool bf16, hipStream_t st) {
+  const dim3 grid((unsigned)((MN + 1023) / 1024));
+  if (bf16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<true>, grid, dim3(256), 0, st, P, S, MN, Y);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, st, P, S, MN, Y);
   return hipGetLastError();
 }
 
@@ -600,33 +651,50 @@ constexpr TileOpt kTiles[] = {
 };
 constexpr int kNumTiles = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
 
-// Tile (index into kTiles) for an M x N x K product: the smallest estimate
+// Plan of the large-M kernel for an M x N x K product: the tile (index into
+// kTiles) and the number of splits of K across workgroups.  The estimate is
 // rounds x (ramp + K steps of a K-group x step time), with 256 workgroups a
-// round and a ramp of 2.5 us a round; ties go to the earlier (larger) tile.
-int gemm_tile(int M, int N, int K) {
+// round and a ramp of 2.5 us a round, plus, with a split, the reduce pass
+// (a launch of about 2 us and the partials written and read back at about
+// 4 TB/s).  Ties go to the earlier (larger) tile and to fewer splits.  A
+// split is only considered with at most 256 tokens (with more, the tiles
+// alone fill the compute units).
+GemmPlan plan_q4_gemm(int M, int N, int K, int max_splits) {
   const long nkb = K / BK;
-  int best = 0;
+  GemmPlan best{0, 1, (int)nkb};
   double best_cost = 0.0;
+  static const int kSplits[] = {1, 2, 3, 4, 6, 8};
   for (int t = 0; t < kNumTiles; ++t) {
     const TileOpt& o = kTiles[t];
-    const long wgs = (long)((M + o.bm - 1) / o.bm) * ((N + o.bn - 1) / o.bn);
-    const double cost = (double)((wgs + 255) / 256) * (2.5 + (double)((nkb + o.wk - 1) / o.wk) * o.step);
-    if (t == 0 || cost < best_cost) {
-      best = t;
-      best_cost = cost;
+    const long tiles = (long)((M + o.bm - 1) / o.bm) * ((N + o.bn - 1) / o.bn);
+    for (int S : kSplits) {
+      if (S > max_splits || (S > 1 && (M > 256 || t == 0))) continue;
+      const long kbs = (nkb + S - 1) / S;
+      const long splits = (nkb + kbs - 1) / kbs;             // no empty split
+      if (S > 1 && splits < 2) continue;
+      const long wgs = tiles * splits;
+      double cost = (double)((wgs + 255) / 256) * (2.5 + (double)((kbs + o.wk - 1) / o.wk) * o.step);
+      if (splits > 1) cost += 2.0 + (double)(2 * splits * 4 + 2) * M * N / 4.0e6;
+      if ((t == 0 && S == 1) || cost < best_cost) {
+        best = GemmPlan{t, (int)splits, (int)kbs};
+        best_cost = cost;
+      }
     }
   }
   return best;
 }
 
-void gemm_tile_shape(int M, int N, int K, int* rows, int* cols) {
-  const TileOpt& o = kTiles[gemm_tile(M, N, K)];
-  *rows = o.bm;
-  *cols = o.bn;
+size_t gemm_workspace_bytes(const GemmPlan& p, int M, int N) {
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+}
+
+void gemm_tile_shape(const GemmPlan& p, int* rows, int* cols) {
+  *rows = kTiles[p.tile].bm;
+  *cols = kTiles[p.tile].bn;
 }
 
 hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const uint8_t* blob, const Q4Layout& L,
-                          void* Y, hipStream_t st) {
+                          const GemmPlan& p, void* Y, float* ws, hipStream_t st) {
   GemmArgs a;
   a.X = static_cast<const uint16_t*>(X);
   a.M = M;
@@ -639,13 +707,19 @@ hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const u
   a.S = reinterpret_cast<const uint32_t*>(blob + L.s_off);
   a.Z = blob + L.z_off;
   a.Y = static_cast<uint16_t*>(Y);
-  switch (gemm_tile(M, N, K)) {
-    case 1: return launch_cfg<Cfg<4, 4, 2, 3>>(a, bf16, st);
-    case 2: return launch_cfg<Cfg<2, 4, 2, 5>>(a, bf16, st);
-    case 3: return launch_cfg<Cfg<2, 2, 4, 3>>(a, bf16, st);
-    case 4: return launch_cfg<Cfg<1, 2, 4, 5>>(a, bf16, st);
-    case 5: return launch_cfg<Cfg<1, 1, 8, 3>>(a, bf16, st);
-    default: break;
+  a.kbs = p.kbs;
+  a.P = p.splits > 1 ? ws : nullptr;
+  if (p.tile != 0) {
+    hipError_t e;
+    switch (p.tile) {
+      case 1: e = launch_cfg<Cfg<4, 4, 2, 3>>(a, bf16, st, p.splits); break;
+      case 2: e = launch_cfg<Cfg<2, 4, 2, 5>>(a, bf16, st, p.splits); break;
+      case 3: e = launch_cfg<Cfg<2, 2, 4, 3>>(a, bf16, st, p.splits); break;
+      case 4: e = launch_cfg<Cfg<1, 2, 4, 5>>(a, bf16, st, p.splits); break;
+      default: e = launch_cfg<Cfg<1, 1, 8, 3>>(a, bf16, st, p.splits); break;
+    }
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_reduce(ws, p.splits, (size_t)M * N, a.Y, bf16, st);
   }
   // 256 x 256 tiles, one workgroup per compute unit.  When their last round
   // would leave at least half the compute units idle (the Llama-3-8B MLP

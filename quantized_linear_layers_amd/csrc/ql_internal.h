@@ -82,18 +82,24 @@ struct GemvPlan {
 
 GemvPlan plan_q4_gemv(int M, int N, int K);
 
-// workgroup tile the large-M kernel uses for an M x N x K product: index
-// into its table, and the tile's rows and columns
-int gemm_tile(int M, int N, int K);
-void gemm_tile_shape(int M, int N, int K, int* rows, int* cols);
+// plan of the large-M kernel for an M x N x K product: its workgroup tile
+// (index into its table) and the split of K across workgroups (splits groups
+// of kbs 64-wide K blocks; splits == 1: no split, no workspace)
+struct GemmPlan {
+  int tile, splits, kbs;
+};
+GemmPlan plan_q4_gemm(int M, int N, int K, int max_splits);
+size_t gemm_workspace_bytes(const GemmPlan& p, int M, int N);
+void gemm_tile_shape(const GemmPlan& p, int* rows, int* cols);
 // token counts served by the decode-family kernel; larger M takes the GEMM
 constexpr int kGemvMaxM = 16;
 hipError_t launch_q4_gemv(const void* X, bool bf16, int M, int K, int N,
                           const uint8_t* blob, const Q4Layout& L, const GemvPlan& P,
                           void* Y, hipStream_t st);
 
-hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N,
-                          const uint8_t* blob, const Q4Layout& L, void* Y, hipStream_t st);
+// ws: the plan's workspace (gemm_workspace_bytes), or null when p.splits == 1
+hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const uint8_t* blob, const Q4Layout& L,
+                          const GemmPlan& p, void* Y, float* ws, hipStream_t st);
 
 hipError_t launch_permute_cols(const void* X, int M, int K, const int32_t* perm, void* Xp, hipStream_t st);
 hipError_t launch_rmsnorm_quant(const void* X, bool bf16, int M, int K, const void* gamma, float eps, int8_t* Aq,

@@ -31,7 +31,8 @@ Evaluation forms (one per kernel family):
   dequant16 the GEMM: each weight s * (q - z) is rounded once to the 16-bit
             type (a deterministic shift of the result, computed exactly from
             the oracle's weights), products are exact in fp32, each MFMA adds
-            16 products (17 roundings), and up to 8 K-group partials are
+            16 products (17 roundings), and the partials of up to 8 K-groups
+            in a workgroup and of up to 8 K splits across workgroups are
             added at the end.
 """
 
@@ -95,7 +96,9 @@ def dequant16_terms(X, Wd, dtype, mfma_k=16):
     W16 = nu.to_bf16(Wd) if dtype == "bf16" else nu.to_f16(Wd).astype(np.float64)
     shift = X @ (np.asarray(W16, np.float64) - Wd).T
     A = np.abs(X) @ np.abs(np.asarray(W16, np.float64)).T             # bound of every partial sum
-    var = ((K // mfma_k) * (mfma_k + 1) + 8) * step_of(A, "f32") ** 2 / 12.0
+    # one rounding per product and per MFMA, then the partial tiles of up to 8
+    # K-groups in a workgroup times up to 8 K splits across workgroups
+    var = ((K // mfma_k) * (mfma_k + 1) + 64) * step_of(A, "f32") ** 2 / 12.0
     return shift, np.sqrt(var)
 
 

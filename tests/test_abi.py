@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -48,22 +48,22 @@ def test_q4_gemm_validation():
     L = ql.lib()
     P = FAKE
     # K not a multiple of the group
-    assert L.q4_gemm(P, 0, 1, 200, 64, P, BIG, 128, P, None) == QL_ERR_SHAPE
+    assert L.q4_gemm(P, 0, 1, 200, 64, P, BIG, 128, P, None, 0, None) == QL_ERR_SHAPE
     assert "multiple" in last_error()
-    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 64, P, None) == QL_ERR_UNSUPPORTED
-    assert L.q4_gemm(P, 7, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_DTYPE
-    assert L.q4_gemm(P, 0, -1, 256, 64, P, BIG, 128, P, None) == QL_ERR_SHAPE
-    assert L.q4_gemm(P, 0, 1, 0, 64, P, BIG, 128, P, None) == QL_ERR_SHAPE
-    assert L.q4_gemm(None, 0, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_NULL
-    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 128, None, None) == QL_ERR_NULL
-    assert L.q4_gemm(FAKE_MIS, 0, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_ALIGN
-    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 128, FAKE_MIS, None) == QL_ERR_ALIGN
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 64, P, None, 0, None) == QL_ERR_UNSUPPORTED
+    assert L.q4_gemm(P, 7, 1, 256, 64, P, BIG, 128, P, None, 0, None) == QL_ERR_DTYPE
+    assert L.q4_gemm(P, 0, -1, 256, 64, P, BIG, 128, P, None, 0, None) == QL_ERR_SHAPE
+    assert L.q4_gemm(P, 0, 1, 0, 64, P, BIG, 128, P, None, 0, None) == QL_ERR_SHAPE
+    assert L.q4_gemm(None, 0, 1, 256, 64, P, BIG, 128, P, None, 0, None) == QL_ERR_NULL
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 128, None, None, 0, None) == QL_ERR_NULL
+    assert L.q4_gemm(FAKE_MIS, 0, 1, 256, 64, P, BIG, 128, P, None, 0, None) == QL_ERR_ALIGN
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, BIG, 128, FAKE_MIS, None, 0, None) == QL_ERR_ALIGN
     # a blob smaller than the layout of (N, K) is rejected
     need = L.q4_packed_bytes(64, 256, 128)
-    assert L.q4_gemm(P, 0, 1, 256, 64, P, need - 1, 128, P, None) == QL_ERR_SIZE
+    assert L.q4_gemm(P, 0, 1, 256, 64, P, need - 1, 128, P, None, 0, None) == QL_ERR_SIZE
     # empty problems are no-ops
-    assert L.q4_gemm(None, 0, 0, 256, 64, None, BIG, 128, None, None) == QL_OK
-    assert L.q4_gemm(None, 0, 4, 256, 0, None, BIG, 128, None, None) == QL_OK
+    assert L.q4_gemm(None, 0, 0, 256, 64, None, BIG, 128, None, None, 0, None) == QL_OK
+    assert L.q4_gemm(None, 0, 4, 256, 0, None, BIG, 128, None, None, 0, None) == QL_OK
 
 
 def test_i8_validation():
@@ -334,18 +334,48 @@ def test_q4_gemm_tile_shape():
     the two non-square tiles above, and the documented errors."""
     assert ql.q4_gemm_tile_shape(16, 4096, 4096) == (0, 0)
     assert ql.q4_gemm_tile_shape(4096, 14336, 4096) == (256, 256)
-    assert ql.q4_gemm_tile_shape(32, 11008, 4096) == (32, 64)
-    assert ql.q4_gemm_tile_shape(128, 11008, 4096) == (64, 128)
-    assert ql.q4_gemm_tile_shape(32, 4096, 4096) == (32, 32)
+    assert ql.q4_gemm_tile_shape(32, 11008, 4096, False) == (32, 64)
+    assert ql.q4_gemm_tile_shape(128, 11008, 4096, False) == (64, 128)
+    assert ql.q4_gemm_tile_shape(32, 4096, 4096, False) == (32, 32)
     for M in (17, 64, 200, 1000):
         for N in (72, 4096, 11008):
-            assert ql.q4_gemm_tile_shape(M, N, 4096) in {(256, 256), (128, 128), (64, 128), (64, 64), (32, 64),
-                                                        (32, 32)}
+            for ws in (False, True):
+                assert ql.q4_gemm_tile_shape(M, N, 4096, ws) in {(256, 256), (128, 128), (64, 128), (64, 64),
+                                                                (32, 64), (32, 32)}
+            assert ql.q4_gemm_plan(M, N, 4096, False)[2] == 1
     L = ql.lib()
     r, c = C.c_int(), C.c_int()
-    assert L.q4_gemm_tile_shape(32, 64, 100, C.byref(r), C.byref(c)) == QL_ERR_SHAPE
-    assert L.q4_gemm_tile_shape(32, 0, 128, C.byref(r), C.byref(c)) == QL_ERR_SHAPE
-    assert L.q4_gemm_tile_shape(32, 64, 128, None, C.byref(c)) == QL_ERR_NULL
+    assert L.q4_gemm_tile_shape(32, 64, 100, 1, C.byref(r), C.byref(c), None) == QL_ERR_SHAPE
+    assert L.q4_gemm_tile_shape(32, 0, 128, 1, C.byref(r), C.byref(c), None) == QL_ERR_SHAPE
+    assert L.q4_gemm_tile_shape(32, 64, 128, 1, None, C.byref(c), None) == QL_ERR_NULL
+    assert L.q4_gemm_tile_shape(32, 64, 128, 0, C.byref(r), C.byref(c), None) == QL_OK
+
+
+def test_q4_gemm_workspace_plan():
+    """The K split: only with M > 16 (and never for prefill-sized M), the
+    workspace is splits x M x N fp32, and a given workspace that is too small
+    is rejected before any launch (no workspace: the layer runs unsplit)."""
+    assert ql.q4_gemm_workspace_bytes(16, 4096, 4096) == 0
+    assert ql.q4_gemm_workspace_bytes(4096, 14336, 4096) == 0
+    assert ql.q4_gemm_plan(4096, 14336, 4096)[2] == 1
+    split_seen = False
+    for M in (17, 32, 64, 128, 256, 300):
+        for (K, N) in ((4096, 4096), (4096, 11008), (11008, 4096), (28672, 8192)):
+            rows, cols, S = ql.q4_gemm_plan(M, N, K)
+            ws = ql.q4_gemm_workspace_bytes(M, N, K)
+            assert ws == (S * M * N * 4 if S > 1 else 0)
+            assert S == 1 or M <= 256
+            split_seen |= S > 1
+    assert split_seen
+    assert ql.q4_gemm_workspace_bytes(32, 4096, 100) == 0           # invalid K
+    L = ql.lib()
+    M, N, K = next((M, N, K) for M in (32, 64) for (K, N) in ((11008, 4096), (28672, 8192))
+                   if ql.q4_gemm_workspace_bytes(M, N, K))
+    need = ql.q4_gemm_workspace_bytes(M, N, K)
+    blob = L.q4_packed_bytes(N, K, 128)
+    assert L.q4_gemm(FAKE, 0, M, K, N, FAKE, blob, 128, FAKE, FAKE, need - 1, None) == QL_ERR_SIZE
+    assert "q4_gemm_workspace_bytes" in last_error()
+    assert L.q4_gemm(FAKE, 0, M, K, N, FAKE, blob, 128, FAKE, FAKE_MIS, need, None) == QL_ERR_ALIGN
 
 
 @pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++17")])

@@ -76,11 +76,21 @@ def assert_parity(Yd, Y64, X64, q, s, z, dtype, M_total, tol=TOL):
     return e
 
 
-def check(W, X, rows=None, cols=None, tol=TOL):
-    """Run the device layer on X and compare the (rows, cols) block with the oracle."""
+def run_unsplit(X, blob, N):
+    """q4_gemm without a workspace (the plan that does not split K)."""
+    Xd = X.cuda()
+    M, K = X.shape
+    Y = torch.full((M, N), float("nan"), dtype=X.dtype, device="cuda")
+    ql.launcher("q4_gemm", Xd, X.dtype, M, K, N, blob, blob.numel(), 128, Y, None, 0)()
+    return Y
+
+
+def check(W, X, rows=None, cols=None, tol=TOL, workspace=True):
+    """Run the device layer on X (with a workspace when its plan needs one, or
+    without) and compare the (rows, cols) block with the oracle."""
     N, K = W.shape
     blob = device_layer(W)
-    Y = ql.q4_gemm(X.cuda(), blob, N)
+    Y = ql.q4_gemm(X.cuda(), blob, N) if workspace else run_unsplit(X, blob, N)
     torch.cuda.synchronize()
     Yd = wl.as_f64(Y.cpu())
     rows = np.arange(X.shape[0]) if rows is None else rows
@@ -142,6 +152,7 @@ def test_gemm_tiles(M, K, N, dtype):
     W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
     X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
     cols = np.sort(r.choice(N, min(N, 512), replace=False))
+    check(W, X, cols=cols, workspace=False)
     check(W, X, cols=cols)
 
 
@@ -154,13 +165,52 @@ def test_gemm_tiles(M, K, N, dtype):
     (70, 2560, 11000, torch.float16, (64, 128)), (100, 6016, 8200, torch.bfloat16, (64, 128)),
     (127, 128, 4160, torch.float16, (64, 128)), (33, 128, 8200, torch.bfloat16, (64, 128))])
 def test_nonsquare_tiles(M, K, N, dtype, tile):
-    assert ql.q4_gemm_tile_shape(M, N, K) == tile
+    assert ql.q4_gemm_tile_shape(M, N, K, with_workspace=False) == tile
     r = np.random.default_rng(M * 7 + K + N)
     W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
     X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
     tail = np.arange(max(0, N - 200), N)
     cols = np.union1d(np.sort(r.choice(N, min(N, 384), replace=False)), tail)
+    check(W, X, cols=cols, workspace=False)
     check(W, X, cols=cols)
+
+
+# shapes whose plan splits K across workgroups (fp32 partials in the
+# workspace, then the reduce pass): the 7B/70B mid-M layers the plan splits,
+# and ragged M, N and K with uneven splits and empty K-group runs; each also
+# runs without a workspace (the unsplit plan) and both are checked
+@pytest.mark.parametrize("M,K,N,dtype", [(32, 11008, 4096, torch.float16), (128, 11008, 4096, torch.float16),
+                                         (64, 28672, 8192, torch.bfloat16), (17, 4096, 4096, torch.bfloat16),
+                                         (40, 11008, 1000, torch.float16), (77, 5248, 700, torch.bfloat16),
+                                         (100, 5248, 500, torch.float16), (130, 6016, 1000, torch.bfloat16),
+                                         (130, 9088, 3000, torch.float16), (200, 9088, 2000, torch.bfloat16)])
+def test_split_k(M, K, N, dtype):
+    rows, cols, S = ql.q4_gemm_plan(M, N, K)
+    assert S > 1, (M, K, N, rows, cols)
+    r = np.random.default_rng(M + K + N)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
+    cols_ = np.union1d(np.sort(r.choice(N, min(N, 384), replace=False)), np.arange(max(0, N - 100), N))
+    check(W, X, cols=cols_)
+    check(W, X, cols=cols_, workspace=False)      # the unsplit plan of the same layer
+
+
+def test_split_k_workspace_contents_do_not_matter():
+    """A workspace full of garbage (NaN bit patterns) gives the same result as
+    a fresh one: every partial is written before the reduce pass reads it."""
+    M, K, N = 32, 11008, 4096
+    w = wl.WORKLOADS["mid_m_7b"]
+    W = wl.weight(w, K, N)
+    X = wl.activations(w, M, K, N).cuda()
+    blob = device_layer(W)
+    need = ql.q4_gemm_workspace_bytes(M, N, K)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    Y1 = ql.q4_gemm(X, blob, N, workspace=ws)
+    ws.fill_(0xFF)
+    Y2 = ql.q4_gemm(X, blob, N, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
 
 
 def test_prefill_sampled():
