@@ -204,6 +204,24 @@ int q4_gemm(const void* X, int x_dtype, int M, int K, int N,
             void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * q4_gemm_no_alloc — q4_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same plan and kernels as q4_gemm with a workspace, the
+ * K-split partials kept in a static device array of the library
+ * (32 MiB per device, held until the process ends; looked up once per device
+ * on the first call there).  Allocates nothing and calls no allocating
+ * routine.  Every call on one device shares that array: calls that overlap
+ * on one device (other streams, other threads) race and must not be issued.
+ * Nothing in the array needs clearing: every partial is written before it is
+ * read.  Arguments as q4_gemm without the workspace.
+ * Errors: as q4_gemm; QL_ERR_SIZE also when the layer's plan needs more
+ *         scratch than the library holds (more than 32 MiB: q4_gemm with a
+ *         workspace serves it).
+ */
+int q4_gemm_no_alloc(const void* X, int x_dtype, int M, int K, int N,
+                     const void* packed, size_t packed_bytes, int group, void* Y, void* stream);
+
+/*
  * q4_gemm_workspace_bytes — bytes of workspace q4_gemm uses for an M x N x K
  * layer (host; 0 when its plan does not split K, and for invalid sizes).
  */

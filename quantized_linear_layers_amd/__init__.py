@@ -45,6 +45,7 @@ def lib():
             "q4_unpack": (I, [P, Z, I, I, I, P, P, P]),
             "q4_gemm": (I, [P, I, I, I, I, P, Z, I, P, P, Z, P]),
             "q4_gemm_workspace_bytes": (Z, [I, I, I, I]),
+            "q4_gemm_no_alloc": (I, [P, I, I, I, I, P, Z, I, P, P]),
             "q4_gemm_tile_shape": (I, [I, I, I, I, P, P, P]),
             "q4_quantize_act_order_host": (I, [P, I, I, I, P, P, P, P]),
             "q4_pack_act_order": (I, [P, P, P, P, I, I, I, P, Z, P]),
@@ -230,6 +231,22 @@ def q4_gemm(X, packed, N, group=GROUP, Y=None, workspace=None, stream=None):
     _same_device("q4_gemm", X, packed, Y, ws)
     _check(lib().q4_gemm(_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group, _ptr(Y),
                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(X, stream)), "q4_gemm")
+    return Y
+
+
+def q4_gemm_no_alloc(X, packed, N, Y, group=GROUP, stream=None):
+    """q4_gemm into a caller-given Y with the library's static scratch: the C
+    call allocates nothing (neither does this wrapper)."""
+    X = _dev(X, name="X")
+    _dev(packed, torch.uint8, "packed")
+    _dev(Y, X.dtype, "Y")
+    if X.dim() != 2:
+        raise QLError(f"q4_gemm_no_alloc: X must be 2-D, got shape {tuple(X.shape)}")
+    M, K = X.shape
+    _shape(Y, (M, N), "q4_gemm_no_alloc: Y")
+    _same_device("q4_gemm_no_alloc", X, packed, Y)
+    _check(lib().q4_gemm_no_alloc(_ptr(X), _dtype_code(X.dtype), M, K, N, _ptr(packed), packed.numel(), group,
+                                  _ptr(Y), _stream(X, stream)), "q4_gemm_no_alloc")
     return Y
 
 

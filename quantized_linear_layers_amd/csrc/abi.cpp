@@ -111,6 +111,31 @@ int q4_gemm(const void* X, int x_dtype, int M, int K, int N, const void* packed,
                         static_cast<hipStream_t>(stream));
 }
 
+int q4_gemm_no_alloc(const void* X, int x_dtype, int M, int K, int N, const void* packed, size_t packed_bytes,
+                     int group, void* Y, void* stream) {
+  ql::Q4Layout L;
+  bool run;
+  const int rc = q4_gemm_check("q4_gemm_no_alloc", X, x_dtype, M, K, N, packed, packed_bytes, group, Y, &L, &run);
+  if (rc != QL_OK || !run) return rc;
+  ql::GemmPlan plan{0, 1, 0};
+  void* ws = nullptr;
+  if (M > ql::kGemvMaxM) {
+    plan = ql::plan_q4_gemm(M, N, K, 8);                 // the plan q4_gemm runs with a workspace
+    const size_t need = ql::gemm_workspace_bytes(plan, M, N);
+    if (need > ql::kStaticScratchBytes)
+      return ql::set_error(QL_ERR_SIZE,
+                           "q4_gemm_no_alloc: M=%d N=%d K=%d needs %zu bytes of scratch; the library's static "
+                           "scratch holds %zu (use q4_gemm with a workspace)",
+                           M, N, K, need, ql::kStaticScratchBytes);
+    if (need) {
+      const int e = hip_status("q4_gemm_no_alloc", ql::static_scratch(&ws));
+      if (e != QL_OK) return e;
+    }
+  }
+  return q4_gemm_launch("q4_gemm_no_alloc", X, x_dtype, M, K, N, packed, L, Y, &plan, static_cast<float*>(ws),
+                        static_cast<hipStream_t>(stream));
+}
+
 int q4_gemm_tile_shape(int M, int N, int K, int with_workspace, int* rows, int* cols, int* splits) {
   if (!rows || !cols) return ql::set_error(QL_ERR_NULL, "q4_gemm_tile_shape: NULL rows or cols");
   if (M < 0 || N <= 0 || K <= 0 || K % ql::kGroup)

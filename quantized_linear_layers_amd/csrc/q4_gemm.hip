@@ -31,6 +31,7 @@
 //     lets each lane read its 8 codes of both steps as one 8-byte word pair.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "ql_internal.h"
@@ -691,6 +692,35 @@ size_t gemm_workspace_bytes(const GemmPlan& p, int M, int N) {
 void gemm_tile_shape(const GemmPlan& p, int* rows, int* cols) {
   *rows = kTiles[p.tile].bm;
   *cols = kTiles[p.tile].bn;
+}
+
+// ---- static scratch for callers that cannot allocate (q4_gemm_no_alloc).
+// Each device that loads the library holds its own copy of this array until
+// the process ends.  In host code `scratch` is only a stand-in symbol: its
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const uint8_t* blob, const Q4Layout& L,

@@ -97,6 +97,11 @@ hipError_t launch_q4_gemv(const void* X, bool bf16, int M, int K, int N,
                           const uint8_t* blob, const Q4Layout& L, const GemvPlan& P,
                           void* Y, hipStream_t st);
 
+// size of the library's static device scratch (q4_gemm_no_alloc), and its
+// address on the current device (looked up on the first call per device)
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void** ptr);
+
 // ws: the plan's workspace (gemm_workspace_bytes), or null when p.splits == 1
 hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const uint8_t* blob, const Q4Layout& L,
                           const GemmPlan& p, void* Y, float* ws, hipStream_t st);

@@ -34,7 +34,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = ql.lib()
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
     assert L.ql_abi_version() == ql.ABI_VERSION
@@ -403,3 +403,20 @@ def test_read_probe_validation():
     assert L.ql_read_probe(None, 1 << 20, P, 64, 0, None) == QL_ERR_NULL
     assert L.ql_read_probe(P, 1 << 20, None, 64, 1, None) == QL_ERR_NULL
     assert L.ql_read_probe(FAKE_MIS, 1 << 20, P, 64, 0, None) == QL_ERR_ALIGN
+
+
+def test_q4_gemm_no_alloc_validation():
+    """The allocation-free entry point checks like q4_gemm, and rejects a layer
+    whose plan needs more than the library's 32 MiB of static scratch, before
+    touching the device."""
+    L = ql.lib()
+    P = FAKE
+    assert L.q4_gemm_no_alloc(P, 0, 1, 200, 64, P, BIG, 128, P, None) == QL_ERR_SHAPE
+    assert L.q4_gemm_no_alloc(P, 7, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_DTYPE
+    assert L.q4_gemm_no_alloc(None, 0, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_NULL
+    assert L.q4_gemm_no_alloc(FAKE_MIS, 0, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_ALIGN
+    assert L.q4_gemm_no_alloc(None, 0, 0, 256, 64, None, BIG, 128, None, None) == QL_OK
+    M, K, N = 200, 16384, 12288
+    assert ql.q4_gemm_workspace_bytes(M, N, K) > 32 << 20
+    assert L.q4_gemm_no_alloc(P, 0, M, K, N, P, BIG, 128, P, None) == QL_ERR_SIZE
+    assert "static scratch" in last_error()
