@@ -335,15 +335,60 @@ def bench_mid_m(ql, reps):
         for M in w.Ms:
             X = wl.activations(w, M, K, N).cuda()
             Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
-            launchers = [ql.q4_gemm_launcher(X, blobs[r], N, Y) for r in range(R)]
+            need = ql.q4_gemm_workspace_bytes(M, N, K)
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+            launchers = [ql.q4_gemm_launcher(X, blobs[r], N, Y, workspace=ws) for r in range(R)]
             # one entry cycling over all copies (> the last-level cache) per timed block
             fn = lambda r, ls=launchers: ls[r % len(ls)]()
             (t,) = time_launches([fn], max(reps, R), torch.cuda.current_stream())
+            # the case's own roofline: the larger of the HBM time of its bytes
+            # and the MFMA time of its products
+            t_hbm = w4a16_bytes(M, K, N) / (HBM_PEAK_GBS * 1e9)
+            t_mfma = 2.0 * M * N * K / MFMA_PEAK["f16"]
+            rows, cols, splits = ql.q4_gemm_plan(M, N, K)
             per_case[f"{M}x{K}x{N}"] = {"us": round(t * 1e3, 2),
                                         "TFLOPS": round(2.0 * M * N * K / (t * 1e-3) / 1e12, 1),
-                                        "GBps": round(w4a16_bytes(M, K, N) / (t * 1e-3) / 1e9, 1)}
+                                        "GBps": round(w4a16_bytes(M, K, N) / (t * 1e-3) / 1e9, 1),
+                                        "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                                        "frac_roofline": round(max(t_hbm, t_mfma) / (t * 1e-3), 4),
+                                        "tile": f"{rows}x{cols}", "k_splits": splits}
         del blobs
     return {"workload": w.name, "per_case": per_case}
+
+
+def bench_library_refs(reps):
+    """The vendor libraries on the same shapes, as context for the GEMM
+    figures (not part of the layer): hipBLASLt's bare int8 product through
+    torch._int_mm, its FP8 E4M3 product with one scale per tensor through
+    torch._scaled_mm, and the dense bf16 product of the W4A16 prefill shape
+    through torch.matmul, all on random data, timed like the extra workloads."""
+    st = torch.cuda.current_stream()
+    out = {}
+    M, N, K = 2048, 4096, 4096
+    A = torch.randint(-128, 127, (M, K), dtype=torch.int8, device="cuda")
+    B = torch.randint(-127, 127, (N, K), dtype=torch.int8, device="cuda")
+    Bt = B.t()
+    (t,) = time_launches([lambda r: torch._int_mm(A, Bt)], reps, st)
+    out["int8_int_mm_2048x4096x4096"] = {"us": round(t * 1e3, 2), "TOPS": round(2 * M * N * K / (t * 1e-3) / 1e12, 1)}
+    try:
+        a = (torch.randn(M, K, device="cuda") * 0.5).to(torch.float8_e4m3fn)
+        b = (torch.randn(N, K, device="cuda") * 0.5).to(torch.float8_e4m3fn)
+        one = torch.tensor(1.0, device="cuda")
+        (t,) = time_launches([lambda r: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.float16)],
+                             reps, st)
+        out["fp8_scaled_mm_per_tensor_2048x4096x4096"] = {"us": round(t * 1e3, 2),
+                                                          "TFLOPS": round(2 * M * N * K / (t * 1e-3) / 1e12, 1)}
+    except Exception as e:                    # an FP8 path this torch build does not offer
+        out["fp8_scaled_mm_per_tensor_2048x4096x4096"] = {"unavailable": str(e)[:120]}
+    Mx, Kx, Nx = 4096, 4096, 14336
+    X = torch.randn(Mx, Kx, device="cuda", dtype=torch.bfloat16)
+    W = torch.randn(Nx, Kx, device="cuda", dtype=torch.bfloat16) * 0.02
+    Wt = W.t()
+    (t,) = time_launches([lambda r: torch.matmul(X, Wt)], max(10, reps // 3), st)
+    out["bf16_dense_matmul_4096x4096x14336"] = {"us": round(t * 1e3, 1),
+                                               "TFLOPS": round(2 * Mx * Nx * Kx / (t * 1e-3) / 1e12, 1),
+                                               "frac_mfma_bf16": round(2 * Mx * Nx * Kx / (t * 1e-3) / MFMA_PEAK["bf16"], 4)}
+    return out
 
 
 def _cpu_model():
@@ -427,6 +472,9 @@ def main():
                     help="back-to-back launches of a kernel before its timed block in the per-kernel figures")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for byte counters)")
+    ap.add_argument("--also-only", default="", metavar="NAMES",
+                    help="run only these extra workloads (comma-separated: decode_7b, w8a8, fp8, prefill, mid_m, "
+                         "libref)")
     args = ap.parse_args()
     WARM_MS = args.warm_ms
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -447,22 +495,31 @@ def main():
         print(f"# decode_70b read ceiling: {main_res['read_ceiling_step']}", flush=True)
         print(f"# decode_70b per case: {main_res['per_case']}", flush=True)
     also = {}
+    want = set(filter(None, args.also_only.split(","))) or {"decode_7b", "w8a8", "fp8", "prefill", "mid_m", "libref"}
     if not args.no_also:
-        r7 = bench_decode(ql, "decode_7b", args.steps, args.warmup)
-        also["decode_7b"] = {"workload": wl.WORKLOADS["decode_7b"].name, "step_GBps": round(r7["value_gbs"], 1),
-                             "ms_step": round(r7["ms_step"], 5),
-                             "frac_hbm": round(r7["value_gbs"] / HBM_PEAK_GBS, 4),
-                             "read_ceiling_step": r7["read_ceiling_step"], "per_case": r7["per_case"]}
-        print(f"# decode_7b: {r7['value_gbs']:.1f} GB/s per step", flush=True)
-        del r7
-        also["w8a8_prefill"] = bench_w8a8(ql, 50)
-        print(f"# w8a8: {also['w8a8_prefill']}", flush=True)
-        also["w8a8_fp8_prefill"] = bench_f8(ql, 50)
-        print(f"# w8a8 fp8: {also['w8a8_fp8_prefill']}", flush=True)
-        also["w4a16_prefill"] = bench_w4_prefill(ql, 20)
-        print(f"# w4a16 prefill: {also['w4a16_prefill']}", flush=True)
-        also["w4a16_mid_m"] = bench_mid_m(ql, 20)
-        print(f"# w4a16 mid-M: {also['w4a16_mid_m']}", flush=True)
+        if "decode_7b" in want:
+            r7 = bench_decode(ql, "decode_7b", args.steps, args.warmup)
+            also["decode_7b"] = {"workload": wl.WORKLOADS["decode_7b"].name, "step_GBps": round(r7["value_gbs"], 1),
+                                 "ms_step": round(r7["ms_step"], 5),
+                                 "frac_hbm": round(r7["value_gbs"] / HBM_PEAK_GBS, 4),
+                                 "read_ceiling_step": r7["read_ceiling_step"], "per_case": r7["per_case"]}
+            print(f"# decode_7b: {r7['value_gbs']:.1f} GB/s per step", flush=True)
+            del r7
+        if "w8a8" in want:
+            also["w8a8_prefill"] = bench_w8a8(ql, 50)
+            print(f"# w8a8: {also['w8a8_prefill']}", flush=True)
+        if "fp8" in want:
+            also["w8a8_fp8_prefill"] = bench_f8(ql, 50)
+            print(f"# w8a8 fp8: {also['w8a8_fp8_prefill']}", flush=True)
+        if "prefill" in want:
+            also["w4a16_prefill"] = bench_w4_prefill(ql, 20)
+            print(f"# w4a16 prefill: {also['w4a16_prefill']}", flush=True)
+        if "mid_m" in want:
+            also["w4a16_mid_m"] = bench_mid_m(ql, 20)
+            print(f"# w4a16 mid-M: {also['w4a16_mid_m']}", flush=True)
+        if "libref" in want:
+            also["library_refs"] = bench_library_refs(50)
+            print(f"# library references: {also['library_refs']}", flush=True)
 
     cpu = None if args.no_cpu else cpu_baseline()
     # the step is nothing but the decode kernel's launches: its mean launch

@@ -18,11 +18,15 @@ Readings where the pages are silent (each listed in the design notes):
     fp32 constant;
   * y is not rounded to the 16-bit activation type before it is quantized
     (the fused step has no intermediate tensor);
-  * precision: the mean square is the fp64 sum of the (exact) squares divided
-    by K in fp64 and rounded once to fp32; everything after it is IEEE fp32 in
-    this order: v = ms + eps, r = sqrt(v), inv = 1 / r, y = (x * inv) * gamma.
-    Both sides take every step that decides a code in the same precision,
-    so codes, scales and zero points are compared bit for bit.
+  * precision: the mean square is the correctly rounded fp64 sum of the
+    (exact) squares, divided by K in fp64 and rounded once to fp32;
+    everything after it is IEEE fp32 in this order: v = ms + eps,
+    r = sqrt(v), inv = 1 / r, y = (x * inv) * gamma.  Both sides take every
+    step that decides a code in the same precision, so codes, scales and zero
+    points are compared bit for bit.  "Correctly rounded" makes the sum
+    independent of the order of the additions: a plain fp64 sum is not, and
+    for a row whose mean square sits next to an fp32 rounding boundary two
+    orders can give two different fp32 mean squares.
 
 rms_norm64 is the plain definition in fp64, for the pins.
 """
@@ -44,8 +48,8 @@ def rms_norm64(X, gamma, eps):
 
 def mean_square_f32(X):
     """Per row: fp32(fp64(sum_k x^2) / K), the sum taken with math.fsum over
-    the squares (exact in fp64 for 16-bit inputs), so it is the correctly
-    rounded fp64 value of the exact sum."""
+    the squares (each exact in fp64 for 16-bit inputs), so it is the
+    correctly rounded fp64 value of the exact sum."""
     X = np.asarray(X, np.float64)
     K = X.shape[1]
     with np.errstate(over="ignore"):         # a mean square beyond the fp32 range becomes inf

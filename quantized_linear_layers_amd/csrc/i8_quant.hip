@@ -95,25 +95,46 @@ __device__ inline void piece_values(uint4 p, uint4 g, float inv, float (&y)[8]) 
   }
 }
 
-// MODE 0: int8 (ASYM selects the zero point); MODE 1: FP8 E4M3 (symmetric,
-// s = max(absmax, 1e-5) / 448, code = E4M3 rounding of x / s).  NORM: the
-// row is first normalized as y = (x * inv) * gamma with
-// inv = 1 / sqrt(fp32(sum of x^2 in fp64 / K) + eps)  ([QK] §9.9: the per-row
-// reduction of the activation quantization fused into the operator that
-// produces the activations; [LQ] "QuaRot：把整个残差流旋转掉" for the form
-// of RMSNorm).
-// Sums of one value per thread over the workgroup: wave shuffles, then the
+// The sum of squares is kept as an unevaluated pair hi + lo of doubles: each
+// addition is done with an error-free transformation (TwoSum: s + e equals
+// a + b exactly, s the rounded sum), the errors are gathered in lo, and
+// hi + lo is rounded once at the end.  The result is as accurate as a sum in
+// twice the fp64 precision rounded once: the correctly rounded fp64 sum,
+// whatever the order of the additions, unless the exact sum lies within
+// about n^2 * 2^-106 (relative; 2^-82 for n = 4096) of an fp64 rounding
+// boundary.  A plain fp64 sum depends on the order: a row whose mean square
+// sits next to an fp32 rounding boundary could round either way.
+struct DD {
+  double hi, lo;
+};
+__device__ inline DD two_sum(double a, double b) {
+  const double s = a + b;
+  const double bp = s - a;
+  return DD{s, (a - (s - bp)) + (b - bp)};
+}
+__device__ inline DD dd_add(DD a, double v) {
+  const DD t = two_sum(a.hi, v);
+  return DD{t.hi, a.lo + t.lo};
+}
+__device__ inline DD dd_add(DD a, DD b) {
+  const DD t = two_sum(a.hi, b.hi);
+  return DD{t.hi, (a.lo + b.lo) + t.lo};
+}
+// Sum over the workgroup of one pair per thread: wave shuffles, then the
 // wave totals through LDS, added in wave order, so every thread gets the same
-// result.
-__device__ inline double block_sum(double v, double* red) {
+// result; returns hi + lo rounded once.
+__device__ inline double block_sum(DD v, double* red) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  for (int o = 32; o > 0; o >>= 1) v = dd_add(v, DD{__shfl_xor(v.hi, o), __shfl_xor(v.lo, o)});
+  if ((threadIdx.x & 63) == 0) {
+    red[2 * (threadIdx.x >> 6)] = v.hi;
+    red[2 * (threadIdx.x >> 6) + 1] = v.lo;
+  }
   __syncthreads();
-  double t = red[0];
+  DD t{red[0], red[1]};
 #pragma unroll
-  for (int w = 1; w < kRowWaves; ++w) t += red[w];
-  return t;
+  for (int w = 1; w < kRowWaves; ++w) t = dd_add(t, DD{red[2 * w], red[2 * w + 1]});
+  return t.hi + t.lo;
 }
 template <bool ASYM>
 __device__ inline void block_range(float& mn, float& mx, float* red) {
@@ -137,17 +158,17 @@ __device__ inline void block_range(float& mn, float& mx, float* red) {
 // MODE 0: int8 (ASYM selects the zero point); MODE 1: FP8 E4M3 (symmetric,
 // s = max(absmax, 1e-5) / 448, code = E4M3 rounding of x / s).  NORM: the
 // row is first normalized as y = (x * inv) * gamma with
-// inv = 1 / sqrt(fp32(sum of x^2 in fp64 / K) + eps)  ([QK] §9.9: the per-row
-// reduction of the activation quantization fused into the operator that
-// produces the activations; [LQ] "QuaRot：把整个残差流旋转掉" for the form
-// of RMSNorm).  One workgroup per row.
+// inv = 1 / sqrt(fp32(S / K) + eps), S the correctly rounded fp64 sum of the
+// squares ([QK] §9.9: the per-row reduction of the activation quantization
+// fused into the operator that produces the activations; [LQ]
+// "QuaRot：把整个残差流旋转掉" for the form of RMSNorm).  One workgroup per row.
 template <bool BF16, bool ASYM, int MODE, bool NORM>
 __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(const uint16_t* __restrict__ X,
                                                                  const uint16_t* __restrict__ gamma, float eps,
                                                                  int M, int K, int8_t* __restrict__ Aq,
                                                                  float* __restrict__ s_a,
                                                                  int32_t* __restrict__ azp) {
-  __shared__ double red_ss[kRowWaves];
+  __shared__ double red_ss[2 * kRowWaves];
   __shared__ float red_range[2 * kRowWaves];
   const int tid = threadIdx.x;
   const int m = blockIdx.x;
@@ -178,21 +199,22 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(const uint16_t*
   }
   constexpr int kHeld = kRowThreads * kLanePieces;           // pieces held in registers
 
-  // ---- RMSNorm: mean square from the fp64 sum of the exact squares
+  // ---- RMSNorm: mean square from the correctly rounded fp64 sum of the
+  // exact squares (each square of a 16-bit value is exact in fp64)
   float inv = 1.0f;
   if constexpr (NORM) {
-    double ss = 0.0;
+    DD acc{0.0, 0.0};
 #pragma unroll
     for (int r = 0; r < kLanePieces; ++r)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss += (double)y[r][i] * (double)y[r][i];
+      for (int i = 0; i < 8; ++i) acc = dd_add(acc, (double)y[r][i] * (double)y[r][i]);
     for (int p = tid + kHeld; p < pieces; p += kRowThreads) {
       float t[8];
       piece_values<BF16, false>(xv[p], xv[p], 1.0f, t);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss += (double)t[i] * (double)t[i];
+      for (int i = 0; i < 8; ++i) acc = dd_add(acc, (double)t[i] * (double)t[i]);
     }
-    ss = block_sum(ss, red_ss);
+    const double ss = block_sum(acc, red_ss);
     const float ms = (float)(ss / (double)K);
     inv = 1.0f / sqrtf(ms + eps);
 #pragma unroll

@@ -1,12 +1,13 @@
 """Fused RMSNorm + per-token int8 quantization on the GPU against the oracle.
 
 Bar: codes, zero points and fp32 scales bit-exact.  Both sides take every
-step that decides a code in the same precision (the mean square as the fp64
-sum of exact squares rounded once to fp32, then IEEE fp32 steps in a fixed
-order).  The device's fp64 sum is a tree sum and the oracle's a correctly
-rounded one; they can round to different fp32 mean squares only when the
-exact mean square lies within about K * 2**-53 (relative) of an fp32
-rounding boundary, which none of the seeded rows here does.
+step that decides a code in the same precision (the mean square as the
+correctly rounded fp64 sum of the exact squares, rounded once to fp32, then
+IEEE fp32 steps in a fixed order).  The device sums with an error-free
+transformation (a double-fp64 running sum), which gives the correctly rounded
+sum in any order unless the exact sum lies within about n^2 * 2^-106 of an
+fp64 rounding boundary; the rows built to sit on and next to an fp32 boundary
+of the mean square (tests/rmsnorm_rows.py) check exactly that case.
 """
 
 import numpy as np
@@ -105,6 +106,23 @@ def test_edge_rows(dtype):
     for eps in (1e-6, 1.0):
         check(X, gamma, eps)
         check(X, gamma, eps, symmetric=True)
+
+
+@pytest.mark.parametrize("row", ["tie", "straddle_first", "straddle_second"])
+def test_mean_square_at_an_fp32_boundary(row):
+    """Rows whose mean square is an fp32 midpoint (ties to even) or lies just
+    above one by less than the fp64 rounding of the sum (rounds up): the tiny
+    squares sit in the first 8-value piece of 96 threads' rows, or in their
+    second piece after a first piece of large values."""
+    from tests import rmsnorm_rows as rr
+    x = {"tie": lambda: rr.tie_row()[0],
+         "straddle_first": lambda: rr.straddle_row()[0],
+         "straddle_second": lambda: rr.straddle_row(tiny_start=2048, big_from=0)[0]}[row]()
+    X = torch.from_numpy(np.stack([x, x[::-1].copy()]).astype(np.float32)).to(torch.float16)
+    assert np.array_equal(wl.as_f64(X)[0], x)               # the row is exact in fp16
+    gamma = torch.ones(rr.K, dtype=torch.float16)
+    check(X, gamma, 1e-6)
+    check(X, gamma, 1e-6, symmetric=True)
 
 
 def test_gamma_signs_and_zeros():

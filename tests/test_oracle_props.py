@@ -472,3 +472,37 @@ def test_act_order_brute_force_tiny():
     # a wrong channel-to-group map changes the result
     g_bad = np.roll(g, 1)
     assert abs(w4.w4a16_linear_gidx(x[None], q, s, z, g_bad)[0, 0] - want) > 1e-6
+
+
+def test_rmsnorm_mean_square_on_and_next_to_an_fp32_boundary():
+    """The mean-square reading (the correctly rounded fp64 sum of the exact
+    squares, then fp32) on rows built with exact integers: a row whose mean
+    square IS an fp32 midpoint rounds to the even neighbour; a row whose exact
+    mean square lies just above the midpoint rounds up, although a plain fp64
+    sum that adds the tiny squares last lands on the midpoint and rounds down
+    (the order dependence the correctly rounded reading removes)."""
+    from fractions import Fraction
+    from oracle import rmsnorm as rn
+    from tests import rmsnorm_rows as rr
+    def neighbours(mid):
+        f = np.float32(mid)
+        below = f if float(f) < mid else np.nextafter(f, np.float32(0))
+        up = np.nextafter(below, np.float32(8))
+        assert float(below) < mid < float(up) and float(up) - mid == mid - float(below)
+        assert int(below.view(np.uint32)) % 2 == 0               # the lower neighbour is the even one
+        return below, up
+
+    x, mid = rr.tie_row()
+    assert sum(Fraction(v) ** 2 for v in x.tolist()) / rr.K == Fraction(mid)
+    below, _ = neighbours(mid)
+    assert rn.mean_square_f32(x[None, :])[0] == below
+    for kw in ({}, {"tiny_start": 2048, "big_from": 0}):
+        x, mid = rr.straddle_row(**kw)
+        below, up = neighbours(mid)
+        exact = sum(Fraction(v) ** 2 for v in x.tolist()) / rr.K
+        assert exact > Fraction(mid) and float(exact - Fraction(mid)) < 1e-14
+        assert rn.mean_square_f32(x[None, :])[0] == up
+        seq = 0.0
+        for v in np.concatenate([x[x != rr.TINY], x[x == rr.TINY]]):
+            seq += v * v
+        assert np.float32(seq / rr.K) == below
