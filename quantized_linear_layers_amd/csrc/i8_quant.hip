@@ -95,10 +95,11 @@ __device__ inline void piece_values(uint4 p, uint4 g, float inv, float (&y)[8]) 
   }
 }
 
-// The sum of squares is kept as an unevaluated pair hi + lo of doubles: each
-// addition is done with an error-free transformation (TwoSum: s + e equals
-// a + b exactly, s the rounded sum), the errors are gathered in lo, and
-// hi + lo is rounded once at the end.  The result is as accurate as a sum in
+// The exact path of the sum of squares (rows whose mean square sits next to
+// an fp32 rounding boundary) keeps an unevaluated pair hi + lo of doubles:
+// each addition is done with an error-free transformation (TwoSum: s + e
+// equals a + b exactly, s the rounded sum), the errors are gathered in lo,
+// and hi + lo is rounded once at the end.  The result is as accurate as a sum in
 // twice the fp64 precision rounded once: the correctly rounded fp64 sum,
 // whatever the order of the additions, unless the exact sum lies within
 // about n^2 * 2^-106 (relative; 2^-82 for n = 4096) of an fp64 rounding
@@ -136,6 +137,36 @@ __device__ inline double block_sum(DD v, double* red) {
   for (int w = 1; w < kRowWaves; ++w) t = dd_add(t, DD{red[2 * w], red[2 * w + 1]});
   return t.hi + t.lo;
 }
+// The exact sum of the squares of a row (TwoSum), re-read from memory, two
+// values at a time (few registers: the rare exact path must not lower the
+// occupancy of the fast one).
+template <bool BF16>
+__device__ inline double exact_sum_of_squares(const uint4* __restrict__ xv, int pieces, double* red) {
+  DD dd{0.0, 0.0};
+  for (int p = threadIdx.x; p < pieces; p += kRowThreads) {
+    const uint4 v = xv[p];
+#pragma unroll 1
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t word = w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+      const double a = half_lo(word, BF16), b = half_hi(word, BF16);
+      dd = dd_add(dd, a * a);
+      dd = dd_add(dd, b * b);
+    }
+  }
+  return block_sum(dd, red);
+}
+
+// The same sum of one plain double per thread (the fast path).
+__device__ inline double block_sum_plain(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowWaves; ++w) t += red[w];
+  return t;
+}
 template <bool ASYM>
 __device__ inline void block_range(float& mn, float& mx, float* red) {
 #pragma unroll
@@ -163,7 +194,7 @@ __device__ inline void block_range(float& mn, float& mx, float* red) {
 // fused into the operator that produces the activations; [LQ]
 // "QuaRot：把整个残差流旋转掉" for the form of RMSNorm).  One workgroup per row.
 template <bool BF16, bool ASYM, int MODE, bool NORM>
-__global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8))) void quant_rows_kernel(const uint16_t* __restrict__ X,
                                                                  const uint16_t* __restrict__ gamma, float eps,
                                                                  int M, int K, int8_t* __restrict__ Aq,
                                                                  float* __restrict__ s_a,
@@ -200,21 +231,33 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(const uint16_t*
   constexpr int kHeld = kRowThreads * kLanePieces;           // pieces held in registers
 
   // ---- RMSNorm: mean square from the correctly rounded fp64 sum of the
-  // exact squares (each square of a 16-bit value is exact in fp64)
+  // exact squares (each square of a 16-bit value is exact in fp64).  A plain
+  // fp64 sum of K nonnegative terms, in any order, lies within
+  // (K - 1) * 2^-53 (relative, to first order) of the exact sum; when the
+  // fp32 mean square is the same at both ends of that interval it is the one
+  // the correctly rounded sum gives (division and rounding are monotone), and
+  // only otherwise (a mean square next to an fp32 rounding boundary: about
+  // K * 2^-29 of the rows) is the sum redone exactly with TwoSum.  The branch
+  // depends only on the workgroup-wide sum, so the whole workgroup takes it.
   float inv = 1.0f;
   if constexpr (NORM) {
-    DD acc{0.0, 0.0};
+    double acc = 0.0;
 #pragma unroll
     for (int r = 0; r < kLanePieces; ++r)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = dd_add(acc, (double)y[r][i] * (double)y[r][i]);
+      for (int i = 0; i < 8; ++i) acc += (double)y[r][i] * (double)y[r][i];
     for (int p = tid + kHeld; p < pieces; p += kRowThreads) {
       float t[8];
       piece_values<BF16, false>(xv[p], xv[p], 1.0f, t);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = dd_add(acc, (double)t[i] * (double)t[i]);
+      for (int i = 0; i < 8; ++i) acc += (double)t[i] * (double)t[i];
     }
-    const double ss = block_sum(acc, red_ss);
+    double ss = block_sum_plain(acc, red_ss);
+    const double err = ss * ((double)K * 0x1p-53 * 1.001);
+    if (__builtin_expect((float)((ss - err) / (double)K) != (float)((ss + err) / (double)K), 0)) {
+      __syncthreads();                           // every thread has read red_ss
+      ss = exact_sum_of_squares<BF16>(xv, pieces, red_ss);
+    }
     const float ms = (float)(ss / (double)K);
     inv = 1.0f / sqrtf(ms + eps);
 #pragma unroll
