@@ -362,9 +362,19 @@ def bench_library_refs(reps):
     figures (not part of the layer): hipBLASLt's bare int8 product through
     torch._int_mm, its FP8 E4M3 product with one scale per tensor through
     torch._scaled_mm, and the dense bf16 product of the W4A16 prefill shape
-    through torch.matmul, all on random data, timed like the extra workloads."""
+    through torch.matmul, all on random data, timed like the extra workloads.
+    Beside the per-token quant kernel: torch's elementwise kernel with the
+    same traffic per value (reads 2 bytes, writes 1: x != 0 into a bool
+    tensor) on the W8A8 activation shape, with no reduction in between."""
     st = torch.cuda.current_stream()
     out = {}
+    Mq, Kq = 2048, 4096
+    Xq = _activation_copies(torch.randn(Mq, Kq, device="cuda", dtype=torch.bfloat16))
+    Bq = torch.empty(Mq, Kq, device="cuda", dtype=torch.bool)
+    (t,) = time_launches([lambda r: torch.ne(Xq[r % len(Xq)], 0, out=Bq)], reps, st)
+    out["elementwise_bf16_to_bool_2048x4096"] = {"us": round(t * 1e3, 2),
+                                                 "GBps": round(3 * Mq * Kq / (t * 1e-3) / 1e9, 1)}
+    del Xq, Bq
     M, N, K = 2048, 4096, 4096
     A = torch.randint(-128, 127, (M, K), dtype=torch.int8, device="cuda")
     B = torch.randint(-127, 127, (N, K), dtype=torch.int8, device="cuda")

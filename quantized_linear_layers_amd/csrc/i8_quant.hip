@@ -35,6 +35,7 @@ namespace {
 constexpr int kRowWaves = 4;                    // waves per row (one workgroup per row)
 constexpr int kRowThreads = 64 * kRowWaves;
 constexpr int kLanePieces = 2;                  // 8-value pieces per thread held in registers (K <= 4096)
+constexpr float kCodeBias = 0x1.8p23f;          // integers of magnitude < 2^22 plus this keep their low bits
 
 __device__ inline float half_lo(uint32_t v, bool bf16) {
   return bf16 ? __builtin_bit_cast(float, v << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
@@ -56,7 +57,7 @@ __device__ inline float half_hi(uint32_t v, bool bf16) {
 //         fp32 significand rounded at bit 20 (ties to even), which stays at
 //         or below the largest code 0x7E.
 template <int MODE>
-__device__ inline uint32_t code_fast(float t, float z, float lo, bool& near) {
+__device__ inline uint32_t code_fast(float t, float zm, float lom, bool& near) {
   if constexpr (MODE == 1) {
     const uint32_t b = __builtin_bit_cast(uint32_t, t);
     const uint32_t a = b & 0x7FFFFFFFu;
@@ -65,9 +66,12 @@ __device__ inline uint32_t code_fast(float t, float z, float lo, bool& near) {
     const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
     return ((b >> 24) & 0x80u) | (((r >> 20) - (120u << 3)) & 0x7Fu);   // garbage below 2^-6 stays in its byte
   } else {
+    // zm = z + 1.5 * 2^23 and lom = lo + 1.5 * 2^23: the clamped rint(t) + z
+    // plus 1.5 * 2^23 is an integer in [2^23, 2^24), exact in fp32, whose low
+    // byte is the two's-complement code
     const float c = rintf(t);
     near = fabsf(t - c) >= 0.5f - fabsf(t) * 0x1p-21f;
-    return (uint32_t)(int32_t)__builtin_amdgcn_fmed3f(c + z, lo, 127.0f) & 0xFFu;
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(c + zm, lom, kCodeBias + 127.0f));
   }
 }
 
@@ -308,14 +312,20 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8))
   const float rs = 1.0f / s;
   const float lo = ASYM ? -128.0f : -127.0f;
 
+  const float zm = z + kCodeBias, lom = lo + kCodeBias;
+
+  // codes of 8 values, packed in order; the low byte of each code_fast /
+  // code_exact result is the code
   auto quant = [&](const float (&t)[8]) -> uint2 {
-    uint32_t out[2] = {0, 0}, fix = 0;
+    uint32_t c[8], fix = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       bool near;
-      out[i >> 2] |= code_fast<MODE>(t[i] * rs, z, lo, near) << (8 * (i & 3));
+      c[i] = code_fast<MODE>(t[i] * rs, zm, lom, near);
       fix |= (uint32_t)near << i;
     }
+    uint2 out = make_uint2(__builtin_amdgcn_perm(c[1], c[0], 0x0C0C0400u) | __builtin_amdgcn_perm(c[3], c[2], 0x04000C0Cu),
+                           __builtin_amdgcn_perm(c[5], c[4], 0x0C0C0400u) | __builtin_amdgcn_perm(c[7], c[6], 0x04000C0Cu));
     // the rare values next to a rounding boundary: exact division, one at a
     // time, outside the unrolled fast path
 #pragma nounroll
@@ -324,13 +334,13 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8))
       float yi = t[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) yi = i == j ? t[j] : yi;
-      const uint32_t sh = 8 * (i & 3), c = code_exact<MODE>(yi, s, z, lo) << sh, keep = ~(0xFFu << sh);
+      const uint32_t sh = 8 * (i & 3), v = (code_exact<MODE>(yi, s, z, lo) & 0xFFu) << sh, keep = ~(0xFFu << sh);
       if (i < 4)
-        out[0] = (out[0] & keep) | c;
+        out.x = (out.x & keep) | v;
       else
-        out[1] = (out[1] & keep) | c;
+        out.y = (out.y & keep) | v;
     }
-    return make_uint2(out[0], out[1]);
+    return out;
   };
   uint2* qo = reinterpret_cast<uint2*>(Aq + (size_t)m * K);
 #pragma unroll
