@@ -327,12 +327,18 @@ def bench_w4_prefill(ql, reps):
 def bench_mid_m(ql, reps):
     """W4A16 with 32 .. 256 tokens (the large-M kernel's small tiles), each
     (M, K, N) case timed on its own, weights rotated over copies larger than
-    the last-level cache."""
+    the last-level cache.  Beside each case: the plain read of the layer's
+    weight bytes (read_us) and the case's time against it (frac_of_read)."""
     w = wl.WORKLOADS["mid_m_7b"]
     per_case = {}
+    st = torch.cuda.current_stream()
     for (K, N) in w.shapes:
         R = _copies_for(ql.q4_packed_bytes(N, K))
         _, blobs = _prepare_w4(ql, w, K, N, R)
+        # the plain read of the same weight copies (fastest probe configuration):
+        # no kernel that reads these bytes once can take less time
+        probes = {p: [ql.read_probe_launcher(b, p[1], p[0]) for b in blobs] for p in READ_PROBES}
+        read_ms = min(time_launches([lambda i, f=f: f[i % R]()], max(reps, 2 * R), st)[0] for f in probes.values())
         for M in w.Ms:
             X = wl.activations(w, M, K, N).cuda()
             Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
@@ -352,6 +358,8 @@ def bench_mid_m(ql, reps):
                                         "GBps": round(w4a16_bytes(M, K, N) / (t * 1e-3) / 1e9, 1),
                                         "bound": "hbm" if t_hbm >= t_mfma else "mfma",
                                         "frac_roofline": round(max(t_hbm, t_mfma) / (t * 1e-3), 4),
+                                        "read_us": round(read_ms * 1e3, 2),
+                                        "frac_of_read": round(read_ms / t, 4),
                                         "tile": f"{rows}x{cols}", "k_splits": splits}
         del blobs
     return {"workload": w.name, "per_case": per_case}
