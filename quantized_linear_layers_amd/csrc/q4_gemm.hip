@@ -630,14 +630,17 @@ hipError_t launch_reduce(const float* P, int S, size_t MN, uint16_t* Y, bool bf1
 
 }  // namespace
 
-// Workgroup tiles of the large-M kernel, largest first.  Every configuration
-// has 8 waves and about 126-130 KB of LDS stages, so one workgroup fills a
-// compute unit, and with few tokens its K loop runs at a near-constant time
-// per step (memory round trips, not arithmetic, set the pace).  step: that
-// time in us, measured on the Llama-2 7B / 70B layers.  The two non-square
-// tiles spend fewer LDS bytes per stage on activations (half the columns'
-// share of each stage instead of four fifths), so their rings hold five
-// stages.
+// Workgroup tiles of the large-M kernel.  Every configuration has 8 waves
+// and about 126-130 KB of LDS stages, so one workgroup fills a compute unit,
+// and with few tokens its K loop runs at a near-constant time per step
+// (memory round trips, not arithmetic, set the pace) until the copies of all
+// the running workgroups saturate (see plan_q4_gemm).  step: that time in us,
+// fitted on the Llama-2 7B / 70B layers.  The non-square tiles spend fewer
+// LDS bytes per stage on activations (64 x 128 and 32 x 64: half the columns'
+// share of each stage instead of four fifths, so their rings hold five
+// stages); the 128 x 256 tile (8 waves of 128 rows x 32 columns, also the
+// prefill's last-round tile) pays off on the wide layers from about 192
+// tokens; it is only planned for 129 to 512 tokens, where it was timed.
 struct TileOpt {
   int bm, bn, wk;
   double step;
@@ -645,37 +648,49 @@ struct TileOpt {
 constexpr TileOpt kTiles[] = {
     {256, 256, 1, 1.38},   // Cfg<8, 8, 1, 3>
     {128, 128, 2, 0.92},   // Cfg<4, 4, 2, 3>
-    {64, 128, 2, 0.72},    // Cfg<2, 4, 2, 5>
-    {64, 64, 4, 0.76},     // Cfg<2, 2, 4, 3>
+    {64, 128, 2, 0.67},    // Cfg<2, 4, 2, 5>
+    {64, 64, 4, 0.71},     // Cfg<2, 2, 4, 3>
     {32, 64, 4, 0.62},     // Cfg<1, 2, 4, 5>
     {32, 32, 8, 0.72},     // Cfg<1, 1, 8, 3>
+    {128, 256, 1, 0.80},   // Cfg<4, 8, 1, 3> (129 to 512 tokens only)
 };
 constexpr int kNumTiles = (int)(sizeof(kTiles) / sizeof(kTiles[0]));
 
 // Plan of the large-M kernel for an M x N x K product: the tile (index into
 // kTiles) and the number of splits of K across workgroups.  The estimate is
 // rounds x (ramp + K steps of a K-group x step time), with 256 workgroups a
-// round and a ramp of 2.5 us a round, plus, with a split, the reduce pass
-// (a launch of about 2 us and the partials written and read back at about
-// 4 TB/s).  Ties go to the earlier (larger) tile and to fewer splits.  A
-// split is only considered with at most 256 tokens (with more, the tiles
-// alone fill the compute units).
+// round and a ramp of 2.5 us a round.  A step takes the tile's own time or,
+// when longer, the time the workgroups of a round need to copy their step's
+// operands (per K-group, 128 bytes of activations per row and 32 bytes of
+// packed weights per column) into LDS at 13.2 TB/s in all.  With a split,
+// the reduce pass adds a launch of about 2.7 us and the partials written and
+// read back at about 3.3 TB/s.  Ties go to the earlier tile and to fewer
+// splits.  A split is only considered with at most 512 tokens (with more,
+// the tiles alone fill the compute units).  The constants are fitted to
+// every plan timed on the 7B and 70B layer shapes at 17 to 512 tokens
+// (weights from HBM): the chosen plans come within 0.7% of the fastest on
+// average and within 8.4% in the worst case (the previous constant-step
+// model: 3.0% and 21%).
 GemmPlan plan_q4_gemm(int M, int N, int K, int max_splits) {
   const long nkb = K / BK;
   GemmPlan best{0, 1, (int)nkb};
   double best_cost = 0.0;
   static const int kSplits[] = {1, 2, 3, 4, 6, 8};
+  constexpr double kRamp = 2.5, kCopyBytesPerUs = 13.2e6, kReduceUs = 2.7, kPartialBytesPerUs = 3.3e6;
   for (int t = 0; t < kNumTiles; ++t) {
     const TileOpt& o = kTiles[t];
+    if (o.bm == 128 && o.bn == 256 && (M <= 128 || M > 512)) continue;   // outside the range it was timed on
     const long tiles = (long)((M + o.bm - 1) / o.bm) * ((N + o.bn - 1) / o.bn);
     for (int S : kSplits) {
-      if (S > max_splits || (S > 1 && (M > 256 || t == 0))) continue;
+      if (S > max_splits || (S > 1 && (M > 512 || t == 0))) continue;
       const long kbs = (nkb + S - 1) / S;
       const long splits = (nkb + kbs - 1) / kbs;             // no empty split
       if (S > 1 && splits < 2) continue;
       const long wgs = tiles * splits;
-      double cost = (double)((wgs + 255) / 256) * (2.5 + (double)((kbs + o.wk - 1) / o.wk) * o.step);
-      if (splits > 1) cost += 2.0 + (double)(2 * splits * 4 + 2) * M * N / 4.0e6;
+      const double copy = (double)(wgs < 256 ? wgs : 256) * o.wk * (o.bm * 128 + o.bn * 32) / kCopyBytesPerUs;
+      const double step = o.step > copy ? o.step : copy;
+      double cost = (double)((wgs + 255) / 256) * (kRamp + (double)((kbs + o.wk - 1) / o.wk) * step);
+      if (splits > 1) cost += kReduceUs + (double)(2 * splits * 4 + 2) * M * N / kPartialBytesPerUs;
       if ((t == 0 && S == 1) || cost < best_cost) {
         best = GemmPlan{t, (int)splits, (int)kbs};
         best_cost = cost;
@@ -746,7 +761,8 @@ hipError_t launch_q4_gemm(const void* X, bool bf16, int M, int K, int N, const u
       case 2: e = launch_cfg<Cfg<2, 4, 2, 5>>(a, bf16, st, p.splits); break;
       case 3: e = launch_cfg<Cfg<2, 2, 4, 3>>(a, bf16, st, p.splits); break;
       case 4: e = launch_cfg<Cfg<1, 2, 4, 5>>(a, bf16, st, p.splits); break;
-      default: e = launch_cfg<Cfg<1, 1, 8, 3>>(a, bf16, st, p.splits); break;
+      case 5: e = launch_cfg<Cfg<1, 1, 8, 3>>(a, bf16, st, p.splits); break;
+      default: e = launch_cfg<Cfg<4, 8, 1, 3>>(a, bf16, st, p.splits); break;
     }
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_reduce(ws, p.splits, (size_t)M * N, a.Y, bf16, st);

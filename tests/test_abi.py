@@ -331,17 +331,22 @@ def test_launcher_rejects_host_tensors():
 
 def test_q4_gemm_tile_shape():
     """The tile diagnostic: the decode kernel for M <= 16, a square or one of
-    the two non-square tiles above, and the documented errors."""
+    the three non-square tiles above, and the documented errors."""
     assert ql.q4_gemm_tile_shape(16, 4096, 4096) == (0, 0)
     assert ql.q4_gemm_tile_shape(4096, 14336, 4096) == (256, 256)
     assert ql.q4_gemm_tile_shape(32, 11008, 4096, False) == (32, 64)
     assert ql.q4_gemm_tile_shape(128, 11008, 4096, False) == (64, 128)
     assert ql.q4_gemm_tile_shape(32, 4096, 4096, False) == (32, 32)
-    for M in (17, 64, 200, 1000):
-        for N in (72, 4096, 11008):
+    assert ql.q4_gemm_tile_shape(256, 28672, 8192, False) == (128, 256)
+    assert ql.q4_gemm_plan(256, 8192, 28672) == (128, 256, 4)
+    for M in (17, 64, 128, 200, 512, 513, 1000):
+        for N in (72, 4096, 11008, 28672):
             for ws in (False, True):
-                assert ql.q4_gemm_tile_shape(M, N, 4096, ws) in {(256, 256), (128, 128), (64, 128), (64, 64),
-                                                                (32, 64), (32, 32)}
+                t = ql.q4_gemm_tile_shape(M, N, 4096, ws)
+                assert t in {(256, 256), (128, 256), (128, 128), (64, 128), (64, 64), (32, 64), (32, 32)}
+                # the 128 x 256 tile only for 129 to 512 tokens, splits only up to 512
+                assert t != (128, 256) or 128 < M <= 512
+                assert M <= 512 or ql.q4_gemm_plan(M, N, 4096, ws)[2] == 1
             assert ql.q4_gemm_plan(M, N, 4096, False)[2] == 1
     L = ql.lib()
     r, c = C.c_int(), C.c_int()
@@ -359,12 +364,12 @@ def test_q4_gemm_workspace_plan():
     assert ql.q4_gemm_workspace_bytes(4096, 14336, 4096) == 0
     assert ql.q4_gemm_plan(4096, 14336, 4096)[2] == 1
     split_seen = False
-    for M in (17, 32, 64, 128, 256, 300):
+    for M in (17, 32, 64, 128, 256, 300, 512, 513, 1000):
         for (K, N) in ((4096, 4096), (4096, 11008), (11008, 4096), (28672, 8192)):
             rows, cols, S = ql.q4_gemm_plan(M, N, K)
             ws = ql.q4_gemm_workspace_bytes(M, N, K)
             assert ws == (S * M * N * 4 if S > 1 else 0)
-            assert S == 1 or M <= 256
+            assert S == 1 or M <= 512
             split_seen |= S > 1
     assert split_seen
     assert ql.q4_gemm_workspace_bytes(32, 4096, 100) == 0           # invalid K
@@ -416,7 +421,7 @@ def test_q4_gemm_no_alloc_validation():
     assert L.q4_gemm_no_alloc(None, 0, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_NULL
     assert L.q4_gemm_no_alloc(FAKE_MIS, 0, 1, 256, 64, P, BIG, 128, P, None) == QL_ERR_ALIGN
     assert L.q4_gemm_no_alloc(None, 0, 0, 256, 64, None, BIG, 128, None, None) == QL_OK
-    M, K, N = 200, 16384, 12288
+    M, K, N = 300, 16384, 12288
     assert ql.q4_gemm_workspace_bytes(M, N, K) > 32 << 20
     assert L.q4_gemm_no_alloc(P, 0, M, K, N, P, BIG, 128, P, None) == QL_ERR_SIZE
     assert "static scratch" in last_error()

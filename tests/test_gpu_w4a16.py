@@ -175,12 +175,30 @@ def test_nonsquare_tiles(M, K, N, dtype, tile):
     check(W, X, cols=cols)
 
 
+# shapes that select the 128 x 256 tile (8 waves of 128 rows x 32 columns,
+# planned for 129 to 512 tokens): with and without a K split, ragged M, N
+# and K, uneven splits; every column of the last column tile is checked
+@pytest.mark.parametrize("M,K,N,dtype,plan_ws,plan_nows", [
+    (300, 1152, 11000, torch.bfloat16, (128, 256, 1), (128, 256, 1)),
+    (130, 9088, 6000, torch.float16, (128, 256, 4), (32, 64, 1)),
+    (193, 9088, 16400, torch.bfloat16, (128, 256, 3), (128, 256, 1))])
+def test_tile_128x256(M, K, N, dtype, plan_ws, plan_nows):
+    assert ql.q4_gemm_plan(M, N, K) == plan_ws
+    assert ql.q4_gemm_plan(M, N, K, False) == plan_nows
+    r = np.random.default_rng(M * 3 + K + N)
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = torch.from_numpy(r.standard_normal((M, K)).astype(np.float32)).to(dtype)
+    cols = np.union1d(np.sort(r.choice(N, 384, replace=False)), np.arange(N - (N % 256 or 256), N))
+    check(W, X, cols=cols)
+    check(W, X, cols=cols, workspace=False)
+
+
 # shapes whose plan splits K across workgroups (fp32 partials in the
 # workspace, then the reduce pass): the 7B/70B mid-M layers the plan splits,
 # and ragged M, N and K with uneven splits and empty K-group runs; each also
 # runs without a workspace (the unsplit plan) and both are checked
 @pytest.mark.parametrize("M,K,N,dtype", [(32, 11008, 4096, torch.float16), (128, 11008, 4096, torch.float16),
-                                         (64, 28672, 8192, torch.bfloat16), (17, 4096, 4096, torch.bfloat16),
+                                         (64, 28672, 8192, torch.bfloat16), (17, 11008, 4096, torch.bfloat16),
                                          (40, 11008, 1000, torch.float16), (77, 5248, 700, torch.bfloat16),
                                          (100, 5248, 500, torch.float16), (130, 6016, 1000, torch.bfloat16),
                                          (130, 9088, 3000, torch.float16), (200, 9088, 2000, torch.bfloat16)])
