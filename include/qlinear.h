@@ -231,8 +231,8 @@ size_t q4_gemm_workspace_bytes(int M, int N, int K, int group);
  * q4_gemm_tile_shape — the plan q4_gemm uses for an M x N x K product, with
  * a workspace (with_workspace != 0) or without one (host; a diagnostic for
  * tests and tuning, no device work).
- * *rows, *cols: the workgroup tile (256 x 256 … 32 x 32, also 64 x 128 and
- * 32 x 64) for M > 16; 0, 0 for M <= 16 (the decode kernel).  *splits (if
+ * *rows, *cols: the workgroup tile (256 x 256 … 32 x 32, also 128 x 256,
+ * 64 x 128 and 32 x 64) for M > 16; 0, 0 for M <= 16 (the decode kernel).  *splits (if
  * splits != NULL): the number of K splits across workgroups (1 = none).
  * The choice depends on the shape only ([LQ] W4A16 section: the batch size
  * decides between the bandwidth- and compute-bound regimes).
