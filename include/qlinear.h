@@ -332,7 +332,8 @@ int i8_azp_adj(const int8_t* Bq, int N, int K, int32_t* azp_adj);
  * with any IEEE implementation of the same steps.
  *
  * X [M][K] fp16/bf16; Aq [M][K] int8 out; s_a [M] fp32 out; azp [M] int32
- * out or NULL.  M == 0 is a no-op.
+ * out or NULL.  M == 0 is a no-op.  A row holding a NaN gets an unspecified
+ * scale, zero point and codes.
  * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M >= 0, K > 0 and
  *         K % 8 == 0; QL_ERR_ALIGN; QL_ERR_HIP.
  */
@@ -357,7 +358,8 @@ int i8_quant_per_token(const void* X, int x_dtype, int M, int K,
  *
  * X [M][K] fp16/bf16; gamma [K] of the same dtype; eps > 0 and finite; Aq
  * [M][K] int8 out; s_a [M] fp32 out; azp [M] int32 out or NULL.  M == 0 is a
- * no-op.  Inputs are read once; nothing is allocated.
+ * no-op.  Inputs are read once; nothing is allocated.  A row whose
+ * normalized values hold a NaN gets an unspecified scale, zero point and codes.
  * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M >= 0, K > 0 and
  *         K % 8 == 0; QL_ERR_RANGE unless eps > 0 and finite; QL_ERR_ALIGN;
  *         QL_ERR_HIP.
@@ -428,7 +430,7 @@ int f8_quant_weight_host(const float* W, int N, int K, uint8_t* Bq, float* s_b);
  * (correctly rounded fp32 division, then one E4M3 rounding: bit-exact with
  * any IEEE implementation of the same steps).
  * X [M][K] fp16/bf16; Aq [M][K] E4M3 codes out; s_a [M] fp32 out.
- * M == 0 is a no-op.
+ * M == 0 is a no-op.  A row holding a NaN gets an unspecified scale and codes.
  * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M >= 0, K > 0 and
  *         K % 8 == 0; QL_ERR_ALIGN; QL_ERR_HIP.
  */

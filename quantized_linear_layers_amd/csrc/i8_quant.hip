@@ -160,10 +160,45 @@ __device__ inline double exact_sum_of_squares(const uint4* __restrict__ xv, int 
   return block_sum(dd, red);
 }
 
+// Cross-lane steps inside rows of 16 lanes as DPP operands (no LDS traffic,
+// no lane-index arithmetic): a butterfly over the quad (lane ^ 1, lane ^ 2),
+// then two rotations of the row by 4 and 8 lanes, after which every lane
+// holds its row's total; the four row totals are then read as scalars.
+constexpr int kDppQuad1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuad2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRor4 = 0x124;     // row_ror:4
+constexpr int kDppRor8 = 0x128;     // row_ror:8
+template <int CTRL>
+__device__ inline int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ inline double dpp(double v) {
+  const int lo = dpp<CTRL>(__double2loint(v)), hi = dpp<CTRL>(__double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
+// the row totals of lanes 0, 16, 32, 48 combined by op (wave-uniform result)
+template <typename T, typename Op>
+__device__ inline T wave_reduce(T v, Op op) {
+  v = op(v, dpp<kDppQuad1>(v));
+  v = op(v, dpp<kDppQuad2>(v));
+  v = op(v, dpp<kDppRor4>(v));
+  v = op(v, dpp<kDppRor8>(v));
+  T r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(T) == 8)
+      r[i] = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 16 * i),
+                              __builtin_amdgcn_readlane(__double2loint(v), 16 * i));
+    else
+      r[i] = __builtin_amdgcn_readlane(v, 16 * i);
+  }
+  return op(op(r[0], r[1]), op(r[2], r[3]));
+}
+
 // The same sum of one plain double per thread (the fast path).
 __device__ inline double block_sum_plain(double v, double* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v = wave_reduce(v, [](double x, double y) { return x + y; });
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   double t = red[0];
@@ -171,23 +206,32 @@ __device__ inline double block_sum_plain(double v, double* red) {
   for (int w = 1; w < kRowWaves; ++w) t += red[w];
   return t;
 }
+
+// A finite or infinite fp32 value as an int that orders like it (-0 below
+// +0), so the range is reduced with integer min / max; the map is its own
+// inverse.  (A NaN in a row gives that row an unspecified range.)
+__device__ inline int order_key(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ inline float from_key(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
 template <bool ASYM>
-__device__ inline void block_range(float& mn, float& mx, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    if constexpr (ASYM) mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
+__device__ inline void block_range(float& mn, float& mx, int* red) {
+  int kmn = 0, kmx = wave_reduce(order_key(mx), [](int x, int y) { return x > y ? x : y; });
+  if constexpr (ASYM) kmn = wave_reduce(order_key(mn), [](int x, int y) { return x < y ? x : y; });
   if ((threadIdx.x & 63) == 0) {
-    red[threadIdx.x >> 6] = mn;
-    red[kRowWaves + (threadIdx.x >> 6)] = mx;
+    red[threadIdx.x >> 6] = kmn;
+    red[kRowWaves + (threadIdx.x >> 6)] = kmx;
   }
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kRowWaves; ++w) {
-    mn = fminf(mn, red[w]);
-    mx = fmaxf(mx, red[kRowWaves + w]);
+    kmn = min(kmn, red[w]);
+    kmx = max(kmx, red[kRowWaves + w]);
   }
+  mn = from_key(kmn);
+  mx = from_key(kmx);
 }
 
 // MODE 0: int8 (ASYM selects the zero point); MODE 1: FP8 E4M3 (symmetric,
@@ -204,7 +248,7 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8))
                                                                  float* __restrict__ s_a,
                                                                  int32_t* __restrict__ azp) {
   __shared__ double red_ss[2 * kRowWaves];
-  __shared__ float red_range[2 * kRowWaves];
+  __shared__ int red_range[2 * kRowWaves];
   const int tid = threadIdx.x;
   const int m = blockIdx.x;
   const uint4* xv = reinterpret_cast<const uint4*>(X + (size_t)m * K);
