@@ -48,6 +48,8 @@
 //   * the waves of a workgroup split K and add their 16 x 16 tiles in LDS.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ql_internal.h"
 
 namespace ql {
@@ -126,6 +128,18 @@ __device__ inline void load_lds4(const void* src, uint8_t* lds) {
 #endif
 }
 
+// A lane's fixed 32-bit offset from a uniform base, made opaque to the
+// optimizer (in place, so no copy is made) so that it stays a separate operand
+// of each copy (the scalar-base plus vector-offset form) instead of being
+// folded into a 64-bit per-lane pointer advanced with vector instructions
+// every group.
+__device__ inline uint32_t lane_offset(uint32_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#endif
+  return v;
+}
+
 // waits until at most N of this wave's vector-memory operations are in flight
 template <int N>
 __device__ inline void wait_vm() {
@@ -157,10 +171,14 @@ __device__ inline void wait_groups(int k) {
   }
 }
 
+// OFF: a byte offset known at compile time, carried in the instruction's
+// offset field (so the ring slot and the slice cost no address arithmetic)
+template <int OFF>
 __device__ inline u32x4 lds_read16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
   u32x4 v;
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
 #else
   v = u32x4{addr, 0, 0, 0};   // host pass only (never executed)
 #endif
@@ -178,14 +196,24 @@ __device__ inline void after_wait(u32x4& v) {
 #endif
 }
 
+template <int OFF>
 __device__ inline uint32_t lds_read4(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
   uint32_t v;
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
 #else
   v = addr;   // host pass only (never executed)
 #endif
   return v;
+}
+
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 __device__ inline void after_wait(uint32_t& v) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -266,14 +294,16 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
   const int full = gridDim.x & ~7;
   const int cb = (int)blockIdx.x < full ? (blockIdx.x & 7) * (full >> 3) + (blockIdx.x >> 3) : blockIdx.x;
 
-  // global sources of this lane's copies
-  const uint4* wsrc[NT];
+  // Global sources of this lane's copies.  The weight and activation copies
+  // address a workgroup-uniform base (advanced per group in scalar registers)
+  // plus a 32-bit lane offset that stays fixed, so advancing costs no vector
+  // instructions.  Weights: lane l of slice t reads channel
+  // (cb NT + t) 16 + l % 16 of K-block l / 16 (uint4 units: + 4 Np per group).
   const size_t np = a.Np;
+  const char* wbase = reinterpret_cast<const char*>(a.W + (size_t)cb * NT * 16);
+  uint32_t wlane[NT];                                       // < 64 Np bytes
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int n = (cb * NT + t) * 16 + cl;                  // output channel of this lane in slice t
-    wsrc[t] = a.W + (size_t)blk * np + n;                   // + 4*Np*g for group g
-  }
+  for (int t = 0; t < NT; ++t) wlane[t] = (uint32_t)(blk * np + cl) * 16u + t * 256u;
   // The combined copy: lane l copies 16 bytes.  For MB = 0, lanes 0..15 copy
   // the token's 16-byte pieces of the group, then (from lane c0 = 16 for
   // MB = 0, 0 otherwise) 4 NT lanes copy the scale words of the workgroup's
@@ -308,11 +338,11 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
   // products only reach output rows that are never stored).  The one row of
   // MB = 0 travels in the combined copy, unswizzled (row 0's key is 0).
   constexpr int kXB = MB == 0 ? 1 : MB;
-  const uint16_t* xsrc[kXB];
+  uint32_t xlane[kXB];                                      // bytes from a.X + 256 g
 #pragma unroll
   for (int b = 0; b < kXB; ++b) {
     const int r = 4 * b + blk;
-    xsrc[b] = a.X + (size_t)min(r, a.M - 1) * a.K + ((cl ^ r) & 15) * 8;   // + 128*g
+    xlane[b] = ((uint32_t)min(r, a.M - 1) * (uint32_t)a.K + ((cl ^ r) & 15) * 8) * 2u;
   }
 
   // LDS byte addresses of this lane's reads inside slot 0
@@ -328,17 +358,29 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) x_rd[j] = rbase + SL::kX + rr * 256 + (((4 * blk + j) ^ rr) & 15) * 16;
 
-  // the copies of group g (inside the wave's range) into ring slot `slot`
+  // the copies of group g (inside the wave's range) into ring slot `slot`;
+  // groups are issued in increasing order, one after the other, and the
+  // combined copy's source (a different array per lane) advances by cg per
+  // group and cp per pair of groups
+  const char* cnext = csrc + (size_t)g0 * cg + (size_t)(g0 >> 1) * cp;
   auto issue = [&](int g, int slot) {
     uint8_t* dst = ring + slot * SL::kBytes;
-    const int pr = g >> 1;
+    const char* wg = wbase + (size_t)g * 64 * np;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) load_lds16_stream(wsrc[t] + (size_t)g * 4 * np, dst + SL::kW + t * 1024);
-    if constexpr (MB > 0) {
-#pragma unroll
-      for (int b = 0; b < MB; ++b) load_lds16(xsrc[b] + (size_t)g * kGroup, dst + SL::kX + b * 1024);
+    for (int t = 0; t < NT; ++t) {
+      wlane[t] = lane_offset(wlane[t]);
+      load_lds16_stream(wg + wlane[t], dst + SL::kW + t * 1024);
     }
-    load_lds16(csrc + (uint32_t)g * cg + (uint32_t)pr * cp, dst + SL::kC);
+    if constexpr (MB > 0) {
+      const char* xg = reinterpret_cast<const char*>(a.X) + (size_t)g * 2 * kGroup;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        xlane[b] = lane_offset(xlane[b]);
+        load_lds16(xg + xlane[b], dst + SL::kX + b * 1024);
+      }
+    }
+    load_lds16(cnext, dst + SL::kC);
+    cnext += cg + ((g & 1) ? cp : 0u);
   };
 
   // the unpacking constants in registers (one v_and_or_b32 per register of
@@ -356,18 +398,18 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int g, int slot) {
-    const uint32_t so = slot * SL::kBytes;
+  auto compute = [&](int g, auto SLOT) {
+    constexpr int so = decltype(SLOT)::value * SL::kBytes;
     u32x4 xa[4], wv[NT];
     uint32_t sv[NT], zv[NT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xa[j] = lds_read16(x_rd[j] + so);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      wv[t] = lds_read16(w_rd + so + t * 1024);
-      sv[t] = lds_read4(s_rd + so + t * 64);
-      zv[t] = lds_read4(z_rd + so + t * 16);
-    }
+    for (int j = 0; j < 4; ++j) xa[j] = lds_read16<so>(x_rd[j]);
+    static_for<0, NT>([&](auto T) {
+      constexpr int t = decltype(T)::value;
+      wv[t] = lds_read16<so + t * 1024>(w_rd);
+      sv[t] = lds_read4<so + t * 64>(s_rd);
+      zv[t] = lds_read4<so + t * 16>(z_rd);
+    });
     lds_wait();
 #pragma unroll
     for (int j = 0; j < 4; ++j) after_wait(xa[j]);
@@ -396,21 +438,29 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int i = 0; i < D - 1; ++i)
     if (g0 + i < g1) issue(g0 + i, i);
-  int slot = 0;
-  for (int g = g0; g < g1; ++g) {
-    // refill the slot the previous group was read from (its reads finished
-    // before its arithmetic) with group g + D - 1, then wait until group g's
-    // copies have landed: the groups issued after it may stay in flight
-    if (g + D - 1 < g1) {
-      issue(g + D - 1, slot == 0 ? D - 1 : slot - 1);
-      wait_vm<(D - 1) * SL::kLoads>();
-    } else {
-      wait_groups<D, SL::kLoads>(g1 - 1 - g);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    compute(g, slot);
-    __builtin_amdgcn_sched_barrier(0);
-    slot = slot == D - 1 ? 0 : slot + 1;
+  // the loop is unrolled over the D ring slots, so that every slot offset is
+  // a constant of the instructions that read it
+  int g = g0;
+  while (g < g1) {
+    static_for<0, D>([&](auto SLOT) {
+      constexpr int slot = decltype(SLOT)::value;
+      if (g < g1) {
+        // refill the slot the previous group was read from (its reads
+        // finished before its arithmetic) with group g + D - 1, then wait
+        // until group g's copies have landed: the groups issued after it may
+        // stay in flight
+        if (g + D - 1 < g1) {
+          issue(g + D - 1, slot == 0 ? D - 1 : slot - 1);
+          wait_vm<(D - 1) * SL::kLoads>();
+        } else {
+          wait_groups<D, SL::kLoads>(g1 - 1 - g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        compute(g, SLOT);
+        __builtin_amdgcn_sched_barrier(0);
+        ++g;
+      }
+    });
   }
   wait_vm<0>();                           // no copy may still target the staging area
 
