@@ -64,6 +64,7 @@ struct I8Args {
   const int8_t* B;
   int M, N, K;
   I8Epi e;
+  bool off32;              // M K and N K below 2^32: lane offsets fit 32 bits
 };
 
 // byte offset of logical 16-byte piece p of row r inside an operand tile: four
@@ -100,6 +101,7 @@ struct FillPlan {
   const int8_t* src[kLoads];   // row of each block
   int p16[kLoads];             // byte offset of this lane's logical piece inside a K block
   int dst[kLoads];             // byte offset of the lane's 1 KB destination block inside a slot
+  uint32_t off[kLoads];        // row * K + p16: the lane's offset from the operand's base (off32 only)
 };
 
 __device__ inline FillPlan make_fill_plan(const I8Args& a, int m0, int n0, int wave, int lane) {
@@ -109,9 +111,11 @@ __device__ inline FillPlan make_fill_plan(const I8Args& a, int m0, int n0, int w
     const bool is_a = i < kAFills;
     const int blk = is_a ? wave * kAFills + i : wave * kBFills + (i - kAFills);
     const int r = blk * (1024 / BK) + lane / kPieces;
-    f.src[i] = is_a ? a.A + (size_t)min(m0 + r, a.M - 1) * a.K : a.B + (size_t)min(n0 + r, a.N - 1) * a.K;
+    const int row = is_a ? min(m0 + r, a.M - 1) : min(n0 + r, a.N - 1);
+    f.src[i] = (is_a ? a.A : a.B) + (size_t)row * a.K;
     f.p16[i] = ((lane % kPieces) ^ swz_key(r)) * 16;
     f.dst[i] = (is_a ? 0 : kASlot) + blk * 1024;
+    f.off[i] = (uint32_t)row * (uint32_t)a.K + (uint32_t)f.p16[i];
   }
   return f;
 }
@@ -125,6 +129,17 @@ __device__ inline void fill(const FillPlan& f, int kb, int K) {
     const int k = min(kb * BK + f.p16[i], K - 16);
     load_lds16(f.src[i] + k, g_lds + S * kSlot + f.dst[i]);
   }
+}
+
+// A lane's fixed 32-bit offset from a uniform base, made opaque to the
+// optimizer (in place) so that each copy keeps the scalar-base plus
+// vector-offset form instead of a 64-bit per-lane address computed with
+// vector instructions every block.
+__device__ inline uint32_t lane_offset(uint32_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#endif
+  return v;
 }
 
 // waits until at most N of this wave's vector-memory operations are in flight
@@ -180,7 +195,7 @@ __device__ inline void after_wait(i32x4& v) {
 //         (pieces 2 (l / 32) + j, j = 0, 1)
 __device__ inline int frag_piece(bool fp8, int j, int half) { return fp8 ? 2 * half + j : 2 * j + half; }
 
-template <int S, bool FP8, typename Mid>
+template <int S, bool FP8, bool FULL, typename Mid>
 __device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard)[2], const uint32_t (&brd)[2],
                                  int half, int kvalid, Mid&& mid) {
   if constexpr (FP8) {
@@ -196,11 +211,11 @@ __device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       // pieces past kvalid (a ragged last block): zero the A side
-      const bool live = frag_piece(true, j, half) * 16 < kvalid;
+      const bool live = FULL || frag_piece(true, j, half) * 16 < kvalid;
 #pragma unroll
       for (int t = 0; t < kMT; ++t) {
         after_wait(af[j][t]);
-        af[j][t] = live ? af[j][t] : i32x4{0, 0, 0, 0};
+        if (!FULL) af[j][t] = live ? af[j][t] : i32x4{0, 0, 0, 0};
       }
 #pragma unroll
       for (int t = 0; t < kNT; ++t) after_wait(bf[j][t]);
@@ -237,11 +252,11 @@ __device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard
     else
       lds_wait<0>();
     // pieces past kvalid (a ragged last block): zero the A side
-    const bool live = (ks * 2 + half) * 16 < kvalid;
+    const bool live = FULL || (ks * 2 + half) * 16 < kvalid;
 #pragma unroll
     for (int t = 0; t < kMT; ++t) {
       after_wait(af[ks][t]);
-      af[ks][t] = live ? af[ks][t] : i32x4{0, 0, 0, 0};
+      if (!FULL) af[ks][t] = live ? af[ks][t] : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int t = 0; t < kNT; ++t) after_wait(bf[ks][t]);
@@ -258,8 +273,8 @@ __device__ inline void mma_block(Acc<FP8> (&acc)[kMT][kNT], const uint32_t (&ard
 // one k-block: wait for slot S, barrier, refill the slot freed by the previous
 // block with block kb + kStages - 1 (clamped to the last block near the end, so
 // that every wave always has the same number of loads in flight), multiply slot S
-template <int S, bool FP8>
-__device__ inline void kstep(const I8Args& a, const FillPlan& f, Acc<FP8> (&acc)[kMT][kNT], int kb, int nkb,
+template <int S, bool FP8, bool FULL, bool PLAIN>
+__device__ inline void kstep(const I8Args& a, FillPlan& f, Acc<FP8> (&acc)[kMT][kNT], int kb, int nkb,
                              const uint32_t (&ard)[kHalves][2], const uint32_t (&brd)[kHalves][2], int half) {
   // this wave's loads of block kb are done once at most (kStages - 2) blocks
   // of its loads remain in flight
@@ -271,10 +286,21 @@ __device__ inline void kstep(const I8Args& a, const FillPlan& f, Acc<FP8> (&acc)
   // stalls on a copy until the address unit takes it, and issuing all of
   // them at once held the whole block's arithmetic back
   const int fb = min(kb + kStages - 1, nkb - 1);
+  // PLAIN (the prefetched block lies wholly inside K and the operands' lane
+  // offsets fit 32 bits): the copies address the operand's base plus the
+  // block's offset (scalar) plus the lane's fixed offset; otherwise K offsets
+  // past a row's end are clamped to its last 16 bytes (zeroed before use: see
+  // mma_block)
   auto copies = [&](auto I0, auto I1) {
     static_for<I0, I1>([&](auto I) {
-      const int k = min(fb * BK + f.p16[I], a.K - 16);
-      load_lds16(f.src[I] + k, g_lds + F * kSlot + f.dst[I]);
+      if constexpr (PLAIN) {
+        const int8_t* base = (I < kAFills ? a.A : a.B) + (size_t)fb * BK;
+        f.off[I] = lane_offset(f.off[I]);
+        load_lds16(base + f.off[I], g_lds + F * kSlot + f.dst[I]);
+      } else {
+        const int k = min(fb * BK + f.p16[I], a.K - 16);
+        load_lds16(f.src[I] + k, g_lds + F * kSlot + f.dst[I]);
+      }
     });
   };
   // four shares: before each half's fragment reads and after its first MFMAs
@@ -285,18 +311,22 @@ __device__ inline void kstep(const I8Args& a, const FillPlan& f, Acc<FP8> (&acc)
     constexpr int b0 = q0 * kQ + (q0 < kR ? q0 : kR), e0 = b0 + kQ + (q0 < kR ? 1 : 0);
     constexpr int b1 = e0, e1 = b1 + kQ + (q1 < kR ? 1 : 0);
     copies(std::integral_constant<int, b0>{}, std::integral_constant<int, e0>{});
-    mma_block<S, FP8>(acc, ard[hh], brd[hh], half, a.K - kb * BK - 64 * hh,
+    mma_block<S, FP8, FULL>(acc, ard[hh], brd[hh], half, a.K - kb * BK - 64 * hh,
                       [&] { copies(std::integral_constant<int, b1>{}, std::integral_constant<int, e1>{}); });
   });
 }
 
-// the last (nkb mod kStages) blocks, slots 0, 1, ... in order
+// the blocks after the main loop (at most 2 kStages - 1 of them, the last
+// possibly ragged), slots continuing in order
 template <int S, bool FP8>
-__device__ inline void kstep_tail(const I8Args& a, const FillPlan& f, Acc<FP8> (&acc)[kMT][kNT], int kb, int nkb,
+__device__ inline void kstep_tail(const I8Args& a, FillPlan& f, Acc<FP8> (&acc)[kMT][kNT], int kb, int nkb,
                                   const uint32_t (&ard)[kHalves][2], const uint32_t (&brd)[kHalves][2], int half) {
-  if constexpr (S < kStages - 1) {
+  if constexpr (S < 2 * kStages - 1) {
     if (kb < nkb) {
-      kstep<S, FP8>(a, f, acc, kb, nkb, ard, brd, half);
+      if (a.K - kb * BK >= BK)
+        kstep<S % kStages, FP8, true, false>(a, f, acc, kb, nkb, ard, brd, half);
+      else
+        kstep<S % kStages, FP8, false, false>(a, f, acc, kb, nkb, ard, brd, half);
       kstep_tail<S + 1, FP8>(a, f, acc, kb + 1, nkb, ard, brd, half);
     }
   }
@@ -351,12 +381,21 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
     }
 
   // prologue: blocks 0 .. kStages - 2 in flight (clamped to the last block)
-  const FillPlan f = make_fill_plan(a, m0, n0, wave, lane);
+  FillPlan f = make_fill_plan(a, m0, n0, wave, lane);
   static_for<0, kStages - 1>([&](auto J) { fill<J>(f, min((int)J, nkb - 1), a.K); });
 
   int kb = 0;
-  for (; kb + kStages <= nkb; kb += kStages)
-    static_for<0, kStages>([&](auto S) { kstep<S, FP8>(a, f, acc, kb + S, nkb, ard, brd, half); });
+  // whole rounds of kStages blocks that lie wholly inside K (no piece of
+  // them to zero), and whose prefetched blocks (kStages - 1 ahead) do too
+  // when the copies can take the scalar-base form; then the rest
+  const int nfull = a.K / BK;
+  if (a.off32) {
+    for (; kb + 2 * kStages - 1 <= nfull; kb += kStages)
+      static_for<0, kStages>([&](auto S) { kstep<S, FP8, true, true>(a, f, acc, kb + S, nkb, ard, brd, half); });
+  } else {
+    for (; kb + kStages <= nfull; kb += kStages)
+      static_for<0, kStages>([&](auto S) { kstep<S, FP8, true, false>(a, f, acc, kb + S, nkb, ard, brd, half); });
+  }
   kstep_tail<0, FP8>(a, f, acc, kb, nkb, ard, brd, half);
   wait_vm<0>();                                  // no load may still target LDS at exit
 
@@ -490,7 +529,7 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
 }  // namespace
 
 hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
-  I8Args a{A, B, M, N, K, e};
+  I8Args a{A, B, M, N, K, e, (size_t)M * K <= 0xFFFFFFFFu && (size_t)N * K <= 0xFFFFFFFFu};
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (e.out_bf16)
     hipLaunchKernelGGL((i8_gemm_kernel<true, false>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
@@ -500,7 +539,8 @@ hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K,
 }
 
 hipError_t launch_f8_gemm(const uint8_t* A, const uint8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
-  I8Args a{reinterpret_cast<const int8_t*>(A), reinterpret_cast<const int8_t*>(B), M, N, K, e};
+  I8Args a{reinterpret_cast<const int8_t*>(A), reinterpret_cast<const int8_t*>(B), M, N, K, e,
+            (size_t)M * K <= 0xFFFFFFFFu && (size_t)N * K <= 0xFFFFFFFFu};
   a.e.azp = nullptr;
   a.e.azp_adj = nullptr;
   a.e.raw = nullptr;
