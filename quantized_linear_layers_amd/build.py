@@ -28,12 +28,15 @@ COMMON = [
 SOURCES = {
     "abi.cpp": [],
     "host_quant.cpp": ["-ffp-contract=off"],
-    "q4_gemv.hip": [],
-    "q4_gemm.hip": [],
-    "i8_quant.hip": ["-ffp-contract=off"],
-    "i8_gemm.hip": [],
-    "act_order.hip": [],
-    "read_probe.hip": [],
+    # "-amdgpu-kernarg-preload-count=n": the kernels' first n arguments are
+    # preloaded into scalar registers at wave launch (no argument loads
+    # before the first copy)
+    "q4_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"],
+    "q4_gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
+    "i8_quant.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-kernarg-preload-count=8"],
+    "i8_gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=6"],
+    "act_order.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
+    "read_probe.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
 }
 
 

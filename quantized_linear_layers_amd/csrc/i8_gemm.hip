@@ -347,8 +347,20 @@ __device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
   nt = (t % gsize) / gm;
 }
 
+// The operands and sizes are separate scalars, first in the list, so that
+// they are preloaded into scalar registers at wave launch; the epilogue's
+// arguments follow, read from memory as usual (needed at the end).
 template <bool OUT_BF16, bool FP8>
-__global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(I8Args a) {
+__global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(const int8_t* A, const int8_t* B, int M, int N, int K,
+                                                              int off32, I8Epi epi) {
+  I8Args a;
+  a.A = A;
+  a.B = B;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.e = epi;
+  a.off32 = off32 != 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int mtile, ntile;
@@ -532,9 +544,11 @@ hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K,
   I8Args a{A, B, M, N, K, e, (size_t)M * K <= 0xFFFFFFFFu && (size_t)N * K <= 0xFFFFFFFFu};
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (e.out_bf16)
-    hipLaunchKernelGGL((i8_gemm_kernel<true, false>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
+    hipLaunchKernelGGL((i8_gemm_kernel<true, false>), dim3(tiles), dim3(64 * kWaves), 0, st, a.A, a.B, a.M, a.N,
+                       a.K, (int)a.off32, a.e);
   else
-    hipLaunchKernelGGL((i8_gemm_kernel<false, false>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
+    hipLaunchKernelGGL((i8_gemm_kernel<false, false>), dim3(tiles), dim3(64 * kWaves), 0, st, a.A, a.B, a.M, a.N,
+                       a.K, (int)a.off32, a.e);
   return hipGetLastError();
 }
 
@@ -546,9 +560,11 @@ hipError_t launch_f8_gemm(const uint8_t* A, const uint8_t* B, int M, int N, int 
   a.e.raw = nullptr;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (e.out_bf16)
-    hipLaunchKernelGGL((i8_gemm_kernel<true, true>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
+    hipLaunchKernelGGL((i8_gemm_kernel<true, true>), dim3(tiles), dim3(64 * kWaves), 0, st, a.A, a.B, a.M, a.N,
+                       a.K, (int)a.off32, a.e);
   else
-    hipLaunchKernelGGL((i8_gemm_kernel<false, true>), dim3(tiles), dim3(64 * kWaves), 0, st, a);
+    hipLaunchKernelGGL((i8_gemm_kernel<false, true>), dim3(tiles), dim3(64 * kWaves), 0, st, a.A, a.B, a.M, a.N,
+                       a.K, (int)a.off32, a.e);
   return hipGetLastError();
 }
 

@@ -440,8 +440,27 @@ __device__ __forceinline__ void kstep(uint8_t* lds, Frag<C>& fr, const GemmArgs&
   }
 }
 
+// The arguments the K loop needs are separate scalars, first in the list, so
+// that they are preloaded into scalar registers at wave launch; the output
+// pointers and stride follow, read from memory as usual (needed at the end).
 template <class C, bool BF16>
-__global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(const uint4* W, const uint16_t* X, const uint32_t* S,
+                                                                 const uint8_t* Z, int M, int K, int N, int Np,
+                                                                 int ldw, int kbs, uint16_t* Y, float* P, int ldy) {
+  GemmArgs a;
+  a.X = X;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.Np = Np;
+  a.ldw = ldw;
+  a.ldy = ldy;
+  a.W = W;
+  a.S = S;
+  a.Z = Z;
+  a.Y = Y;
+  a.kbs = kbs;
+  a.P = P;
   constexpr int kMT = C::kMT, kAFills = C::kAFills, kStages = C::kStages;
   __shared__ __align__(1024) uint8_t lds[C::kLds];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -613,9 +632,11 @@ template <class C>
 hipError_t launch_cfg(const GemmArgs& a, bool bf16, hipStream_t st, int splits = 1) {
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
   if (bf16)
-    hipLaunchKernelGGL((q4_gemm_kernel<C, true>), dim3(tiles, splits), dim3(64 * C::kWaves), 0, st, a);
+    hipLaunchKernelGGL((q4_gemm_kernel<C, true>), dim3(tiles, splits), dim3(64 * C::kWaves), 0, st, a.W, a.X, a.S, a.Z,
+                       a.M, a.K, a.N, a.Np, a.ldw, a.kbs, a.Y, a.P, a.ldy);
   else
-    hipLaunchKernelGGL((q4_gemm_kernel<C, false>), dim3(tiles, splits), dim3(64 * C::kWaves), 0, st, a);
+    hipLaunchKernelGGL((q4_gemm_kernel<C, false>), dim3(tiles, splits), dim3(64 * C::kWaves), 0, st, a.W, a.X, a.S, a.Z,
+                       a.M, a.K, a.N, a.Np, a.ldw, a.kbs, a.Y, a.P, a.ldy);
   return hipGetLastError();
 }
 

@@ -270,8 +270,26 @@ constexpr int gemv_lds_bytes(int NT, int MB, int NW) { return NW * ring_depth_of
 // NT: 16-column slices per workgroup; MB: blocks of 4 activation rows staged
 // per group (4 * MB >= M; 0: the one row of M = 1); NW: waves per workgroup
 // (they split K).
+//
+// The arguments are separate scalars, in the order the kernel first needs
+// them, so that the leading ones can be preloaded into scalar registers at
+// wave launch instead of read from the argument segment (two dependent
+// memory round trips before the first copy); Y, needed only at the end, is
+// read from memory as usual.
 template <bool BF16, int NT, int MB, int NW>
-__global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(const uint4* W, const uint16_t* X, const uint32_t* S,
+                                                          const uint8_t* Z, int K, int Np, int M, int N, uint16_t* Y) {
+  GemvArgs a;
+  a.X = X;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.Np = Np;
+  a.Kp = 0;
+  a.W = W;
+  a.S = S;
+  a.Z = Z;
+  a.Y = Y;
   using SL = Slot<NT, MB>;
   constexpr int D = ring_depth<NT, MB, NW>();
   constexpr int kWaveBytes = D * SL::kBytes;
@@ -291,7 +309,7 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(GemvArgs a) {
   // 8 XCDs, each with its own L2; neighbouring blocks share the 128-byte lines
   // of the scale and zero-point rows, so consecutive blocks go to one XCD
   // (otherwise up to 8 L2s would each fetch the same line).
-  const int full = gridDim.x & ~7;
+  const int full = (int)((uint32_t)Np / (16 * NT)) & ~7;       // of the grid's Np / (16 NT) workgroups
   const int cb = (int)blockIdx.x < full ? (blockIdx.x & 7) * (full >> 3) + (blockIdx.x >> 3) : blockIdx.x;
 
   // Global sources of this lane's copies.  The weight and activation copies
@@ -496,9 +514,11 @@ template <bool BF16, int NT, int MB>
 hipError_t launch_cfg(const GemvArgs& a, const GemvPlan& P, hipStream_t st) {
   const dim3 grid(a.Np / (16 * NT));
   if (P.waves == 8)
-    hipLaunchKernelGGL((q4_gemv_kernel<BF16, NT, MB, 8>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((q4_gemv_kernel<BF16, NT, MB, 8>), grid, dim3(512), 0, st, a.W, a.X, a.S, a.Z, a.K, a.Np, a.M,
+                       a.N, a.Y);
   else
-    hipLaunchKernelGGL((q4_gemv_kernel<BF16, NT, MB, 4>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((q4_gemv_kernel<BF16, NT, MB, 4>), grid, dim3(256), 0, st, a.W, a.X, a.S, a.Z, a.K, a.Np, a.M,
+                       a.N, a.Y);
   return hipGetLastError();
 }
 

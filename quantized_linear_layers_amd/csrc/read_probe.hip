@@ -46,16 +46,19 @@ __device__ inline uint32_t read_range(const u32x4* __restrict__ src, uint64_t b,
   return acc;
 }
 
+// The arguments (with the grid's size, nwg = gridDim.x) are preloaded into
+// scalar registers at wave launch, as for the decode kernel, so that both
+// start streaming after the same latency.
 template <bool CHUNK>
 __global__ __launch_bounds__(kThreads) void read_probe_kernel(const u32x4* __restrict__ src, uint64_t n16,
-                                                              uint32_t* __restrict__ sink) {
+                                                              uint32_t nwg, uint32_t* __restrict__ sink) {
   uint32_t acc;
   if constexpr (CHUNK) {
-    const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const uint64_t per = (n16 + nwg - 1) / nwg;
     const uint64_t b = min((uint64_t)blockIdx.x * per, n16), e = min(b + per, n16);
     acc = read_range(src, b, e, threadIdx.x, kThreads);
   } else {
-    acc = read_range(src, 0, n16, (uint64_t)blockIdx.x * kThreads + threadIdx.x, (uint64_t)gridDim.x * kThreads);
+    acc = read_range(src, 0, n16, (uint64_t)blockIdx.x * kThreads + threadIdx.x, (uint64_t)nwg * kThreads);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
@@ -71,10 +74,10 @@ hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int 
   const u32x4* s = static_cast<const u32x4*>(src);
   if (mode == 1)
     hipLaunchKernelGGL(read_probe_kernel<true>, dim3(workgroups), dim3(kThreads), 0, st, s, (uint64_t)(bytes / 16),
-                       sink);
+                       (uint32_t)workgroups, sink);
   else
     hipLaunchKernelGGL(read_probe_kernel<false>, dim3(workgroups), dim3(kThreads), 0, st, s, (uint64_t)(bytes / 16),
-                       sink);
+                       (uint32_t)workgroups, sink);
   return hipGetLastError();
 }
 
