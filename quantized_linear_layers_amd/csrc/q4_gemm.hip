@@ -600,8 +600,13 @@ __global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(const uint4* W,
 // Y = the 16-bit rounding of the sum of the S fp32 partial results P[s]
 // (split s of K), added in split order: 4 consecutive elements per thread,
 // the last partial group element by element.
-template <bool BF16>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int S, size_t MN,
+// Adds the S partial tiles in split order and rounds once.  S is a template
+// argument so that a thread issues all S loads of its four elements before
+// the first addition (with S a loop bound, each addition waited for its
+// load: S memory round trips in a row); the order of the additions is the
+// same either way.
+template <bool BF16, int S>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, size_t MN,
                                                             uint16_t* __restrict__ Y) {
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= MN) return;
@@ -609,13 +614,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     return BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
   };
   if (i + 4 <= MN) {
-    float4 acc = *reinterpret_cast<const float4*>(P + i);
+    float4 v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) v[s] = *reinterpret_cast<const float4*>(P + (size_t)s * MN + i);
+    float4 acc = v[0];
+#pragma unroll
     for (int s = 1; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(P + (size_t)s * MN + i);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+      acc.x += v[s].x;
+      acc.y += v[s].y;
+      acc.z += v[s].z;
+      acc.w += v[s].w;
     }
     const uint2 o = make_uint2(cvt(acc.x) | ((uint32_t)cvt(acc.y) << 16), cvt(acc.z) | ((uint32_t)cvt(acc.w) << 16));
     *reinterpret_cast<uint2*>(Y + i) = o;
@@ -640,13 +648,29 @@ hipError_t launch_cfg(const GemmArgs& a, bool bf16, hipStream_t st, int splits =
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const float* P, int S, size_t MN, uint16_t* Y, bool bf16, hipStream_t st) {
+template <bool BF16, int S>
+hipError_t launch_reduce_s(const float* P, size_t MN, uint16_t* Y, hipStream_t st) {
   const dim3 grid((unsigned)((MN + 1023) / 1024));
-  if (bf16)
-    hipLaunchKernelGGL(splitk_reduce_kernel<true>, grid, dim3(256), 0, st, P, S, MN, Y);
-  else
-    hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, st, P, S, MN, Y);
+  hipLaunchKernelGGL((splitk_reduce_kernel<BF16, S>), grid, dim3(256), 0, st, P, MN, Y);
   return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_reduce_t(const float* P, int S, size_t MN, uint16_t* Y, hipStream_t st) {
+  switch (S) {
+    case 2: return launch_reduce_s<BF16, 2>(P, MN, Y, st);
+    case 3: return launch_reduce_s<BF16, 3>(P, MN, Y, st);
+    case 4: return launch_reduce_s<BF16, 4>(P, MN, Y, st);
+    case 5: return launch_reduce_s<BF16, 5>(P, MN, Y, st);
+    case 6: return launch_reduce_s<BF16, 6>(P, MN, Y, st);
+    case 7: return launch_reduce_s<BF16, 7>(P, MN, Y, st);
+    case 8: return launch_reduce_s<BF16, 8>(P, MN, Y, st);
+    default: return hipErrorInvalidValue;      // plans split K at most 8 ways
+  }
+}
+
+hipError_t launch_reduce(const float* P, int S, size_t MN, uint16_t* Y, bool bf16, hipStream_t st) {
+  return bf16 ? launch_reduce_t<true>(P, S, MN, Y, st) : launch_reduce_t<false>(P, S, MN, Y, st);
 }
 
 }  // namespace
