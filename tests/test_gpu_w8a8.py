@@ -143,6 +143,39 @@ def test_gemm_wide_zero_points():
     check_gemm(Aq, Bq, s_a, s_b, (azp % 64).astype(np.int32), wide_adj.astype(np.int32))
 
 
+def test_gemm_operand_over_4gib():
+    """Aq past 4 GiB (M*K > 2^32): the main loop's copies then take 64-bit
+    row addresses instead of 32-bit lane offsets from the operand's base.
+    Aq is drawn on the device from a seeded generator; sampled rows (among
+    them the first and the last tile's) are checked against the oracle: the
+    int32 accumulator bit-exact, both output paths within the tolerance."""
+    M, N, K = (1 << 20) + 7, 160, 4112            # ragged M, N and K
+    assert M * K > 0xFFFFFFFF
+    g = torch.Generator(device="cuda").manual_seed(11)
+    Aq = torch.randint(-128, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+    r = np.random.default_rng(12)
+    Bq, s_b = ow8.quant_weight_per_channel_sym((r.standard_normal((N, K)) * 0.02).astype(np.float32))
+    s_a = (r.random(M) * 0.01 + 1e-3).astype(np.float32)
+    azp = r.integers(-128, 128, M).astype(np.int32)
+    adj = ow8.azp_adj(Bq)
+    bias = torch.from_numpy(r.standard_normal(N).astype(np.float32) * 0.1).half()
+    args = (Aq, cu(Bq), cu(s_a), cu(s_b), cu(azp), cu(adj), bias.cuda())
+    out, raw = ql.i8_gemm_scaled(*args, raw=True)
+    out_fast = ql.i8_gemm_scaled(*args)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, M // 2, M - 257, M - 8, M - 1], r.integers(0, M, 24)]))
+    ri = torch.from_numpy(rows).cuda()
+    C, out64 = ow8.w8a8_linear(Aq.index_select(0, ri).cpu().numpy(), Bq, s_a[rows], s_b, azp[rows], adj,
+                               wl.as_f64(bias))
+    assert np.array_equal(raw.index_select(0, ri).cpu().numpy().astype(np.int64), C)
+    for o in (out, out_fast):
+        od = wl.as_f64(o.index_select(0, ri).cpu())
+        e = float(np.abs(od - out64).max() / np.abs(out64).max())
+        assert e <= TOL, f"relative error {e:.3e}"
+    del Aq, raw, out, out_fast
+    torch.cuda.empty_cache()
+
+
 def test_launcher_matches_the_binding():
     """The pre-marshalled launcher (used for tight launch loops) gives the
     same bytes as the checked binding, for the quant and the GEMM entry
