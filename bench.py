@@ -86,9 +86,10 @@ def _copies_for(total_bytes):
 
 
 # plain-read probe configurations (mode, workgroups); the fastest per layer is
-# the read ceiling (grid-stride reads win on tens of MB, one contiguous chunk
-# per workgroup on hundreds)
-READ_PROBES = ((0, 2048), (1, 512), (1, 1024))
+# the read ceiling (grid-stride reads on 2048 workgroups win on tens of MB; on
+# hundreds, grid-stride reads on 256 and one contiguous chunk per workgroup on
+# 512 or 1024 come within a few percent of each other, box to box)
+READ_PROBES = ((0, 2048), (0, 256), (1, 512), (1, 1024))
 # back-to-back steps before the W warm-up steps: the first tens of
 # milliseconds of work after the weights are prepared run slower (measured:
 # 147 us for the 70B step after 30 ms of warm-up, 118-121 us after 60 ms more)
