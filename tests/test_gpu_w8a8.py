@@ -4,8 +4,9 @@ i8_quant_per_token: codes, zero points and fp32 scales bit-exact with the
 oracle (both decide the codes in IEEE fp32 with round-half-to-even).
 i8_gemm_scaled: the int32 corrected accumulator (raw_out) bit-exact with the
 oracle's exact integer product, the fp16/bf16 output within
-max|out - out64| / max|out64| <= 1e-2.  The GEMM's inputs are the oracle's
-own quantized operands.
+max|out - out64| / max|out64| <= 1e-2 and, element by element, within the
+bound of the epilogue's own roundings (epilogue_bound).  The GEMM's inputs
+are the oracle's own quantized operands.
 """
 
 import numpy as np
@@ -38,6 +39,30 @@ def check_quant(X, symmetric=False):
     assert np.array_equal(Aq.cpu().numpy(), Aq_o)
 
 
+def epilogue_bound(C, s_a, s_b, bias, out64, out_dtype):
+    """Element-wise bound of the fused epilogue's float output: the int32 C
+    is exact, then at most four fp32 roundings (C to fp32, the two scale
+    products, the bias add), each within 2^-24 of a magnitude at most
+    |s_a s_b C| + |bias|, and one rounding to the output type (half an ulp:
+    at most 2^-11 |out| for fp16 and 2^-8 |out| for bf16, plus half the
+    fp16 subnormal spacing).  The fp32 term takes 5 units instead of 4 to
+    cover the output rounding's share of the fp32 error."""
+    sa = np.broadcast_to(np.asarray(s_a, np.float64).reshape(-1, 1), out64.shape)
+    sb = np.broadcast_to(np.asarray(s_b, np.float64).reshape(1, -1), out64.shape)
+    mag = np.abs(sa * sb * C.astype(np.float64))
+    if bias is not None:
+        mag = mag + np.abs(wl.as_f64(bias)).reshape(1, -1)
+    half_ulp = (2.0 ** -11 * np.abs(out64) + 2.0 ** -25) if out_dtype == torch.float16 else 2.0 ** -8 * np.abs(out64)
+    return half_ulp + 5 * 2.0 ** -24 * mag
+
+
+def check_epilogue_bound(o, C, s_a, s_b, bias, out64, out_dtype):
+    err = np.abs(wl.as_f64(o.cpu()) - out64)
+    b = epilogue_bound(C, s_a, s_b, bias, out64, out_dtype)
+    worst = np.unravel_index(np.argmax(err / b), err.shape)
+    assert (err <= b).all(), f"element {worst}: |err| {err[worst]:.3e} exceeds the epilogue bound {b[worst]:.3e}"
+
+
 def check_gemm(Aq, Bq, s_a, s_b, azp=None, adj=None, bias=None, out_dtype=torch.float16):
     """With raw_out (per-element epilogue, the int32 accumulator kept) and
     without it (tiles wholly inside Y stage their outputs through LDS and
@@ -54,6 +79,7 @@ def check_gemm(Aq, Bq, s_a, s_b, azp=None, adj=None, bias=None, out_dtype=torch.
         od = wl.as_f64(o.cpu())
         e = float(np.abs(od - out64).max() / np.abs(out64).max())
         assert e <= TOL, f"relative error {e:.3e}"
+        check_epilogue_bound(o, C, s_a, s_b, bias, out64, out_dtype)
 
 
 # ---------------------------------------------------------------- the workload
@@ -169,9 +195,11 @@ def test_gemm_operand_over_4gib():
                                wl.as_f64(bias))
     assert np.array_equal(raw.index_select(0, ri).cpu().numpy().astype(np.int64), C)
     for o in (out, out_fast):
-        od = wl.as_f64(o.index_select(0, ri).cpu())
+        os_ = o.index_select(0, ri)
+        od = wl.as_f64(os_.cpu())
         e = float(np.abs(od - out64).max() / np.abs(out64).max())
         assert e <= TOL, f"relative error {e:.3e}"
+        check_epilogue_bound(os_, C, s_a[rows], s_b, bias, out64, torch.float16)
     del Aq, raw, out, out_fast
     torch.cuda.empty_cache()
 
