@@ -35,6 +35,7 @@ SOURCES = {
     "q4_gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
     "i8_quant.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-kernarg-preload-count=8"],
     "i8_gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=6"],
+    "i8_gemm_small.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=6"],
     "act_order.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
     "read_probe.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
 }

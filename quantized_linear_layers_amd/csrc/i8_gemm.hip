@@ -20,6 +20,16 @@
 // pieces of 16 bytes) stored with the piece index XORed by row bits 1..3, so
 // the 16 rows one operand read serves at a time fall on 16 different 16-byte
 // bank groups.
+//
+// Small grids: built a second time with QL_I8_SMALL_TILE (i8_gemm_small.hip),
+// the same kernel takes 128 x 128 tiles of 4 waves of 64 x 64, walking K in
+// 64-byte blocks through 4 slots of 16 KB (64 KB: two workgroups share a
+// compute unit, each multiplying while the other waits at its own barrier).
+// launch_i8_gemm / launch_f8_gemm take it when the 256 x 128 grid would fill
+// at most half the compute units: there the extra tiles outweigh the larger
+// tile's fewer copies per product (measured: 128 tokens on a 4096 x 4096
+// layer 26.8 -> 14.8 us, 512 tokens 22.9 -> 18.5 us; a wash at 128 large
+// tiles; slower beyond).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -38,16 +48,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 template <bool FP8>
 using Acc = std::conditional_t<FP8, f32x16, i32x16>;
 
-#ifndef QL_I8_WAVES
-#define QL_I8_WAVES 8
+#ifdef QL_I8_SMALL_TILE
+constexpr int BM = 128, BN = 128, BK = 64;       // BK in bytes (int8 elements)
+constexpr int kWaves = 4;
+constexpr int kStages = 4;                       // 64 KB of slots: two workgroups per compute unit
+#else
+constexpr int BM = 256, BN = 128, BK = 128;
+constexpr int kWaves = 8;
+constexpr int kStages = 3;                       // 144 KB of slots: one workgroup per compute unit
 #endif
-#ifndef QL_I8_BK
-#define QL_I8_BK 128
-#endif
-constexpr int BM = 256, BN = 128, BK = QL_I8_BK; // BK in bytes (int8 elements): 64 or 128
-constexpr int kWaves = QL_I8_WAVES;              // (BM / (32 kMT)) x 2 waves; wave (wm, wn) owns
-constexpr int kMT = 16 / kWaves, kNT = 2;        //   32 kMT rows x 64 columns (32 x 32 MFMA tiles)
-constexpr int kStages = BK == 64 ? 6 : 3;       // 144 KB of slots either way
+constexpr int kMT = BM / (16 * kWaves), kNT = 2; // (kWaves / 2) x 2 waves; wave (wm, wn) owns
+                                                 //   32 kMT rows x 64 columns (32 x 32 MFMA tiles)
 constexpr int kHalves = BK / 64;                 // 64-byte halves of a block (one mma_block each)
 constexpr int kASlot = BM * BK;                  // 16 KB
 constexpr int kBSlot = BN * BK;                  // 8 KB
@@ -350,8 +361,13 @@ __device__ inline void tile_of(int bid, int tm, int tn, int& mt, int& nt) {
 // The operands and sizes are separate scalars, first in the list, so that
 // they are preloaded into scalar registers at wave launch; the epilogue's
 // arguments follow, read from memory as usual (needed at the end).
+#ifdef QL_I8_SMALL_TILE
+#define QL_I8_KERNEL_ATTR __attribute__((amdgpu_waves_per_eu(2)))
+#else
+#define QL_I8_KERNEL_ATTR
+#endif
 template <bool OUT_BF16, bool FP8>
-__global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(const int8_t* A, const int8_t* B, int M, int N, int K,
+__global__ __launch_bounds__(64 * kWaves) QL_I8_KERNEL_ATTR void i8_gemm_kernel(const int8_t* A, const int8_t* B, int M, int N, int K,
                                                               int off32, I8Epi epi) {
   I8Args a;
   a.A = A;
@@ -418,7 +434,7 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(const int8_t* A, c
   // go through LDS (the operand slots are free now), a lane's columns through
   // registers.
   const I8Epi& e = a.e;
-  constexpr int kOutWave = (kMT * 32) * (kNT * 32) * 2;      // a wave's output tile in LDS: 16 KB
+  constexpr int kOutWave = (kMT * 32) * (kNT * 32) * 2;      // a wave's output tile in LDS
   constexpr int kRowParams = kWaves * kOutWave;              // row scales, then row zero points
   static_assert(kRowParams + BM * 8 <= kStages * kSlot, "epilogue staging fits in the slots");
   float* row_s = reinterpret_cast<float*>(g_lds + kRowParams);
@@ -540,7 +556,13 @@ __global__ __launch_bounds__(64 * kWaves) void i8_gemm_kernel(const int8_t* A, c
 
 }  // namespace
 
+#ifdef QL_I8_SMALL_TILE
+hipError_t launch_i8_gemm_small(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e,
+                                hipStream_t st) {
+#else
 hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
+  if (i8_small_grid(M, N)) return launch_i8_gemm_small(A, B, M, N, K, e, st);
+#endif
   I8Args a{A, B, M, N, K, e, (size_t)M * K <= 0xFFFFFFFFu && (size_t)N * K <= 0xFFFFFFFFu};
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (e.out_bf16)
@@ -552,7 +574,13 @@ hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K,
   return hipGetLastError();
 }
 
+#ifdef QL_I8_SMALL_TILE
+hipError_t launch_f8_gemm_small(const uint8_t* A, const uint8_t* B, int M, int N, int K, const I8Epi& e,
+                                hipStream_t st) {
+#else
 hipError_t launch_f8_gemm(const uint8_t* A, const uint8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
+  if (i8_small_grid(M, N)) return launch_f8_gemm_small(A, B, M, N, K, e, st);
+#endif
   I8Args a{reinterpret_cast<const int8_t*>(A), reinterpret_cast<const int8_t*>(B), M, N, K, e,
             (size_t)M * K <= 0xFFFFFFFFu && (size_t)N * K <= 0xFFFFFFFFu};
   a.e.azp = nullptr;

@@ -130,6 +130,17 @@ hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K,
 // FP8 (E4M3) operands with the same tiling; e.azp, e.azp_adj and e.raw must be null
 hipError_t launch_f8_gemm(const uint8_t* A, const uint8_t* B, int M, int N, int K,
                           const I8Epi& e, hipStream_t st);
+// the same GEMMs on 128 x 128 tiles (two workgroups per compute unit), which
+// launch_i8_gemm / launch_f8_gemm use when i8_small_grid(M, N)
+hipError_t launch_i8_gemm_small(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e,
+                                hipStream_t st);
+hipError_t launch_f8_gemm_small(const uint8_t* A, const uint8_t* B, int M, int N, int K, const I8Epi& e,
+                                hipStream_t st);
+// true when the 256 x 128 tiles of an M x N output would occupy at most half
+// of the 256 compute units
+inline bool i8_small_grid(int M, int N) {
+  return 2 * (long)((M + 255) / 256) * ((N + 127) / 128) <= 256;
+}
 
 // plain streaming read of `bytes` bytes (a multiple of 16): the achievable
 // HBM read rate; sink receives read_probe_sink_words(workgroups) words

@@ -95,7 +95,9 @@ def test_quant_extremes():
 
 # ---------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (5, 40, 48), (130, 72, 96), (256, 384, 512), (300, 260, 1040)])
+# 128 x 128 tiles on small grids (the first five), 256 x 128 tiles otherwise
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (5, 40, 48), (130, 72, 96), (256, 384, 512), (300, 260, 1040),
+                                   (2100, 2050, 1040)])
 def test_gemm_ragged(M, N, K):
     r = np.random.default_rng(M + N + K)
     Aq, s_a = of8.quant_per_token_fp8(r.standard_normal((M, K)).astype(np.float32))
@@ -104,10 +106,11 @@ def test_gemm_ragged(M, N, K):
     check_gemm(Aq, Bq, s_a, s_b, bias)
 
 
-def test_gemm_all_codes_and_epilogue_variants():
+@pytest.mark.parametrize("M,N", [(96, 136), (2100, 2050)])                 # 128 x 128 and 256 x 128 tiles
+def test_gemm_all_codes_and_epilogue_variants(M, N):
     """Random codes over the whole E4M3 range (subnormals, both signs), then
     per-tensor scales, no bias and a bf16 output."""
-    M, N, K = 96, 136, 256
+    K = 256
     r = np.random.default_rng(11)
     Aq, Bq = _codes(r, (M, K)), _codes(r, (N, K))
     # |D| can reach 448 * 448 * K (about 5e7): scales keep the output inside fp16
@@ -119,9 +122,10 @@ def test_gemm_all_codes_and_epilogue_variants():
     check_gemm(Aq, Bq, s_a, s_b, b16, out_dtype=torch.bfloat16)
 
 
-def test_gemm_extreme_codes():
+@pytest.mark.parametrize("M,N", [(64, 64), (2304, 2048)])                 # 128 x 128 and 256 x 128 tiles
+def test_gemm_extreme_codes(M, N):
     """All codes at +-448: D = -448 * 448 * K exactly (49 * 2**24 for K = 4096)."""
-    M, N, K = 64, 64, 4096
+    K = 4096
     Aq = np.full((M, K), 0x7E, np.uint8)
     Bq = np.full((N, K), 0xFE, np.uint8)
     s_a = np.full(M, 2.0 ** -20, np.float32)

@@ -123,15 +123,21 @@ def _operands(M, N, K, seed):
     return Aq, s_a, azp, Bq, s_b
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (5, 40, 48), (130, 72, 96), (256, 384, 512), (300, 260, 1040)])
+# the GEMM takes 128 x 128 tiles when 256 x 128 ones would fill at most half
+# the compute units (the first five shapes) and 256 x 128 tiles otherwise
+SMALL_AND_LARGE = [(1, 16, 16), (5, 40, 48), (130, 72, 96), (256, 384, 512), (300, 260, 1040), (2100, 2050, 1040),
+                   (4097, 1000, 528)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_AND_LARGE)
 def test_gemm_ragged(M, N, K):
     Aq, s_a, azp, Bq, s_b = _operands(M, N, K, M + N + K)
     bias = torch.from_numpy(np.random.default_rng(1).standard_normal(N).astype(np.float32) * 0.1).half()
     check_gemm(Aq, Bq, s_a, s_b, azp, ow8.azp_adj(Bq), bias)
 
 
-def test_gemm_epilogue_variants():
-    M, N, K = 96, 136, 256
+@pytest.mark.parametrize("M,N,K", [(96, 136, 256), (2100, 2050, 256)])    # 128 x 128 and 256 x 128 tiles
+def test_gemm_epilogue_variants(M, N, K):
     Aq, s_a, azp, Bq, s_b = _operands(M, N, K, 5)
     adj = ow8.azp_adj(Bq)
     check_gemm(Aq, Bq, s_a, s_b)                                   # symmetric, no bias
@@ -141,9 +147,10 @@ def test_gemm_epilogue_variants():
     check_gemm(Aq, Bq, s_a, s_b, azp, adj, b16, out_dtype=torch.bfloat16)
 
 
-def test_gemm_extreme_codes():
+@pytest.mark.parametrize("M,N", [(64, 64), (2304, 2048)])                 # 128 x 128 and 256 x 128 tiles
+def test_gemm_extreme_codes(M, N):
     """All codes at the int8 extremes: Dq reaches 128 * 127 * K exactly."""
-    M, N, K = 64, 64, 4096
+    K = 4096
     Aq = np.full((M, K), -128, np.int8)
     Bq = np.full((N, K), -127, np.int8)
     s_a = np.full(M, 1e-3, np.float32)
@@ -151,11 +158,12 @@ def test_gemm_extreme_codes():
     check_gemm(Aq, Bq, s_a, s_b)
 
 
-def test_gemm_wide_zero_points():
+@pytest.mark.parametrize("M,N", [(256, 256), (2048, 2304)])               # 128 x 128 and 256 x 128 tiles
+def test_gemm_wide_zero_points(M, N):
     """Zero points and column sums past 24 bits (the epilogue then forms
-    azp * azp_adj with a 32-bit multiply): still exact.  Full 256 x 128 tiles,
-    so the row-staged store path is the one checked without raw_out."""
-    M, N, K = 256, 256, 512
+    azp * azp_adj with a 32-bit multiply): still exact.  Full tiles of either
+    shape, so the row-staged store path is the one checked without raw_out."""
+    K = 512
     r = np.random.default_rng(11)
     Aq = r.integers(-128, 128, (M, K)).astype(np.int8)
     Bq = np.zeros((N, K), np.int8)
@@ -201,6 +209,34 @@ def test_gemm_operand_over_4gib():
         assert e <= TOL, f"relative error {e:.3e}"
         check_epilogue_bound(os_, C, s_a[rows], s_b, bias, out64, torch.float16)
     del Aq, raw, out, out_fast
+    torch.cuda.empty_cache()
+
+
+def test_gemm_small_tiles_operand_over_4gib():
+    """The 128 x 128 tiles with Aq past 4 GiB (a few rows of a very long K,
+    ragged against the 64-byte blocks): 64-bit row addresses in that tile's
+    main loop too.  Sampled rows against the oracle, as above."""
+    M, N, K = 259, 16, (1 << 24) + 48
+    assert M * K > 0xFFFFFFFF
+    g = torch.Generator(device="cuda").manual_seed(13)
+    Aq = torch.randint(-128, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+    r = np.random.default_rng(14)
+    Bq = r.integers(-127, 128, (N, K)).astype(np.int8)
+    s_a = (r.random(M) * 0.01 + 1e-3).astype(np.float32)
+    s_b = (r.random(N) * 1e-4 + 1e-5).astype(np.float32)
+    azp = r.integers(-128, 128, M).astype(np.int32)
+    adj = ow8.azp_adj(Bq)
+    args = (Aq, cu(Bq), cu(s_a), cu(s_b), cu(azp), cu(adj), None)
+    out, raw = ql.i8_gemm_scaled(*args, raw=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 200, M - 1])
+    ri = torch.from_numpy(rows).cuda()
+    C, out64 = ow8.w8a8_linear(Aq.index_select(0, ri).cpu().numpy(), Bq, s_a[rows], s_b, azp[rows], adj)
+    assert np.array_equal(raw.index_select(0, ri).cpu().numpy().astype(np.int64), C)
+    os_ = out.index_select(0, ri)
+    assert float(np.abs(wl.as_f64(os_.cpu()) - out64).max() / np.abs(out64).max()) <= TOL
+    check_epilogue_bound(os_, C, s_a[rows], s_b, None, out64, torch.float16)
+    del Aq, raw, out
     torch.cuda.empty_cache()
 
 
