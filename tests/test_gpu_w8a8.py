@@ -124,9 +124,10 @@ def _operands(M, N, K, seed):
 
 
 # the GEMM takes 128 x 128 tiles when 256 x 128 ones would fill at most half
-# the compute units (the first five shapes) and 256 x 128 tiles otherwise
+# the compute units (the first five shapes, and 1024 x 4096: exactly 128 of
+# them) and 256 x 128 tiles otherwise (1025 x 4096: 160)
 SMALL_AND_LARGE = [(1, 16, 16), (5, 40, 48), (130, 72, 96), (256, 384, 512), (300, 260, 1040), (2100, 2050, 1040),
-                   (4097, 1000, 528)]
+                   (4097, 1000, 528), (1024, 4096, 272), (1025, 4096, 272)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL_AND_LARGE)
