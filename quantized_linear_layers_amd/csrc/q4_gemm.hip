@@ -575,7 +575,7 @@ __global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(const uint4* W,
   // ---- store: acc element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32; with a K split the fp32 partial tile goes to the split's
   // slice of P instead (added and rounded by splitk_reduce_kernel)
-  float* part = a.P ? a.P + (size_t)blockIdx.y * a.M * a.ldy : nullptr;
+  float* part = a.P ? a.P + (size_t)blockIdx.y * splitk_slice((size_t)a.M * a.ldy) : nullptr;
 #pragma unroll
   for (int t = 0; t < kNTW; ++t) {
     const int n = nw0 + 32 * t + l32;
@@ -598,8 +598,9 @@ __global__ __launch_bounds__(64 * C::kWaves) void q4_gemm_kernel(const uint4* W,
 }
 
 // Y = the 16-bit rounding of the sum of the S fp32 partial results P[s]
-// (split s of K), added in split order: 4 consecutive elements per thread,
-// the last partial group element by element.
+// (split s of K, at P + s * splitk_slice(MN): every slice 16-byte aligned),
+// added in split order: 4 consecutive elements per thread, the last partial
+// group element by element.
 // Adds the S partial tiles in split order and rounds once.  S is a template
 // argument so that a thread issues all S loads of its four elements before
 // the first addition (with S a loop bound, each addition waited for its
@@ -610,13 +611,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             uint16_t* __restrict__ Y) {
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= MN) return;
+  const size_t slice = splitk_slice(MN);
   auto cvt = [](float v) {
     return BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
   };
   if (i + 4 <= MN) {
     float4 v[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) v[s] = *reinterpret_cast<const float4*>(P + (size_t)s * MN + i);
+    for (int s = 0; s < S; ++s) v[s] = *reinterpret_cast<const float4*>(P + (size_t)s * slice + i);
     float4 acc = v[0];
 #pragma unroll
     for (int s = 1; s < S; ++s) {
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   } else {
     for (size_t j = i; j < MN; ++j) {
       float acc = P[j];
-      for (int s = 1; s < S; ++s) acc += P[(size_t)s * MN + j];
+      for (int s = 1; s < S; ++s) acc += P[(size_t)s * slice + j];
       Y[j] = cvt(acc);
     }
   }
@@ -746,7 +748,7 @@ GemmPlan plan_q4_gemm(int M, int N, int K, int max_splits) {
 }
 
 size_t gemm_workspace_bytes(const GemmPlan& p, int M, int N) {
-  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+  return p.splits > 1 ? (size_t)p.splits * splitk_slice((size_t)M * N) * sizeof(float) : 0;
 }
 
 void gemm_tile_shape(const GemmPlan& p, int* rows, int* cols) {

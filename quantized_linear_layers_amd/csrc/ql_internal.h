@@ -90,6 +90,10 @@ struct GemmPlan {
 };
 GemmPlan plan_q4_gemm(int M, int N, int K, int max_splits);
 size_t gemm_workspace_bytes(const GemmPlan& p, int M, int N);
+// elements between consecutive K-split slices of the workspace: M * N rounded
+// up to a multiple of 4, so that every slice starts 16-byte aligned (the
+// reduction reads four elements at a time)
+__host__ __device__ inline size_t splitk_slice(size_t MN) { return (MN + 3) & ~(size_t)3; }
 void gemm_tile_shape(const GemmPlan& p, int* rows, int* cols);
 // token counts served by the decode-family kernel; larger M takes the GEMM
 constexpr int kGemvMaxM = 16;

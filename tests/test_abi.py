@@ -358,8 +358,10 @@ def test_q4_gemm_tile_shape():
 
 def test_q4_gemm_workspace_plan():
     """The K split: only with M > 16 (and never for prefill-sized M), the
-    workspace is splits x M x N fp32, and a given workspace that is too small
-    is rejected before any launch (no workspace: the layer runs unsplit)."""
+    workspace is `splits` fp32 slices of M x N, each rounded up to a multiple
+    of 4 elements (so that every slice starts 16-byte aligned), and a given
+    workspace that is too small is rejected before any launch (no workspace:
+    the layer runs unsplit)."""
     assert ql.q4_gemm_workspace_bytes(16, 4096, 4096) == 0
     assert ql.q4_gemm_workspace_bytes(4096, 14336, 4096) == 0
     assert ql.q4_gemm_plan(4096, 14336, 4096)[2] == 1
@@ -368,11 +370,14 @@ def test_q4_gemm_workspace_plan():
         for (K, N) in ((4096, 4096), (4096, 11008), (11008, 4096), (28672, 8192)):
             rows, cols, S = ql.q4_gemm_plan(M, N, K)
             ws = ql.q4_gemm_workspace_bytes(M, N, K)
-            assert ws == (S * M * N * 4 if S > 1 else 0)
+            assert ws == (S * ((M * N + 3) // 4 * 4) * 4 if S > 1 else 0)
             assert S == 1 or M <= 512
             split_seen |= S > 1
     assert split_seen
     assert ql.q4_gemm_workspace_bytes(32, 4096, 100) == 0           # invalid K
+    M, N, K = 129, 7, 4096                                          # M * N = 903: padded slices
+    S = ql.q4_gemm_plan(M, N, K)[2]
+    assert S > 1 and ql.q4_gemm_workspace_bytes(M, N, K) == S * 904 * 4
     L = ql.lib()
     M, N, K = next((M, N, K) for M in (32, 64) for (K, N) in ((11008, 4096), (28672, 8192))
                    if ql.q4_gemm_workspace_bytes(M, N, K))
