@@ -36,6 +36,7 @@ SOURCES = {
     "i8_quant.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-kernarg-preload-count=8"],
     "i8_gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=6"],
     "i8_gemm_small.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=6"],
+    "i8_gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=5"],
     "act_order.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
     "read_probe.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
 }

@@ -140,6 +140,11 @@ hipError_t launch_i8_gemm_small(const int8_t* A, const int8_t* B, int M, int N, 
                                 hipStream_t st);
 hipError_t launch_f8_gemm_small(const uint8_t* A, const uint8_t* B, int M, int N, int K, const I8Epi& e,
                                 hipStream_t st);
+// the same products for M <= kGemvMaxM tokens: a workgroup streams 16 or 32
+// output channels' weights for all of K (fp8: E4M3 codes, e.azp, e.azp_adj
+// and e.raw null); launch_i8_gemm / launch_f8_gemm use it for such M
+hipError_t launch_i8_gemv(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, bool fp8,
+                          hipStream_t st);
 // true when the 256 x 128 tiles of an M x N output would occupy at most half
 // of the 256 compute units
 inline bool i8_small_grid(int M, int N) {

@@ -106,6 +106,28 @@ def test_gemm_ragged(M, N, K):
     check_gemm(Aq, Bq, s_a, s_b, bias)
 
 
+# M <= 16: the decode kernel (one 128-byte group per MFMA, fp32 sums added
+# across the waves in wave order)
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (1, 4096, 4096), (5, 100, 1040), (8, 8200, 528), (16, 4096, 4112),
+                                   (12, 1, 272), (13, 12000, 2064), (8, 16400, 272), (16, 28672, 400)])
+def test_gemm_decode(M, N, K):
+    r = np.random.default_rng(3 * M + N + K)
+    Aq, s_a = of8.quant_per_token_fp8(r.standard_normal((M, K)).astype(np.float32))
+    Bq, s_b = of8.quant_weight_per_channel_fp8((r.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bias = torch.from_numpy(r.standard_normal(N).astype(np.float32) * 0.1).half()
+    check_gemm(Aq, Bq, s_a, s_b, bias)
+    check_gemm(Aq, Bq, s_a[:1], s_b[:1], None, out_dtype=torch.bfloat16)
+
+
+def test_gemm_decode_all_codes():
+    """Every E4M3 code on both sides (random over the whole finite range) with
+    few tokens."""
+    r = np.random.default_rng(21)
+    M, N, K = 16, 300, 2048
+    Aq, Bq = _codes(r, (M, K)), _codes(r, (N, K))
+    check_gemm(Aq, Bq, np.full(M, 1e-3, np.float32), np.full(N, 1e-3, np.float32))
+
+
 @pytest.mark.parametrize("M,N", [(96, 136), (2100, 2050)])                 # 128 x 128 and 256 x 128 tiles
 def test_gemm_all_codes_and_epilogue_variants(M, N):
     """Random codes over the whole E4M3 range (subnormals, both signs), then

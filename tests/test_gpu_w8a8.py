@@ -137,6 +137,41 @@ def test_gemm_ragged(M, N, K):
     check_gemm(Aq, Bq, s_a, s_b, azp, ow8.azp_adj(Bq), bias)
 
 
+# M <= 16 takes the decode kernel: 16, 32 or 64 output channels per
+# workgroup, K in 128-byte groups split among 8 or 4 waves, rings of 3 or 2
+# slots (ragged K, K shorter than the waves, N not a multiple of 16, 8 or 16
+# staged activation rows; 12000 columns: 4 waves, 16400: 64 channels per
+# workgroup, 28672: 64 channels and 2 slots)
+DECODE = [(1, 16, 16), (1, 4096, 4096), (3, 100, 1040), (8, 8200, 528), (9, 1000, 4112), (16, 4096, 4096),
+          (16, 8192, 1024), (2, 17, 48), (13, 12000, 2064), (16, 1, 272), (8, 16400, 272), (16, 28672, 400)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE)
+def test_gemm_decode(M, N, K):
+    Aq, s_a, azp, Bq, s_b = _operands(M, N, K, 7 * M + N + K)
+    bias = torch.from_numpy(np.random.default_rng(2).standard_normal(N).astype(np.float32) * 0.1).half()
+    check_gemm(Aq, Bq, s_a, s_b, azp, ow8.azp_adj(Bq), bias)
+
+
+def test_gemm_decode_variants_and_extremes():
+    """The decode kernel's epilogue variants, all codes at the int8 extremes
+    (Dq = 128 * 127 * K exactly), and zero points past 24 bits."""
+    M, N, K = 11, 520, 4096
+    Aq, s_a, azp, Bq, s_b = _operands(M, N, K, 8)
+    adj = ow8.azp_adj(Bq)
+    check_gemm(Aq, Bq, s_a, s_b)
+    check_gemm(Aq, Bq, s_a[:1], s_b[:1], None, (5 * adj).astype(np.int32))
+    b16 = torch.from_numpy(np.linspace(-1, 1, N).astype(np.float32)).to(torch.bfloat16)
+    check_gemm(Aq, Bq, s_a, s_b, azp, adj, b16, out_dtype=torch.bfloat16)
+    check_gemm(np.full((M, K), -128, np.int8), np.full((N, K), -127, np.int8), np.full(M, 1e-3, np.float32),
+               np.full(N, 1e-4, np.float32))
+    r = np.random.default_rng(9)
+    wide = (r.integers(-1, 2, M) * ((1 << 23) + r.integers(0, 1 << 20, M))).astype(np.int32)
+    Bz = np.zeros((N, K), np.int8)
+    Bz[:, :3] = r.integers(-1, 2, (N, 3))
+    check_gemm(Aq, Bz, np.full(M, 1e-6, np.float32), np.full(N, 1e-2, np.float32), wide, ow8.azp_adj(Bz))
+
+
 @pytest.mark.parametrize("M,N,K", [(96, 136, 256), (2100, 2050, 256)])    # 128 x 128 and 256 x 128 tiles
 def test_gemm_epilogue_variants(M, N, K):
     Aq, s_a, azp, Bq, s_b = _operands(M, N, K, 5)
