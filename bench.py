@@ -311,6 +311,55 @@ def bench_f8(ql, reps):
             "quant_us": round(tq * 1e3, 2), "end_to_end_us": round((tq + tg) * 1e3, 2)}
 
 
+def w8a8_bytes(M, K, N):
+    """Algorithmic bytes of one W8A8 layer: the weight codes, the activation
+    codes, per-channel fp32 scales, int32 column sums and fp16 bias, per-token
+    fp32 scales and int32 zero points, and the fp16 output."""
+    return N * K + M * K + N * (4 + 4 + 2) + M * (4 + 4) + M * N * 2
+
+
+def bench_w8a8_decode(ql, reps):
+    """W8A8 with few tokens (the decode kernel) on the Llama-2-70B layer
+    shapes and token counts of the headline workload, int8 and FP8 codes from
+    the same fp32 weights, weight copies rotated over more than the last-level
+    cache.  Beside each layer: the plain read of its weight bytes."""
+    w = wl.WORKLOADS["decode_70b"]
+    st = torch.cuda.current_stream()
+    bias = wl.bias(wl.WORKLOADS["w8a8_prefill"], max(N for _, N in w.shapes))
+    per_case = {}
+    for (K, N) in w.shapes:
+        W = torch.from_numpy(_weight(w, K, N))
+        Bq, s_b = ql.i8_quant_weight_host(W)
+        adj = ql.i8_azp_adj(Bq).cuda()
+        B8, s_b8 = ql.f8_quant_weight_host(W)
+        R = _copies_for(N * K)
+        Bqs = [Bq.cuda() for _ in range(R)]
+        B8s = [B8.cuda() for _ in range(R)]
+        del W, Bq, B8
+        s_b, s_b8, b = s_b.cuda(), s_b8.cuda(), bias[:N].cuda()
+        probes = {p: [ql.read_probe_launcher(x, p[1], p[0]) for x in Bqs] for p in READ_PROBES}
+        read_ms = min(time_launches([lambda i, f=f: f[i % R]()], max(reps, 2 * R), st)[0] for f in probes.values())
+        for M in w.Ms:
+            X = wl.activations(w, M, K, N).cuda()
+            Aq, s_a, azp = ql.i8_quant_per_token(X)
+            A8, s_a8 = ql.f8_quant_per_token(X)
+            out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            li = [ql.launcher("i8_gemm_scaled", Aq, x, M, N, K, s_a, M, s_b, N, azp, adj, b, out, torch.float16, None)
+                  for x in Bqs]
+            lf = [ql.launcher("f8_gemm_scaled", A8, x, M, N, K, s_a8, M, s_b8, N, b, out, torch.float16) for x in B8s]
+            ti, tf = time_launches([lambda r: li[r % R](), lambda r: lf[r % R]()], max(reps, R), st)
+            nb = w8a8_bytes(M, K, N)
+            per_case[f"{M}x{K}x{N}"] = {
+                "int8_us": round(ti * 1e3, 2), "int8_GBps": round(nb / (ti * 1e-3) / 1e9, 1),
+                "int8_frac_hbm": round(nb / (ti * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "fp8_us": round(tf * 1e3, 2), "fp8_GBps": round(nb / (tf * 1e-3) / 1e9, 1),
+                "fp8_frac_hbm": round(nb / (tf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "read_us": round(read_ms * 1e3, 2),
+                "int8_frac_of_read": round(read_ms / ti, 4), "fp8_frac_of_read": round(read_ms / tf, 4)}
+        del Bqs, B8s, probes
+    return {"workload": "Llama-2-70B-shaped decode layers (M = 1, 8), W8A8 int8 and FP8 codes", "per_case": per_case}
+
+
 def bench_w4_prefill(ql, reps):
     w = wl.WORKLOADS["w4a16_prefill"]
     M, (K, N) = w.Ms[0], w.shapes[0]
@@ -493,8 +542,8 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for byte counters)")
     ap.add_argument("--also-only", default="", metavar="NAMES",
-                    help="run only these extra workloads (comma-separated: decode_7b, w8a8, fp8, prefill, mid_m, "
-                         "libref)")
+                    help="run only these extra workloads (comma-separated: decode_7b, w8a8, fp8, w8a8_decode, "
+                         "prefill, mid_m, libref)")
     args = ap.parse_args()
     WARM_MS = args.warm_ms
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -515,7 +564,8 @@ def main():
         print(f"# decode_70b read ceiling: {main_res['read_ceiling_step']}", flush=True)
         print(f"# decode_70b per case: {main_res['per_case']}", flush=True)
     also = {}
-    want = set(filter(None, args.also_only.split(","))) or {"decode_7b", "w8a8", "fp8", "prefill", "mid_m", "libref"}
+    want = set(filter(None, args.also_only.split(","))) or {"decode_7b", "w8a8", "fp8", "w8a8_decode", "prefill",
+                                                            "mid_m", "libref"}
     if not args.no_also:
         if "decode_7b" in want:
             r7 = bench_decode(ql, "decode_7b", args.steps, args.warmup)
@@ -531,6 +581,9 @@ def main():
         if "fp8" in want:
             also["w8a8_fp8_prefill"] = bench_f8(ql, 50)
             print(f"# w8a8 fp8: {also['w8a8_fp8_prefill']}", flush=True)
+        if "w8a8_decode" in want:
+            also["w8a8_decode"] = bench_w8a8_decode(ql, 50)
+            print(f"# w8a8 decode: {also['w8a8_decode']}", flush=True)
         if "prefill" in want:
             also["w4a16_prefill"] = bench_w4_prefill(ql, 20)
             print(f"# w4a16 prefill: {also['w4a16_prefill']}", flush=True)
