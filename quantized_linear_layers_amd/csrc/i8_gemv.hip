@@ -12,11 +12,11 @@
 // kernel rather than like the tiled GEMM, whose 128-row tiles would leave
 // 7/8 of each tile and most compute units idle:
 //   * a workgroup owns 16 NT output channels for the whole of K (no partial
-//     sums leave it), NT the widest of 1, 2 or 4 that still gives every
-//     compute unit a workgroup;
-//   * its 8 (or 4) waves split K in groups of 128 bytes (one 128-byte line
-//     per row); each wave streams its groups through a ring of 3 (or 2) LDS
-//     slots filled by global_load_lds two groups (one) ahead: per group the 16 (or 8, for M <= 8)
+//     sums leave it), NT = 1 up to N = 16384 (more, smaller workgroups
+//     stream best), 2 or 4 beyond;
+//   * its 4 waves split K in groups of 128 bytes (one 128-byte line per row);
+//     each wave streams its groups through a ring of 3 LDS slots filled by
+//     global_load_lds two groups ahead: per group the 16 (or 8, for M <= 8)
 //     activation rows and the NT 16-channel weight blocks, 1 KB per copy
 //     instruction, full lines, the weights marked non-temporal;
 //   * rows are stored with their 16-byte pieces XOR-swizzled by row bits 1..3,
@@ -290,59 +290,40 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
   }
 }
 
-// The plan, as for the W4A16 decode kernel: the widest of 1, 2 or 4 slices
-// per workgroup that still gives every compute unit a workgroup; eight waves
-// with one or two slices, four with four; and where the workgroups would not
-// all be resident at once, four waves, then a ring of two slots.
-struct GvPlan {
-  int nt, waves, depth;
-};
-GvPlan plan_gv(int M, int N) {
-  constexpr int kCUs = 256, kLdsPerCU = 160 * 1024;
-  const int slices = (N + 15) / 16, mx = M <= 8 ? 1 : 2;
-  GvPlan p;
-  p.nt = slices / 4 >= kCUs ? 4 : slices / 2 >= kCUs ? 2 : 1;
-  p.waves = p.nt == 4 ? 4 : 8;
-  p.depth = 3;
-  auto resident = [&](const GvPlan& q) {
-    return (long)((slices + q.nt - 1) / q.nt) <= (long)kCUs * (kLdsPerCU / gv_lds_bytes(q.nt, mx, q.waves, q.depth));
-  };
-  if (!resident(p)) p.waves = 4;
-  if (!resident(p)) p.depth = 2;
-  return p;
+// The plan: one 16-channel slice per workgroup up to 1024 slices (N up to
+// 16384), then two, then four; four waves, three slots (48 KB of LDS for
+// one slice: three workgroups per compute unit).  Measured against
+// every (slices, waves, slots) combination on the 7B and 70B layer shapes at
+// 1, 8 and 16 tokens (weights from HBM): more, smaller workgroups beat the
+// W4A16 kernel's rule here (8192 x 8192: 16.4 -> 12.3 us for one token with
+// one slice on four waves instead of two slices on eight), since a group's
+// weight block is 2 KB per slice instead of 1 KB.
+constexpr int kGvWaves = 4, kGvDepth = 3;
+int plan_gv_slices(int N) {
+  const int slices = (N + 15) / 16;
+  return slices <= 1024 ? 1 : slices <= 2048 ? 2 : 4;
 }
 
 template <bool FP8, bool OUT_BF16, int NT, int MX>
-hipError_t launch_mx(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, const GvPlan& p,
-                     hipStream_t st) {
+hipError_t launch_mx(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
   const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)));
-  if constexpr (gv_lds_bytes(NT, MX, 8, 3) <= 160 * 1024) {
-    if (p.waves == 8) {
-      hipLaunchKernelGGL((i8_gemv_kernel<FP8, OUT_BF16, NT, MX, 8, 3>), grid, dim3(512), 0, st, A, B, M, N, K, e);
-      return hipGetLastError();
-    }
-  }
-  if (p.depth == 3)
-    hipLaunchKernelGGL((i8_gemv_kernel<FP8, OUT_BF16, NT, MX, 4, 3>), grid, dim3(256), 0, st, A, B, M, N, K, e);
-  else
-    hipLaunchKernelGGL((i8_gemv_kernel<FP8, OUT_BF16, NT, MX, 4, 2>), grid, dim3(256), 0, st, A, B, M, N, K, e);
+  hipLaunchKernelGGL((i8_gemv_kernel<FP8, OUT_BF16, NT, MX, kGvWaves, kGvDepth>), grid, dim3(64 * kGvWaves), 0, st, A,
+                     B, M, N, K, e);
   return hipGetLastError();
 }
 
 template <bool FP8, bool OUT_BF16, int NT>
-hipError_t launch_nt(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, const GvPlan& p,
-                     hipStream_t st) {
-  return M <= 8 ? launch_mx<FP8, OUT_BF16, NT, 1>(A, B, M, N, K, e, p, st)
-                : launch_mx<FP8, OUT_BF16, NT, 2>(A, B, M, N, K, e, p, st);
+hipError_t launch_nt(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
+  return M <= 8 ? launch_mx<FP8, OUT_BF16, NT, 1>(A, B, M, N, K, e, st)
+                : launch_mx<FP8, OUT_BF16, NT, 2>(A, B, M, N, K, e, st);
 }
 
 template <bool FP8, bool OUT_BF16>
 hipError_t launch_out(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
-  const GvPlan p = plan_gv(M, N);
-  switch (p.nt) {
-    case 4: return launch_nt<FP8, OUT_BF16, 4>(A, B, M, N, K, e, p, st);
-    case 2: return launch_nt<FP8, OUT_BF16, 2>(A, B, M, N, K, e, p, st);
-    default: return launch_nt<FP8, OUT_BF16, 1>(A, B, M, N, K, e, p, st);
+  switch (plan_gv_slices(N)) {
+    case 4: return launch_nt<FP8, OUT_BF16, 4>(A, B, M, N, K, e, st);
+    case 2: return launch_nt<FP8, OUT_BF16, 2>(A, B, M, N, K, e, st);
+    default: return launch_nt<FP8, OUT_BF16, 1>(A, B, M, N, K, e, st);
   }
 }
 

@@ -137,13 +137,13 @@ def test_gemm_ragged(M, N, K):
     check_gemm(Aq, Bq, s_a, s_b, azp, ow8.azp_adj(Bq), bias)
 
 
-# M <= 16 takes the decode kernel: 16, 32 or 64 output channels per
-# workgroup, K in 128-byte groups split among 8 or 4 waves, rings of 3 or 2
-# slots (ragged K, K shorter than the waves, N not a multiple of 16, 8 or 16
-# staged activation rows; 12000 columns: 4 waves, 16400: 64 channels per
-# workgroup, 28672: 64 channels and 2 slots)
+# M <= 16 takes the decode kernel: 16 output channels per workgroup up to
+# N = 16384, 32 up to 32768, 64 beyond (16400, 28672 and 33000 columns), K in
+# 128-byte groups split among 4 waves (ragged K, K shorter than the waves, N
+# not a multiple of 16, 8 or 16 staged activation rows)
 DECODE = [(1, 16, 16), (1, 4096, 4096), (3, 100, 1040), (8, 8200, 528), (9, 1000, 4112), (16, 4096, 4096),
-          (16, 8192, 1024), (2, 17, 48), (13, 12000, 2064), (16, 1, 272), (8, 16400, 272), (16, 28672, 400)]
+          (16, 8192, 1024), (2, 17, 48), (13, 12000, 2064), (16, 1, 272), (8, 16400, 272), (16, 28672, 400),
+          (2, 33000, 144)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE)
