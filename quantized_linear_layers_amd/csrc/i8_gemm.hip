@@ -561,7 +561,7 @@ hipError_t launch_i8_gemm_small(const int8_t* A, const int8_t* B, int M, int N, 
                                 hipStream_t st) {
 #else
 hipError_t launch_i8_gemm(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
-  if (M <= kGemvMaxM) return launch_i8_gemv(A, B, M, N, K, e, false, st);
+  if (i8_gemv_serves(M, N)) return launch_i8_gemv(A, B, M, N, K, e, false, st);
   if (i8_small_grid(M, N)) return launch_i8_gemm_small(A, B, M, N, K, e, st);
 #endif
   I8Args a{A, B, M, N, K, e, (size_t)M * K <= 0xFFFFFFFFu && (size_t)N * K <= 0xFFFFFFFFu};
@@ -580,7 +580,7 @@ hipError_t launch_f8_gemm_small(const uint8_t* A, const uint8_t* B, int M, int N
                                 hipStream_t st) {
 #else
 hipError_t launch_f8_gemm(const uint8_t* A, const uint8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
-  if (M <= kGemvMaxM) {
+  if (i8_gemv_serves(M, N)) {
     I8Epi f = e;
     f.azp = nullptr;
     f.azp_adj = nullptr;

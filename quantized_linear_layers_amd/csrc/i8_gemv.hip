@@ -1,5 +1,5 @@
-// W8A8 decode kernel (M <= 16): the GEMM and fused epilogue of
-// i8_gemm_scaled / f8_gemm_scaled for a few tokens,
+// W8A8 decode kernel (few tokens: see i8_gemv_serves): the GEMM and fused
+// epilogue of i8_gemm_scaled / f8_gemm_scaled for a few tokens,
 //   C[m][n]   = sum_k Aq[m][k] Bq[n][k] - azp[m] azp_adj[n]      (int32, exact)
 //   out[m][n] = s_a[m] (s_b[n] C[m][n]) + bias[n]
 // ([LQ] W8A8 section; [VE] "2.4" for the zero-point term, [VE] "一、背景" for
@@ -16,13 +16,14 @@
 //     stream best), 2 or 4 beyond;
 //   * its 4 waves split K in groups of 128 bytes (one 128-byte line per row);
 //     each wave streams its groups through a ring of 3 LDS slots filled by
-//     global_load_lds two groups ahead: per group the 16 (or 8, for M <= 8)
-//     activation rows and the NT 16-channel weight blocks, 1 KB per copy
-//     instruction, full lines, the weights marked non-temporal;
+//     global_load_lds two groups ahead: per group the activation rows (8,
+//     16, 32 or 64: the fewest that hold M) and the NT 16-channel weight
+//     blocks, 1 KB per copy instruction, full lines, the weights marked
+//     non-temporal;
 //   * rows are stored with their 16-byte pieces XOR-swizzled by row bits 1..3,
 //     so that the 16 rows one fragment read serves fall on distinct banks;
-//   * products on v_mfma_i32_16x16x64_i8 (two per group and slice) or
-//     v_mfma_f32_16x16x128_f8f6f4 (one), one row per token;
+//   * products on v_mfma_i32_16x16x64_i8 (two per group, slice and block of
+//     16 rows) or v_mfma_f32_16x16x128_f8f6f4 (one), one row per token;
 //   * the waves' 16 x 16 tiles are added in LDS in wave order, and the first
 //     wave applies the epilogue and stores.
 #include <hip/hip_runtime.h>
@@ -117,7 +118,8 @@ __device__ inline void gv_for(F&& f) {
 constexpr int gv_lds_bytes(int NT, int MX, int W, int D) { return W * D * (MX * 1024 + NT * 2048); }
 
 // NT: 16-channel slices per workgroup; MX: 1 KB activation copies per group
-// (1: rows 0..7, for M <= 8; 2: rows 0..15); W: waves (they split K); D:
+// (8 MX rows; MX = 1: rows 0..7 for M <= 8, else 16 MX / 2 rows in MX / 2
+// blocks of 16 for the products); W: waves (they split K); D:
 // ring slots per wave (D - 1 groups in flight while one is multiplied).
 // Rows past M repeat row M - 1 and channels past N repeat channel N - 1
 // (valid loads whose products only reach outputs that are never stored).
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
   constexpr int L = SL::kLoads;
   static_assert(gv_lds_bytes(NT, MX, W, D) <= 160 * 1024, "LDS per workgroup");
   constexpr int kWaveBytes = D * SL::kBytes;
-  static_assert(kWaveBytes >= NT * 64 * 16, "the reduction reuses a wave's ring");
+  static_assert(kWaveBytes >= NT * (MX == 1 ? 1 : MX / 2) * 64 * 16, "the reduction reuses a wave's ring");
   __shared__ __align__(1024) int8_t lds_all[W * kWaveBytes];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -140,6 +142,7 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
 
   // this lane's copies: row (lane / 8) + 8 j of each 1 KB block, logical
   // piece (lane % 8) ^ key(row) into stored piece lane % 8
+  constexpr int MR = MX == 1 ? 1 : MX / 2;       // 16-row blocks of products
   const int crow = lane >> 3;
   const int8_t* xsrc[MX];
   int xp16[MX];
@@ -176,25 +179,29 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
   const uint32_t rbase = (uint32_t)(uintptr_t)(lds_ptr)ring;
   const int fr = lane & 15, lg = lane >> 4;
   const int xr = MX == 1 ? (fr & 7) : fr;
-  uint32_t xa[2], wa[2];
+  uint32_t xa[MR][2], wa[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int p = FP8 ? 2 * lg + s : 4 * s + lg;
-    xa[s] = rbase + SL::kX + gv_swz(xr, p);
+#pragma unroll
+    for (int rb = 0; rb < MR; ++rb) xa[rb][s] = rbase + SL::kX + gv_swz(xr + 16 * rb, p);
     wa[s] = rbase + SL::kW + gv_swz(fr, p);
   }
 
-  GvAcc<FP8> acc[NT];
+  GvAcc<FP8> acc[NT][MR];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = GvAcc<FP8>{0, 0, 0, 0};
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int rb = 0; rb < MR; ++rb) acc[t][rb] = GvAcc<FP8>{0, 0, 0, 0};
 
   auto compute = [&](int g, auto SLOT) {
     constexpr int so = decltype(SLOT)::value * SL::kBytes;
-    const int fence = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, acc[NT - 1][0]));
-    i32x4 xf[2], wf[NT][2];
+    const int fence = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, acc[NT - 1][MR - 1][0]));
+    i32x4 xf[MR][2], wf[NT][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      xf[s] = gv_read16<so>(xa[s], fence);
+#pragma unroll
+      for (int rb = 0; rb < MR; ++rb) xf[rb][s] = gv_read16<so>(xa[rb][s], fence);
       gv_for<0, NT>([&](auto T) { wf[T][s] = gv_read16<so + decltype(T)::value * 2048>(wa[s], fence); });
     }
     gv_lds_wait();
@@ -203,24 +210,29 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
     const int kg = g * kGrp;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      gv_after_wait(xf[s]);
       const int p = FP8 ? 2 * lg + s : 4 * s + lg;
-      if (kg + 16 * p >= K) xf[s] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int rb = 0; rb < MR; ++rb) {
+        gv_after_wait(xf[rb][s]);
+        if (kg + 16 * p >= K) xf[rb][s] = i32x4{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) gv_after_wait(wf[t][s]);
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if constexpr (FP8) {
-        const i32x8 a8 = __builtin_shufflevector(xf[0], xf[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        const i32x8 b8 = __builtin_shufflevector(wf[t][0], wf[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
-        // format codes 0, 0: both operands FP8 E4M3; no block scales
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t], 0, 0, 0, 0, 0, 0);
-      } else {
-        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[0], wf[t][0], acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[1], wf[t][1], acc[t], 0, 0, 0);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int rb = 0; rb < MR; ++rb) {
+        if constexpr (FP8) {
+          const i32x8 a8 = __builtin_shufflevector(xf[rb][0], xf[rb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const i32x8 b8 = __builtin_shufflevector(wf[t][0], wf[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          // format codes 0, 0: both operands FP8 E4M3; no block scales
+          acc[t][rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[t][rb], 0, 0, 0, 0, 0, 0);
+        } else {
+          acc[t][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[rb][0], wf[t][0], acc[t][rb], 0, 0, 0);
+          acc[t][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[rb][1], wf[t][1], acc[t][rb], 0, 0, 0);
+        }
       }
-    }
   };
 
   // prologue: groups g0 .. g0 + D - 2 in flight (those inside the range)
@@ -252,12 +264,17 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
   // ---- add the waves' tiles (each in its own ring) in wave order
   GvAcc<FP8>* red = reinterpret_cast<GvAcc<FP8>*>(ring);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) red[t * 64 + lane] = acc[t];
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int rb = 0; rb < MR; ++rb) red[(t * MR + rb) * 64 + lane] = acc[t][rb];
   __syncthreads();
   if (wave != 0) return;
   for (int w = 1; w < W; ++w)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] += reinterpret_cast<const GvAcc<FP8>*>(lds_all + w * kWaveBytes)[t * 64 + lane];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int rb = 0; rb < MR; ++rb)
+        acc[t][rb] += reinterpret_cast<const GvAcc<FP8>*>(lds_all + w * kWaveBytes)[(t * MR + rb) * 64 + lane];
 
   // ---- epilogue: lane l holds column l % 16 of each slice, rows 4 (l / 16) + i
 #pragma unroll
@@ -272,14 +289,16 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
       b = OUT_BF16 ? __builtin_bit_cast(float, (uint32_t)bb << 16) : (float)__builtin_bit_cast(_Float16, bb);
     }
 #pragma unroll
+    for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = 4 * lg + i;
+      const int m = 16 * rb + 4 * lg + i;
       if (m >= M) continue;
       float c;
       if constexpr (FP8) {
-        c = acc[t][i];
+        c = acc[t][rb][i];
       } else {
-        const int32_t ci = acc[t][i] - (e.azp ? e.azp[m] * adj : adj);
+        const int32_t ci = acc[t][rb][i] - (e.azp ? e.azp[m] * adj : adj);
         if (e.raw) e.raw[(size_t)m * N + n] = ci;
         c = (float)ci;
       }
@@ -314,8 +333,13 @@ hipError_t launch_mx(const int8_t* A, const int8_t* B, int M, int N, int K, cons
 
 template <bool FP8, bool OUT_BF16, int NT>
 hipError_t launch_nt(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, hipStream_t st) {
-  return M <= 8 ? launch_mx<FP8, OUT_BF16, NT, 1>(A, B, M, N, K, e, st)
-                : launch_mx<FP8, OUT_BF16, NT, 2>(A, B, M, N, K, e, st);
+  if (M <= 8) return launch_mx<FP8, OUT_BF16, NT, 1>(A, B, M, N, K, e, st);
+  if (M <= 16) return launch_mx<FP8, OUT_BF16, NT, 2>(A, B, M, N, K, e, st);
+  if constexpr (NT < 4) {      // more than 16 tokens only with M N <= 2^19 (N < 32768: NT <= 2)
+    if (M <= 32) return launch_mx<FP8, OUT_BF16, NT, 4>(A, B, M, N, K, e, st);
+    if (M <= 64) return launch_mx<FP8, OUT_BF16, NT, 8>(A, B, M, N, K, e, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <bool FP8, bool OUT_BF16>

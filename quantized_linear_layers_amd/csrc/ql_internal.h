@@ -140,11 +140,15 @@ hipError_t launch_i8_gemm_small(const int8_t* A, const int8_t* B, int M, int N, 
                                 hipStream_t st);
 hipError_t launch_f8_gemm_small(const uint8_t* A, const uint8_t* B, int M, int N, int K, const I8Epi& e,
                                 hipStream_t st);
-// the same products for M <= kGemvMaxM tokens: a workgroup streams 16 or 32
-// output channels' weights for all of K (fp8: E4M3 codes, e.azp, e.azp_adj
-// and e.raw null); launch_i8_gemm / launch_f8_gemm use it for such M
+// the same products for few tokens: a workgroup streams 16, 32 or 64 output
+// channels' weights for all of K (fp8: E4M3 codes, e.azp, e.azp_adj and
+// e.raw null); launch_i8_gemm / launch_f8_gemm use it when i8_gemv_serves(M, N)
 hipError_t launch_i8_gemv(const int8_t* A, const int8_t* B, int M, int N, int K, const I8Epi& e, bool fp8,
                           hipStream_t st);
+// up to 16 tokens always; up to 64 while M N <= 2^19, where the tiled GEMM's
+// 128-column tiles would leave most compute units idle (measured on the 7B and
+// 70B layer shapes: 2 - 2.8x faster there, slower beyond)
+inline bool i8_gemv_serves(int M, int N) { return M <= 16 || (M <= 64 && (long)M * N <= (1L << 19)); }
 // true when the 256 x 128 tiles of an M x N output would occupy at most half
 // of the 256 compute units
 inline bool i8_small_grid(int M, int N) {

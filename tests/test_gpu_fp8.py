@@ -106,11 +106,11 @@ def test_gemm_ragged(M, N, K):
     check_gemm(Aq, Bq, s_a, s_b, bias)
 
 
-# M <= 16: the decode kernel (one 128-byte group per MFMA, fp32 sums added
-# across the waves in wave order)
+# few tokens: the decode kernel (one 128-byte group per MFMA, fp32 sums
+# added across the waves in wave order; up to 64 tokens while M N <= 2^19)
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (1, 4096, 4096), (5, 100, 1040), (8, 8200, 528), (16, 4096, 4112),
                                    (12, 1, 272), (13, 12000, 2064), (8, 16400, 272), (16, 28672, 400),
-                                   (2, 33000, 144)])
+                                   (2, 33000, 144), (20, 4096, 2064), (64, 8192, 400), (30, 17000, 528)])
 def test_gemm_decode(M, N, K):
     r = np.random.default_rng(3 * M + N + K)
     Aq, s_a = of8.quant_per_token_fp8(r.standard_normal((M, K)).astype(np.float32))

@@ -137,13 +137,16 @@ def test_gemm_ragged(M, N, K):
     check_gemm(Aq, Bq, s_a, s_b, azp, ow8.azp_adj(Bq), bias)
 
 
-# M <= 16 takes the decode kernel: 16 output channels per workgroup up to
-# N = 16384, 32 up to 32768, 64 beyond (16400, 28672 and 33000 columns), K in
-# 128-byte groups split among 4 waves (ragged K, K shorter than the waves, N
-# not a multiple of 16, 8 or 16 staged activation rows)
+# Up to 16 tokens, and up to 64 while M N <= 2^19, take the decode kernel: 16
+# output channels per workgroup up to N = 16384, 32 up to 32768, 64 beyond
+# (16400, 20000, 28672 and 33000 columns), K in 128-byte groups split among 4
+# waves (ragged K, K shorter than the waves, N not a multiple of 16, 8, 16,
+# 32 or 64 staged activation rows); 64 x 8193 is just past the rule (tiled
+# GEMM)
 DECODE = [(1, 16, 16), (1, 4096, 4096), (3, 100, 1040), (8, 8200, 528), (9, 1000, 4112), (16, 4096, 4096),
           (16, 8192, 1024), (2, 17, 48), (13, 12000, 2064), (16, 1, 272), (8, 16400, 272), (16, 28672, 400),
-          (2, 33000, 144)]
+          (2, 33000, 144), (17, 4096, 1040), (33, 2000, 4112), (64, 8192, 528), (48, 100, 2064), (24, 20000, 272),
+          (64, 8193, 272)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE)
