@@ -390,6 +390,9 @@ int i8_rmsnorm_quant_per_token(const void* X, int x_dtype, int M, int K,
  * or NULL; azp_adj [N] int32 or NULL; bias [N] of out_dtype or NULL ([VE]
  * "4.1": bias dtype equals the output dtype).  out [M][N] of out_dtype.
  * raw_out: optional [M][N] int32 that receives C (for exact checks), or NULL.
+ * Few tokens (M <= 16, or M <= 64 with M * N <= 2^19) run a kernel that
+ * streams Bq once per block of output channels; larger M the LDS-tiled MFMA
+ * GEMM.  Both give the same C.
  * M == 0 or N == 0 is a no-op.
  * Errors: QL_ERR_NULL (also azp without azp_adj); QL_ERR_DTYPE; QL_ERR_SHAPE
  *         unless M, N >= 0, K > 0, K % 16 == 0, s_a_len in {1, M},
@@ -443,7 +446,9 @@ int f8_quant_per_token(const void* X, int x_dtype, int M, int K, uint8_t* Aq, fl
  * one round-to-nearest-even to out_dtype at the single store.
  * Aq [M][K] and Bq [N][K] E4M3 codes (NaN codes are not allowed); s_a:
  * s_a_len 1 or M; s_b: s_b_len 1 or N; bias [N] of out_dtype or NULL;
- * out [M][N] of out_dtype.  M == 0 or N == 0 is a no-op.
+ * out [M][N] of out_dtype.  M == 0 or N == 0 is a no-op.  The same two
+ * kernels as i8_gemm_scaled (chosen by the same rule); the fp32 sums of the
+ * two differ only in their order.
  * Errors: QL_ERR_NULL; QL_ERR_DTYPE; QL_ERR_SHAPE unless M, N >= 0, K > 0,
  *         K % 16 == 0, s_a_len in {1, M}, s_b_len in {1, N}; QL_ERR_ALIGN;
  *         QL_ERR_HIP.
