@@ -117,10 +117,10 @@ __device__ inline void gv_for(F&& f) {
 // LDS of one workgroup: W waves, each with a ring of D slots
 constexpr int gv_lds_bytes(int NT, int MX, int W, int D) { return W * D * (MX * 1024 + NT * 2048); }
 
-// NT: 16-channel slices per workgroup; MX: 1 KB activation copies per group
-// (8 MX rows; MX = 1: rows 0..7 for M <= 8, else 16 MX / 2 rows in MX / 2
-// blocks of 16 for the products); W: waves (they split K); D:
-// ring slots per wave (D - 1 groups in flight while one is multiplied).
+// NT: 16-channel slices per workgroup; MX: 1 KB activation copies per group,
+// 8 MX rows (MX = 1: the 8 rows of M <= 8, whose products take one block of
+// 16 rows; MX = 2, 4, 8: MX / 2 blocks of 16 rows); W: waves (they split K);
+// D: ring slots per wave (D - 1 groups in flight while one is multiplied).
 // Rows past M repeat row M - 1 and channels past N repeat channel N - 1
 // (valid loads whose products only reach outputs that are never stored).
 template <bool FP8, bool OUT_BF16, int NT, int MX, int W, int D>
@@ -276,7 +276,8 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
       for (int rb = 0; rb < MR; ++rb)
         acc[t][rb] += reinterpret_cast<const GvAcc<FP8>*>(lds_all + w * kWaveBytes)[(t * MR + rb) * 64 + lane];
 
-  // ---- epilogue: lane l holds column l % 16 of each slice, rows 4 (l / 16) + i
+  // ---- epilogue: lane l holds column l % 16 of each slice, rows
+  // 16 rb + 4 (l / 16) + i of each block rb
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int n = n0 + t * 16 + fr;
@@ -291,21 +292,21 @@ __global__ __launch_bounds__(64 * W) void i8_gemv_kernel(const int8_t* A, const 
 #pragma unroll
     for (int rb = 0; rb < MR; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * rb + 4 * lg + i;
-      if (m >= M) continue;
-      float c;
-      if constexpr (FP8) {
-        c = acc[t][rb][i];
-      } else {
-        const int32_t ci = acc[t][rb][i] - (e.azp ? e.azp[m] * adj : adj);
-        if (e.raw) e.raw[(size_t)m * N + n] = ci;
-        c = (float)ci;
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * rb + 4 * lg + i;
+        if (m >= M) continue;
+        float c;
+        if constexpr (FP8) {
+          c = acc[t][rb][i];
+        } else {
+          const int32_t ci = acc[t][rb][i] - (e.azp ? e.azp[m] * adj : adj);
+          if (e.raw) e.raw[(size_t)m * N + n] = ci;
+          c = (float)ci;
+        }
+        const float v = e.s_a[e.s_a_vec ? m : 0] * (sb * c) + b;
+        static_cast<uint16_t*>(e.out)[(size_t)m * N + n] =
+            OUT_BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
       }
-      const float v = e.s_a[e.s_a_vec ? m : 0] * (sb * c) + b;
-      static_cast<uint16_t*>(e.out)[(size_t)m * N + n] =
-          OUT_BF16 ? __builtin_bit_cast(uint16_t, (__bf16)v) : __builtin_bit_cast(uint16_t, (_Float16)v);
-    }
   }
 }
 
