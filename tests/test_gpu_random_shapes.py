@@ -4,11 +4,13 @@ The fixed-shape tests pin the workloads and the edges someone thought of
 (ragged tails, tile and plan boundaries, extreme codes).  This sweep draws
 further shapes from a seeded generator, so that combinations nobody listed
 (a plan, a tile shape, a K split and ragged M, N and K at once) are checked
-as well.  Every case runs the same checks as the fixed-shape tests of its
-entry point: W4A16 within the 1e-2 gate and the element-wise rounding bound,
-the int8 accumulator bit-exact and its fp16/bf16 output within the epilogue
-bound, FP8 within the gate, quantized codes and scales bit-exact.  Sizes are
-kept where the oracle's fp64 products take about a second.
+as well; the few-token W8A8 shapes (up to 64 tokens) are drawn separately,
+so that the kernel that serves them gets its own sample.  Every case runs the
+same checks as the fixed-shape tests of its entry point: W4A16 within the
+1e-2 gate and the element-wise rounding bound, the int8 accumulator
+bit-exact and its fp16/bf16 output within the epilogue bound, FP8 within the
+gate, quantized codes and scales bit-exact.  Sizes are kept where the
+oracle's fp64 products take about a second.
 """
 
 import numpy as np
@@ -95,6 +97,40 @@ def test_fp8_gemm_random_shape(case, M, N, K):
     t8f.check_gemm(Aq, Bq, s_a, s_b, bias, out_dtype=out_dtype)
 
 
+def _few_token_cases(n, seed):
+    """Shapes for the few-token W8A8 kernel: up to 64 tokens, N drawn so that
+    M N stays within 2^19 (the range that kernel serves above 16 tokens)."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = _log_uniform(r, 1, 64)
+        N = _log_uniform(r, 1, max(1, min(20000, (1 << 19) // M)))
+        K = 16 * int(r.integers(1, 300))
+        cases.append((i, M, N, K))
+    return cases
+
+
+@pytest.mark.parametrize("case,M,N,K", _few_token_cases(16, 7070))
+def test_int8_gemm_few_tokens_random_shape(case, M, N, K):
+    r = np.random.default_rng(60_000 + case)
+    Aq, s_a, azp, Bq, s_b = t8._operands(M, N, K, 70_000 + case)
+    out_dtype = torch.bfloat16 if case % 2 else torch.float16
+    bias = torch.from_numpy(r.standard_normal(N).astype(np.float32) * 0.1).to(out_dtype) if case % 3 else None
+    if case % 4 == 3:
+        s_a, s_b = s_a[:1], s_b[:1]
+    t8.check_gemm(Aq, Bq, s_a, s_b, azp, ow8.azp_adj(Bq), bias, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("case,M,N,K", _few_token_cases(8, 8080))
+def test_fp8_gemm_few_tokens_random_shape(case, M, N, K):
+    r = np.random.default_rng(80_000 + case)
+    Aq, s_a = of8.quant_per_token_fp8((r.standard_normal((M, K)) + 0.3).astype(np.float32))
+    Bq, s_b = of8.quant_weight_per_channel_fp8((r.standard_normal((N, K)) * 0.02).astype(np.float32))
+    out_dtype = torch.bfloat16 if case % 2 else torch.float16
+    bias = torch.from_numpy(r.standard_normal(N).astype(np.float32) * 0.1).to(out_dtype) if case % 3 else None
+    t8f.check_gemm(Aq, Bq, s_a, s_b, bias, out_dtype=out_dtype)
+
+
 def _quant_cases(n=16):
     r = np.random.default_rng(6060)
     return [(i, _log_uniform(r, 1, 300), 8 * _log_uniform(r, 1, 2600)) for i in range(n)]
@@ -118,3 +154,5 @@ def test_random_cases_cover_the_plans():
     assert min(ms) <= 16 < max(ms)
     small = [2 * ((M + 255) // 256) * ((N + 127) // 128) <= 256 for _, M, N, _ in _w8_cases()]
     assert any(small) and not all(small)
+    few = [M for _, M, N, _ in _few_token_cases(16, 7070)]
+    assert min(few) <= 16 < max(few)
