@@ -564,10 +564,16 @@ GemvPlan plan_q4_gemv(int M, int N, int K) {
   // waves measured 4-9% faster; and four when the eight-wave workgroups
   // would not all be resident at once (their rings take too much LDS for
   // the grid to fit on the compute units in one round: 16 tokens on the
-  // 4096 x 11008 layer measured 13.2 us with eight waves in two rounds)
+  // 4096 x 11008 layer measured 13.2 us with eight waves in two rounds).
+  // With 16 staged rows, whose copies then outweigh the weights', such a
+  // grid also takes twice the slices (half the activation copies): 12 and
+  // 16 tokens on the 4096 x 11008 layer 9.6 -> 8.8 and 10.1 -> 8.9 us.
   P.waves = P.nt == 4 ? 4 : 8;
   const int grid = slices / P.nt;
-  if (P.waves == 8 && grid > kCUs * (kLdsPerCU / gemv_lds_bytes(P.nt, row_blocks(M), 8))) P.waves = 4;
+  if (P.waves == 8 && grid > kCUs * (kLdsPerCU / gemv_lds_bytes(P.nt, row_blocks(M), 8))) {
+    P.waves = 4;
+    if (row_blocks(M) == 4 && P.nt == 2) P.nt = 4;
+  }
   return P;
 }
 
