@@ -118,24 +118,35 @@ def copy_calibration(mib):
     del src, dst
 
 
-WARM_MS = 10.0                    # warm-up per timed kernel (--warm-ms)
+# warm-up per timed kernel (--warm-ms): after an idle gap a kernel needs about
+# 50 ms of its own back-to-back launches before it runs at its sustained
+# speed (measured: the W4A16 prefill 527 us after 10 ms, 439-457 us after
+# 50-1000 ms; the int8 GEMM 40.1 us, then 35.2-35.4 us)
+WARM_MS = 100.0
 
 
-def warm(fn_list, ms=30.0, cap=5000):
-    """Runs the launches back to back for about `ms` of GPU time, so that the
-    timed ones start at the clock a sustained load settles at (an idle part
-    ramps its clock up over the first milliseconds of work)."""
+def warm(fn_list, ms=30.0, cap=20000):
+    """Runs the launches back to back until about `ms` of GPU time has
+    elapsed, so that the timed ones start at the speed a sustained load
+    settles at (after an idle gap the part takes tens of milliseconds to get
+    there, and the first launches run slower than the later ones, so the
+    elapsed time is measured batch by batch rather than estimated from the
+    first launch)."""
     s = torch.cuda.current_stream()
-    a, b = _events()
-    a.record(s)
-    for fn in fn_list:
-        fn(0)
-    b.record(s)
-    torch.cuda.synchronize()
-    n = min(cap, max(1, int(ms / max(a.elapsed_time(b), 1e-3))))
-    for i in range(n):
-        for fn in fn_list:
-            fn(i)
+    done, i, batch = 0.0, 0, 1
+    while done < ms and i < cap:
+        a, b = _events()
+        a.record(s)
+        for _ in range(batch):
+            for fn in fn_list:
+                fn(i)
+            i += 1
+        b.record(s)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b)
+        done += t
+        # next batch: about 10 ms of launches (at least one)
+        batch = max(1, min(cap - i, int(batch * 10.0 / max(t, 1e-3))))
     torch.cuda.synchronize()
 
 

@@ -40,6 +40,7 @@ namespace ql {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -526,12 +527,15 @@ __global__ __launch_bounds__(64 * kWaves) QL_I8_KERNEL_ATTR void i8_gemm_kernel(
       stage([](int z, int adj) { return __mul24(z, adj); });
     else
       stage([](int z, int adj) { return z * adj; });
+    // the output is written once, all tiles at about the same moment: the
+    // stores carry the non-temporal hint (measured 3-6% faster on
+    // 2048 x 4096 x 4096, 4096^3 and 2048 x 11008 x 4096, int8 and FP8)
     uint16_t* out = static_cast<uint16_t*>(e.out);
 #pragma unroll
     for (int i = 0; i < (kMT * 32) / 8; ++i) {
       const int rl = (lane >> 3) + 8 * i, piece = lane & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(region + rl * 128 + ((piece ^ (rl & 7)) << 4));
-      *reinterpret_cast<uint4*>(out + (size_t)(m0 + wm + rl) * a.N + n0 + wn + piece * 8) = v;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + rl * 128 + ((piece ^ (rl & 7)) << 4));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (size_t)(m0 + wm + rl) * a.N + n0 + wn + piece * 8));
     }
   } else {
 #pragma unroll
