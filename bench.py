@@ -167,7 +167,7 @@ def time_launches(fn_list, reps, stream, warm_ms=None):
         b.record(stream)
         torch.cuda.synchronize()
         out[i] = a.elapsed_time(b) / reps
-    return out
+    return [float(x) for x in out]
 
 
 def bench_decode(ql, wname, steps, warmup, per_case=True):
